@@ -1,0 +1,38 @@
+"""Block-scaled (MX) GEMM for AMD Instinct MI355X (gfx950).
+
+The computation is C = (A * 2^sA)(B * 2^sB)^T over operands stored as FP8 E4M3
+or packed E2M1 codes with one UE8M0 scale per 32 contiguous K elements, fp32
+output; a dense fp16 GEMM is the comparison path.  All arithmetic runs in the
+HIP kernels of ``libmxgemm.so`` behind a C ABI (``include/mxgemm.h``); the
+Python binding in :mod:`block_scaled_precision_mxgemm_amd.mxgemm` only
+marshals torch device tensors to it.
+
+Importing the package loads nothing; the binding is loaded on first use of one
+of its names and raises if the HIP library has not been built.
+"""
+from __future__ import annotations
+
+_BINDING_NAMES = (
+    "mxgemm_quantize",
+    "mxgemm_run",
+    "fp16gemm_run",
+    "mxgemm_run_dequant_fp16",
+    "mxgemm_device_supported",
+    "MXGemmError",
+    "E4M3",
+    "E2M1",
+    "FMT_FP8_FP8",
+    "FMT_FP8_FP4",
+    "FMT_FP4_FP4",
+    "library_path",
+)
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import mxgemm as _b
+
+        return getattr(_b, name)
+    raise AttributeError(name)

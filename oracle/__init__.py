@@ -1,0 +1,250 @@
+"""CPU oracle for the block-scaled (MX) matrix multiply and its fp16 comparison.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never imports, links or executes
+anything here, and this package imports nothing from the product path.
+
+The arithmetic lives in ``mxref.c`` (plain C, float64, OpenMP over output
+points only), compiled with gcc into ``oracle/_build/libmxref.so``.  This file
+only marshals numpy arrays to it and holds the tolerance gate.
+
+Sources (page title, section):
+  * Operand model, one UE8M0 scale per 32 K-elements: "Metal tensors でカスタム
+    機械学習オペレーションを最適化する", sections "多平面 tensor" and "Scale
+    Factor 付き量子化 tensor を作成する".
+  * float64 reference from the exact quantized bytes, per-dtype tolerance gate:
+    "Resumo Técnico: RIGEL", section "Metodologia: O Harness RIGEL".
+  * E4M3 saturates at +-448 with no infinity; accumulator at least fp32:
+    "Resumo Técnico: RIGEL", section 3 "Semântica Numérica e Restrições Ocultas".
+  * Plain triple loop: "Treinar LLM em Swift", section "Passo 1".
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against torch's
+independent fp8/e8m0 dtypes, the OCP MX E2M1 value list, exact rational brute
+force, closed forms and the accumulator-width example the RIGEL summary prints.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+E4M3 = 0
+E2M1 = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxref.c")
+_LIB = os.path.join(_HERE, "_build", "libmxref.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile mxref.c with gcc (-O2, OpenMP, no FP contraction)."""
+    os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
+           "-D_GNU_SOURCE", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    lib.mxref_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_e4m3_value.restype = ctypes.c_double
+    lib.mxref_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_e2m1_value.restype = ctypes.c_double
+    lib.mxref_ue8m0_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_ue8m0_value.restype = ctypes.c_double
+    lib.mxref_fp16_value.argtypes = [ctypes.c_uint16]
+    lib.mxref_fp16_value.restype = ctypes.c_double
+    lib.mxref_quantize.argtypes = [p, i64, i64, ci, p, p]
+    lib.mxref_quantize.restype = ci
+    lib.mxref_gemm.argtypes = [p, p, ci, p, p, ci, i64, i64, i64, p, p]
+    lib.mxref_gemm.restype = ci
+    lib.mxref_gemm_points.argtypes = [p, p, ci, p, p, ci, i64, i64, i64, p, p, i64, p, p]
+    lib.mxref_gemm_points.restype = ci
+    lib.mxref_fp16_gemm.argtypes = [p, p, i64, i64, i64, ci, p, p]
+    lib.mxref_fp16_gemm.restype = ci
+    lib.mxref_fp16_gemm_points.argtypes = [p, p, i64, i64, i64, ci, p, p, i64, p, p]
+    lib.mxref_fp16_gemm_points.restype = ci
+    lib.mxref_num_threads.argtypes = []
+    lib.mxref_num_threads.restype = ci
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
+    return int(_load().mxref_num_threads())
+
+
+# ----------------------------------------------------------------- tables
+
+def e4m3_table() -> np.ndarray:
+    """float64[256]: value of every E4M3 code (NaN for 0x7F and 0xFF)."""
+    lib = _load()
+    return np.array([lib.mxref_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e2m1_table() -> np.ndarray:
+    """float64[16]: value of every E2M1 nibble."""
+    lib = _load()
+    return np.array([lib.mxref_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def ue8m0_table() -> np.ndarray:
+    """float64[256]: 2^(e-127) for every scale byte, NaN for 255."""
+    lib = _load()
+    return np.array([lib.mxref_ue8m0_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp16_value(bits: int) -> float:
+    return float(_load().mxref_fp16_value(bits))
+
+
+def row_bytes(K: int, elem: int) -> int:
+    """Bytes per operand row: K for E4M3, K/2 for packed E2M1."""
+    return K if elem == E4M3 else K // 2
+
+
+# --------------------------------------------------------------- quantize
+
+def quantize(x: np.ndarray, elem: int):
+    """Quantize fp32 rows (K contiguous) to (codes uint8, scales uint8).
+
+    codes: rows x K (E4M3) or rows x K/2 (E2M1, even k in the low nibble);
+    scales: rows x K/32 UE8M0 bytes.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    q = np.zeros((rows, row_bytes(K, elem)), dtype=np.uint8)
+    s = np.zeros((rows, K // 32), dtype=np.uint8)
+    rc = _load().mxref_quantize(_ptr(x), rows, K, elem, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E2M1)")
+    return q, s
+
+
+# ------------------------------------------------------------------- GEMM
+
+def _check_operand(q, s, rows, K, elem, name):
+    if q.dtype != np.uint8 or s.dtype != np.uint8:
+        raise TypeError(name + ": codes and scales must be uint8")
+    if q.shape != (rows, row_bytes(K, elem)) or s.shape != (rows, K // 32):
+        raise ValueError(name + ": shape mismatch")
+
+
+def mx_gemm(a_q, a_s, elem_a, b_q, b_s, elem_b, M, N, K, points=None):
+    """float64 reference C and the magnitude sum |A||B| (same shape).
+
+    A is M x K codes with M x K/32 scales; B is N x K codes with N x K/32
+    scales (both K contiguous).  With ``points=(I, J)`` only those output
+    elements are computed and 1-D arrays are returned.
+    """
+    a_q = np.ascontiguousarray(a_q)
+    a_s = np.ascontiguousarray(a_s)
+    b_q = np.ascontiguousarray(b_q)
+    b_s = np.ascontiguousarray(b_s)
+    _check_operand(a_q, a_s, M, K, elem_a, "A")
+    _check_operand(b_q, b_s, N, K, elem_b, "B")
+    lib = _load()
+    if points is None:
+        C = np.empty((M, N), dtype=np.float64)
+        ABS = np.empty((M, N), dtype=np.float64)
+        rc = lib.mxref_gemm(_ptr(a_q), _ptr(a_s), elem_a, _ptr(b_q), _ptr(b_s), elem_b,
+                            M, N, K, _ptr(C), _ptr(ABS))
+    else:
+        I = np.ascontiguousarray(points[0], dtype=np.int64)
+        J = np.ascontiguousarray(points[1], dtype=np.int64)
+        C = np.empty(I.shape[0], dtype=np.float64)
+        ABS = np.empty(I.shape[0], dtype=np.float64)
+        rc = lib.mxref_gemm_points(_ptr(a_q), _ptr(a_s), elem_a, _ptr(b_q), _ptr(b_s), elem_b,
+                                   M, N, K, _ptr(I), _ptr(J), I.shape[0], _ptr(C), _ptr(ABS))
+    if rc != 0:
+        raise ValueError("oracle mx_gemm: bad arguments")
+    return C, ABS
+
+
+def fp16_gemm(a_bits, b_bits, M, N, K, b_is_nk, points=None):
+    """float64 reference for C = A B on binary16 inputs (given as uint16 bits).
+
+    A is M x K row-major; B is K x N row-major (b_is_nk=0) or N x K (b_is_nk=1).
+    """
+    a = np.ascontiguousarray(a_bits).view(np.uint16)
+    b = np.ascontiguousarray(b_bits).view(np.uint16)
+    if a.shape != (M, K) or b.shape != ((N, K) if b_is_nk else (K, N)):
+        raise ValueError("oracle fp16_gemm: shape mismatch")
+    lib = _load()
+    if points is None:
+        C = np.empty((M, N), dtype=np.float64)
+        ABS = np.empty((M, N), dtype=np.float64)
+        rc = lib.mxref_fp16_gemm(_ptr(a), _ptr(b), M, N, K, int(b_is_nk), _ptr(C), _ptr(ABS))
+    else:
+        I = np.ascontiguousarray(points[0], dtype=np.int64)
+        J = np.ascontiguousarray(points[1], dtype=np.int64)
+        C = np.empty(I.shape[0], dtype=np.float64)
+        ABS = np.empty(I.shape[0], dtype=np.float64)
+        rc = lib.mxref_fp16_gemm_points(_ptr(a), _ptr(b), M, N, K, int(b_is_nk),
+                                        _ptr(I), _ptr(J), I.shape[0], _ptr(C), _ptr(ABS))
+    if rc != 0:
+        raise ValueError("oracle fp16_gemm: bad arguments")
+    return C, ABS
+
+
+# ------------------------------------------------------------------- gate
+
+U = 2.0 ** -24  # unit roundoff of fp32
+
+
+def gate(c_test, c_ref, abs_ref, K):
+    """Checksum gate: |c_test - c_ref| <= K * 2^-24 * sum|a b| for every element,
+    NaN positions identical, +-Inf positions and signs identical.
+
+    The fp8 x fp8 (or fp4, fp16) products times power-of-two scales are exact
+    in fp32, so the only admissible error is fp32 accumulation error; the
+    bound is the classical recursive-summation bound with K terms.  Returns a
+    dict with 'ok', 'n_bad', 'max_ratio', 'nan_mismatch', 'n_exact'.
+    """
+    t = np.asarray(c_test, dtype=np.float64)
+    r = np.asarray(c_ref, dtype=np.float64)
+    a = np.asarray(abs_ref, dtype=np.float64)
+    if t.shape != r.shape or r.shape != a.shape:
+        raise ValueError("gate: shape mismatch")
+    nan_t, nan_r = np.isnan(t), np.isnan(r)
+    nan_mismatch = int(np.count_nonzero(nan_t != nan_r))
+    inf_t, inf_r = np.isinf(t), np.isinf(r)
+    inf_mismatch = int(np.count_nonzero((inf_t != inf_r) | (inf_t & inf_r & (np.sign(t) != np.sign(r)))))
+    fin = ~(nan_t | nan_r | inf_t | inf_r)
+    tol = K * U * a[fin]
+    err = np.abs(t[fin] - r[fin])
+    bad = err > tol
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+    n_exact = int(np.count_nonzero(t[fin] == r[fin].astype(np.float32).astype(np.float64)))
+    n_bad = int(np.count_nonzero(bad)) + nan_mismatch + inf_mismatch
+    return {
+        "ok": n_bad == 0,
+        "n_bad": n_bad,
+        "n": int(t.size),
+        "max_ratio": float(ratio.max()) if ratio.size else 0.0,
+        "nan_mismatch": nan_mismatch,
+        "inf_mismatch": inf_mismatch,
+        "n_exact": n_exact,
+    }

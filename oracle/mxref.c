@@ -1,0 +1,375 @@
+/*
+ * mxref.c - CPU oracle for the block-scaled ("MX") matrix multiply.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or constant with the
+ * HIP library: every value below is derived here, from the format
+ * definitions, in plain C and float64.
+ *
+ * What it computes, and the passages it follows:
+ *   - The operand model: each operand is a data plane of low-precision codes
+ *     plus a scale plane holding one FP8 E8M0 (UE8M0) power of two per block
+ *     of 32 consecutive elements along the reduction axis.  Source: WWDC26
+ *     session 330 summary "Metal tensors でカスタム機械学習オペレーションを
+ *     最適化する", sections "多平面 tensor" and "Scale Factor 付き量子化
+ *     tensor を作成する" (blockFactors {32, 1}); the same session's
+ *     transcript "Metal 텐서로 맞춤형 머신 러닝 연산 최적화하기", chapter
+ *     "Multi-plane tensors".
+ *   - The check itself: a float64 reference computed from exactly the bytes
+ *     the GPU consumed.  Source: "Resumo Técnico: RIGEL", section
+ *     "Metodologia: O Harness RIGEL" (checksum-gated verification).
+ *   - The product: a plain triple loop over rows, columns and the reduction
+ *     index.  Source: "Treinar LLM em Swift: multiplicação de matrizes do
+ *     Gflop/s ao Tflop/s", section "Passo 1 - Baseline: matmul ingênua".
+ *   - E4M3 saturates to +-448 and has no infinity.  Source: "Resumo Técnico:
+ *     RIGEL", section 3 "Semântica Numérica e Restrições Ocultas".
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes as well):
+ *   - Scale selection is the OCP Microscaling rule: the block exponent is
+ *     floor(log2(amax)) - emax_elem, emax_elem = 8 for E4M3 and 2 for E2M1,
+ *     clamped to [-127, 127]; an all-zero block gets exponent -127.
+ *   - Elements are rounded to nearest, ties to even, and saturated to the
+ *     largest finite magnitude (448 for E4M3, 6 for E2M1).
+ *   - A block holding a NaN or an infinity gets scale byte 255 (NaN) and
+ *     element codes 0.
+ *   - E2M1 codes are packed two per byte, the even K index in the low nibble.
+ *   - UE8M0 byte e means 2^(e-127); e = 255 is NaN.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define MXREF_E4M3 0
+#define MXREF_E2M1 4
+
+/* ---------------------------------------------------------------- decode */
+
+/* OCP E4M3 ("FN") code -> value: sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-9); the all-ones pattern
+ * S.1111.111 is NaN; there is no infinity. */
+double mxref_e4m3_value(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* OCP E2M1 nibble -> value: sign, 2 exponent bits (bias 1), 1 mantissa bit;
+ * exponent field 0 is subnormal (m * 0.5); no NaN, no infinity. */
+double mxref_e2m1_value(uint8_t nibble)
+{
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
+    return s ? -v : v;
+}
+
+/* UE8M0 scale byte -> 2^(e-127); 255 is NaN. */
+double mxref_ue8m0_value(uint8_t e)
+{
+    return e == 255 ? NAN : ldexp(1.0, (int)e - 127);
+}
+
+/* IEEE binary16 bits -> value. */
+double mxref_fp16_value(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp(1.0 + m / 1024.0, e - 15);
+    return s ? -v : v;
+}
+
+/* -------------------------------------------------------------- quantize */
+
+/* floor(log2(a)) for finite a > 0, exactly (no floating log2). */
+static int floor_log2(double a)
+{
+    int e;
+    frexp(a, &e); /* a = f * 2^e with f in [0.5, 1) */
+    return e - 1;
+}
+
+/* Round |v| to the E4M3 grid (ties to even), saturate at 448, encode. */
+static uint8_t encode_e4m3(double v)
+{
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v), quantum, r;
+    uint8_t code;
+    /* normal binades [2^-6, ...) carry 3 fraction bits; below 2^-6 the
+     * spacing is the subnormal step 2^-9 */
+    quantum = (a >= ldexp(1.0, -6)) ? ldexp(1.0, floor_log2(a) - 3) : ldexp(1.0, -9);
+    r = nearbyint(a / quantum) * quantum; /* default mode: nearest, ties even */
+    if (r > 448.0)
+        r = 448.0;
+    if (r < ldexp(1.0, -6)) {
+        code = (uint8_t)(r * 512.0); /* subnormal: m = r / 2^-9, 0..7 */
+    } else {
+        int e = floor_log2(r);
+        int m = (int)((r / ldexp(1.0, e) - 1.0) * 8.0);
+        code = (uint8_t)(((e + 7) << 3) | m);
+    }
+    return (uint8_t)(code | (neg << 7));
+}
+
+/* Round |v| to the E2M1 grid (ties to even), saturate at 6, encode. */
+static uint8_t encode_e2m1(double v)
+{
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v), quantum, r;
+    uint8_t code;
+    quantum = (a >= 1.0) ? ldexp(1.0, floor_log2(a) - 1) : 0.5;
+    r = nearbyint(a / quantum) * quantum;
+    if (r > 6.0)
+        r = 6.0;
+    if (r < 1.0) {
+        code = (uint8_t)(r * 2.0); /* subnormal: 0 or 0.5 */
+    } else {
+        int e = floor_log2(r);
+        int m = (int)((r / ldexp(1.0, e) - 1.0) * 2.0);
+        code = (uint8_t)(((e + 1) << 1) | m);
+    }
+    return (uint8_t)(code | (neg << 3));
+}
+
+/* Quantize X[rows][K] (fp32, K contiguous) to codes Q and scales S.
+ *   E4M3: Q is rows x K bytes.   E2M1: Q is rows x K/2 bytes, two per byte.
+ *   S is rows x K/32 UE8M0 bytes.
+ * Returns 0, or -1 on a bad argument (K not a multiple of 32, unknown elem). */
+int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
+                   uint8_t *q, uint8_t *s)
+{
+    int emax;
+    int64_t nb = K / 32;
+    if (K <= 0 || K % 32 != 0 || rows < 0)
+        return -1;
+    if (elem == MXREF_E4M3)
+        emax = 8; /* 448 = 1.75 * 2^8 */
+    else if (elem == MXREF_E2M1)
+        emax = 2; /* 6 = 1.5 * 2^2 */
+    else
+        return -1;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *blk = x + r * K + b * 32;
+            double amax = 0.0;
+            int bad = 0, e, i;
+            for (i = 0; i < 32; i++) {
+                double v = blk[i];
+                if (isnan(v) || isinf(v))
+                    bad = 1;
+                else if (fabs(v) > amax)
+                    amax = fabs(v);
+            }
+            if (bad) {
+                s[r * nb + b] = 255;
+                for (i = 0; i < 32; i++) {
+                    int64_t k = b * 32 + i;
+                    if (elem == MXREF_E4M3)
+                        q[r * K + k] = 0;
+                    else
+                        q[r * (K / 2) + k / 2] &= (uint8_t)((k & 1) ? 0x0F : 0xF0);
+                }
+                continue;
+            }
+            e = (amax == 0.0) ? -127 : floor_log2(amax) - emax;
+            if (e < -127)
+                e = -127;
+            if (e > 127)
+                e = 127;
+            s[r * nb + b] = (uint8_t)(e + 127);
+            for (i = 0; i < 32; i++) {
+                int64_t k = b * 32 + i;
+                double v = ldexp((double)blk[i], -e); /* exact */
+                if (elem == MXREF_E4M3) {
+                    q[r * K + k] = encode_e4m3(v);
+                } else {
+                    uint8_t nib = encode_e2m1(v);
+                    uint8_t *p = q + r * (K / 2) + k / 2;
+                    if (k & 1)
+                        *p = (uint8_t)((*p & 0x0F) | (nib << 4));
+                    else
+                        *p = (uint8_t)((*p & 0xF0) | nib);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+static double tab_e4m3[256], tab_e2m1[16], tab_ue8m0[256];
+static int tabs_ready = 0;
+
+static void make_tables(void)
+{
+    int i;
+    if (tabs_ready)
+        return;
+    for (i = 0; i < 256; i++)
+        tab_e4m3[i] = mxref_e4m3_value((uint8_t)i);
+    for (i = 0; i < 16; i++)
+        tab_e2m1[i] = mxref_e2m1_value((uint8_t)i);
+    for (i = 0; i < 256; i++)
+        tab_ue8m0[i] = mxref_ue8m0_value((uint8_t)i);
+    tabs_ready = 1;
+}
+
+/* Value of element k of one operand row (codes only, no scale). */
+static double element(const uint8_t *row, int elem, int64_t k)
+{
+    if (elem == MXREF_E4M3)
+        return tab_e4m3[row[k]];
+    return tab_e2m1[(row[k >> 1] >> ((k & 1) * 4)) & 15];
+}
+
+/* One output element:
+ *   C[i][j] = sum_b 2^(sA[i][b]-127) * 2^(sB[j][b]-127) * sum_{k in block b} a_ik * b_jk
+ * A is M x K codes (K contiguous), B is N x K codes (K contiguous): both
+ * scale planes run along K.  Each block partial is a sum of 32 products of
+ * short significands, exact in float64; multiplying by a power of two is
+ * exact; only the sum across blocks rounds (relative error below
+ * (K/32) * 2^-53).  abs_out receives sum_k |a_ik * b_jk| * scales, the
+ * magnitude that sets the accumulation-error bound. */
+static void mx_point(const uint8_t *A, const uint8_t *sA, int elemA,
+                     const uint8_t *B, const uint8_t *sB, int elemB,
+                     int64_t K, int64_t i, int64_t j, double *out, double *abs_out)
+{
+    int64_t nb = K / 32;
+    int64_t rowbytesA = (elemA == MXREF_E4M3) ? K : K / 2;
+    int64_t rowbytesB = (elemB == MXREF_E4M3) ? K : K / 2;
+    const uint8_t *ra = A + i * rowbytesA, *rb = B + j * rowbytesB;
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t b = 0; b < nb; b++) {
+        double part = 0.0, part_abs = 0.0;
+        double scale = tab_ue8m0[sA[i * nb + b]] * tab_ue8m0[sB[j * nb + b]];
+        for (int64_t k = b * 32; k < b * 32 + 32; k++) {
+            double p = element(ra, elemA, k) * element(rb, elemB, k);
+            part += p;
+            part_abs += fabs(p);
+        }
+        acc += part * scale;
+        acc_abs += part_abs * scale;
+    }
+    *out = acc;
+    *abs_out = acc_abs;
+}
+
+/* Full product: C and ABS are M x N float64, row-major. */
+int mxref_gemm(const uint8_t *A, const uint8_t *sA, int elemA,
+               const uint8_t *B, const uint8_t *sB, int elemB,
+               int64_t M, int64_t N, int64_t K, double *C, double *ABS)
+{
+    if (K <= 0 || K % 32 != 0 || M < 0 || N < 0)
+        return -1;
+    if ((elemA != MXREF_E4M3 && elemA != MXREF_E2M1) ||
+        (elemB != MXREF_E4M3 && elemB != MXREF_E2M1))
+        return -1;
+    make_tables();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t j = 0; j < N; j++)
+            mx_point(A, sA, elemA, B, sB, elemB, K, i, j,
+                     &C[i * N + j], &ABS[i * N + j]);
+    return 0;
+}
+
+/* Sampled product: only the npts points (I[p], J[p]); C and ABS have npts
+ * entries.  Same arithmetic as mxref_gemm. */
+int mxref_gemm_points(const uint8_t *A, const uint8_t *sA, int elemA,
+                      const uint8_t *B, const uint8_t *sB, int elemB,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t *I, const int64_t *J, int64_t npts,
+                      double *C, double *ABS)
+{
+    if (K <= 0 || K % 32 != 0)
+        return -1;
+    if ((elemA != MXREF_E4M3 && elemA != MXREF_E2M1) ||
+        (elemB != MXREF_E4M3 && elemB != MXREF_E2M1))
+        return -1;
+    for (int64_t p = 0; p < npts; p++)
+        if (I[p] < 0 || I[p] >= M || J[p] < 0 || J[p] >= N)
+            return -1;
+    make_tables();
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t p = 0; p < npts; p++)
+        mx_point(A, sA, elemA, B, sB, elemB, K, I[p], J[p], &C[p], &ABS[p]);
+    return 0;
+}
+
+/* ----------------------------------------------------------- fp16 GEMM */
+
+/* fp16 comparison product, C = A B with A M x K row-major and B either
+ * K x N row-major (b_is_nk = 0) or N x K row-major (b_is_nk = 1).
+ * Products of two binary16 values are exact in float64; the K-term sum
+ * rounds with relative error below K * 2^-53.  This is the half-precision
+ * rung of "Treinar LLM em Swift", section "Passo 6" (FP16 in place of FP32),
+ * computed with the plain loop of its section "Passo 1". */
+static void f16_point(const uint16_t *A, const uint16_t *B, int64_t N, int64_t K,
+                      int b_is_nk, int64_t i, int64_t j, double *out, double *abs_out)
+{
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t k = 0; k < K; k++) {
+        uint16_t bb = b_is_nk ? B[j * K + k] : B[k * N + j];
+        double p = mxref_fp16_value(A[i * K + k]) * mxref_fp16_value(bb);
+        acc += p;
+        acc_abs += fabs(p);
+    }
+    *out = acc;
+    *abs_out = acc_abs;
+}
+
+int mxref_fp16_gemm(const uint16_t *A, const uint16_t *B, int64_t M, int64_t N,
+                    int64_t K, int b_is_nk, double *C, double *ABS)
+{
+    if (K <= 0 || M < 0 || N < 0)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t j = 0; j < N; j++)
+            f16_point(A, B, N, K, b_is_nk, i, j, &C[i * N + j], &ABS[i * N + j]);
+    return 0;
+}
+
+int mxref_fp16_gemm_points(const uint16_t *A, const uint16_t *B, int64_t M,
+                           int64_t N, int64_t K, int b_is_nk,
+                           const int64_t *I, const int64_t *J, int64_t npts,
+                           double *C, double *ABS)
+{
+    if (K <= 0)
+        return -1;
+    for (int64_t p = 0; p < npts; p++)
+        if (I[p] < 0 || I[p] >= M || J[p] < 0 || J[p] >= N)
+            return -1;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t p = 0; p < npts; p++)
+        f16_point(A, B, N, K, b_is_nk, I[p], J[p], &C[p], &ABS[p]);
+    return 0;
+}
+
+/* Number of threads the parallel loops above use. */
+int mxref_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
