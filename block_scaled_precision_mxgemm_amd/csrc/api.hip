@@ -1,0 +1,115 @@
+// api.hip - the exported C ABI (declared in include/mxgemm.h): argument
+// validation, device check and kernel choice.  No entry point allocates,
+// frees or synchronizes; all work is enqueued on the caller's stream.
+#include <string.h>
+
+#include "../../include/mxgemm.h"
+#include "mxg_internal.h"
+
+namespace {
+
+// gfx950 check, cached per device (the library runs on one kind of GPU).
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices];  // 0 = unknown, 1 = gfx950, -1 = other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXG_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MXG_EUNSUPPORTED;
+  int v = __atomic_load_n(&g_arch_ok[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MXG_EHIP;
+    v = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    __atomic_store_n(&g_arch_ok[dev], v, __ATOMIC_RELAXED);
+  }
+  return v == 1 ? MXG_OK : MXG_EUNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dim_ok(int64_t d) { return d >= 1 && d <= MXG_MAX_DIM; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? MXG_OK : MXG_EHIP; }
+
+int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const float* C, int64_t M,
+                int64_t N, int64_t K, int fmt) {
+  if (!A || !SA || !B || !SB || !C) return MXG_EINVAL;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
+  if (fmt != MXG_FMT_FP8_FP8 && fmt != MXG_FMT_FP8_FP4 && fmt != MXG_FMT_FP4_FP4) return MXG_EINVAL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXG_EALIGN;
+  return MXG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxgemm_status_string(int status) {
+  switch (status) {
+    case MXG_OK:
+      return "ok";
+    case MXG_EINVAL:
+      return "invalid argument (null pointer, dimension out of range, K not a multiple of 32, or unknown format)";
+    case MXG_EALIGN:
+      return "data pointer not 16-byte aligned";
+    case MXG_EUNSUPPORTED:
+      return "device is not gfx950 (MI355X)";
+    case MXG_EHIP:
+      return "HIP runtime error at launch";
+    default:
+      return "unknown status";
+  }
+}
+
+int mxgemm_device_supported(void) {
+  const int s = check_device();
+  if (s == MXG_OK) return 1;
+  if (s == MXG_EUNSUPPORTED) return 0;
+  return -s;
+}
+
+int mxgemm_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S, void* stream) {
+  if (!X || !Q || !S) return MXG_EINVAL;
+  if (!dim_ok(rows) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
+  if (elem != MXG_ELEM_E4M3 && elem != MXG_ELEM_E2M1) return MXG_EINVAL;
+  if (!aligned16(X) || !aligned16(Q)) return MXG_EALIGN;
+  const int d = check_device();
+  if (d != MXG_OK) return d;
+  return to_status(mxg::launch_quantize(X, rows, K, elem, Q, S, (hipStream_t)stream));
+}
+
+int mxgemm_run(const void* A, const uint8_t* scaleA, const void* B, const uint8_t* scaleB, float* C, int64_t M,
+               int64_t N, int64_t K, int fmt, void* stream) {
+  int s = validate_mx(A, scaleA, B, scaleB, C, M, N, K, fmt);
+  if (s != MXG_OK) return s;
+  s = check_device();
+  if (s != MXG_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (M <= mxg::kSkinnyMaxM && fmt != MXG_FMT_FP4_FP4)
+    return to_status(mxg::launch_mx_skinny(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
+  return to_status(mxg::launch_mx_tiled(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
+}
+
+int fp16gemm_run(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K, int b_is_nk,
+                 void* stream) {
+  if (!A || !B || !C) return MXG_EINVAL;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (K % 8) != 0) return MXG_EINVAL;
+  if (b_is_nk != 0 && b_is_nk != 1) return MXG_EINVAL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXG_EALIGN;
+  const int s = check_device();
+  if (s != MXG_OK) return s;
+  return to_status(mxg::launch_f16_tiled(A, B, C, M, N, K, b_is_nk, (hipStream_t)stream));
+}
+
+int mxgemm_run_dequant_fp16(const void* A, const uint8_t* scaleA, const void* B, const uint8_t* scaleB, float* C,
+                            int64_t M, int64_t N, int64_t K, int fmt, void* stream) {
+  int s = validate_mx(A, scaleA, B, scaleB, C, M, N, K, fmt);
+  if (s != MXG_OK) return s;
+  if (fmt != MXG_FMT_FP8_FP8) return MXG_EINVAL;
+  s = check_device();
+  if (s != MXG_OK) return s;
+  return to_status(mxg::launch_deq_tiled(A, scaleA, B, scaleB, C, M, N, K, (hipStream_t)stream));
+}
+
+}  // extern "C"

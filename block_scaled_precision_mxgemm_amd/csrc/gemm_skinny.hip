@@ -1,0 +1,202 @@
+// gemm_skinny.hip - MX GEMM for decode shapes (M <= 64 rows of activations
+// against a large weight matrix).  Such a product is bound by the bytes of
+// B, which must stream from HBM exactly once; the weight plane is what
+// quantization shrinks ("Metal tensors でカスタム機械学習オペレーションを
+// 最適化する", section "主要内容": inference is memory-bandwidth bound and
+// quantization cuts both the footprint and the traffic).
+//
+// Design (gfx950):
+//   * no LDS staging of B: every lane loads its MFMA operand bytes straight
+//     from global memory (16-byte loads) in the scaled-MFMA register layout,
+//     so each B byte is read once and used once;
+//   * a workgroup owns NF * 16 columns of C (rows of B); its 4 waves split
+//     the K range four ways (split-K) and the partial sums are added in LDS
+//     in a fixed order, so the result is deterministic and needs no atomics
+//     and no zero-initialised output;
+//   * each wave keeps two groups of U slices in flight (registers), loading
+//     group j+1 while the MFMAs of group j run;
+//   * the activation rows (<= 64, a few hundred KiB) are re-read from L2 by
+//     every workgroup.
+#include "mxg_device.h"
+#include "mxg_internal.h"
+
+namespace mxg {
+namespace {
+
+struct SkArgs {
+  const uint8_t* A;
+  const uint8_t* SA;
+  const uint8_t* B;
+  const uint8_t* SB;
+  float* C;
+  int M, N, K;
+  int64_t lda, ldb;  // row strides in bytes
+  int nslices;       // ceil(K / 128)
+};
+
+template <int MT, int NF, bool BF4, int U>
+struct Skinny {
+  struct Group {
+    v8i a[U][MT];
+    v8i b[U][NF];
+    int sa[U][MT];
+    int sb[U][NF];
+  };
+
+  // fp8 operand bytes of one lane: k = 16g..16g+15 and 64+16g..64+16g+15
+  static __device__ __forceinline__ v8i load_fp8(const uint8_t* row, int k0, int g, int K) {
+    v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+    if (k0 + 16 * g < K) lo = *reinterpret_cast<const v4i*>(row + k0 + 16 * g);
+    if (k0 + 64 + 16 * g < K) hi = *reinterpret_cast<const v4i*>(row + k0 + 64 + 16 * g);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  // fp4 operand bytes of one lane: k = 32g..32g+31 (16 bytes)
+  static __device__ __forceinline__ v8i load_fp4(const uint8_t* row, int k0, int g, int K) {
+    v4i lo = {0, 0, 0, 0};
+    if (k0 + 32 * g < K) lo = *reinterpret_cast<const v4i*>(row + (k0 >> 1) + 16 * g);
+    return v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+  }
+  static __device__ __forceinline__ int load_scale(const uint8_t* srow, int blk, int nb) {
+    return (blk < nb) ? (int)srow[blk] : 127;
+  }
+
+  static __device__ __forceinline__ void load_group(const SkArgs& a, int n0, int s, int s_end, int g, int r,
+                                                    Group& G) {
+    const int nb = a.K >> 5;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int sl = s + u;
+      const bool live = sl < s_end;
+      const int k0 = sl * 128;
+#pragma unroll
+      for (int j = 0; j < NF; j++) {
+        const int n = min(n0 + j * 16 + r, a.N - 1);
+        const uint8_t* brow = a.B + (int64_t)n * a.ldb;
+        if (live) {
+          G.b[u][j] = BF4 ? load_fp4(brow, k0, g, a.K) : load_fp8(brow, k0, g, a.K);
+          G.sb[u][j] = load_scale(a.SB + (int64_t)n * nb, sl * 4 + g, nb);
+        } else {
+          G.b[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          G.sb[u][j] = 127;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < MT; t++) {
+        const int m = min(t * 16 + r, a.M - 1);
+        const uint8_t* arow = a.A + (int64_t)m * a.lda;
+        if (live) {
+          G.a[u][t] = load_fp8(arow, k0, g, a.K);
+          G.sa[u][t] = load_scale(a.SA + (int64_t)m * nb, sl * 4 + g, nb);
+        } else {
+          G.a[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          G.sa[u][t] = 127;
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void compute(const Group& G, v4f (&acc)[MT][NF]) {
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int t = 0; t < MT; t++)
+#pragma unroll
+        for (int j = 0; j < NF; j++)
+          acc[t][j] = mfma_scaled_16x16x128<BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8>(G.b[u][j], G.a[u][t], acc[t][j],
+                                                                             G.sb[u][j], G.sa[u][t]);
+  }
+
+  static __device__ __forceinline__ void run(const SkArgs& a) {
+    __shared__ v4f red[3][MT][NF][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int n0 = blockIdx.x * NF * 16;
+    // K split: wave w takes slices [s_begin, s_end)
+    const int per = (a.nslices + 3) / 4;
+    const int s_begin = min(wave * per, a.nslices);
+    const int s_end = min(s_begin + per, a.nslices);
+
+    v4f acc[MT][NF];
+#pragma unroll
+    for (int t = 0; t < MT; t++)
+#pragma unroll
+      for (int j = 0; j < NF; j++) acc[t][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    Group cur, nxt;
+    if (s_begin < s_end) load_group(a, n0, s_begin, s_end, g, r, cur);
+    for (int s = s_begin; s < s_end; s += U) {
+      if (s + U < s_end) load_group(a, n0, s + U, s_end, g, r, nxt);
+      compute(cur, acc);
+      cur = nxt;
+    }
+
+    if (wave > 0) {
+#pragma unroll
+      for (int t = 0; t < MT; t++)
+#pragma unroll
+        for (int j = 0; j < NF; j++) red[wave - 1][t][j][lane] = acc[t][j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int t = 0; t < MT; t++) {
+      const int m = t * 16 + r;
+#pragma unroll
+      for (int j = 0; j < NF; j++) {
+        v4f v = acc[t][j];
+#pragma unroll
+        for (int w = 0; w < 3; w++) v += red[w][t][j][lane];
+        if (m >= a.M) continue;
+        const int n = n0 + j * 16 + 4 * g;
+        float* crow = a.C + (int64_t)m * a.N;
+        if ((a.N & 3) == 0 && n + 3 < a.N) {
+          *reinterpret_cast<v4f*>(crow + n) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            if (n + i < a.N) crow[n + i] = v[i];
+        }
+      }
+    }
+  }
+};
+
+template <int MT, int NF, bool BF4, int U>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void skinny_kernel(SkArgs a) {
+  Skinny<MT, NF, BF4, U>::run(a);
+}
+
+template <int MT, int NF, bool BF4, int U>
+hipError_t launch_sk(const SkArgs& a, hipStream_t stream) {
+  const int grid = (a.N + NF * 16 - 1) / (NF * 16);
+  hipLaunchKernelGGL((skinny_kernel<MT, NF, BF4, U>), dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF4>
+hipError_t launch_by_m(const SkArgs& a, hipStream_t stream) {
+  if (a.M <= 16) return launch_sk<1, 4, BF4, 2>(a, stream);
+  if (a.M <= 32) return launch_sk<2, 4, BF4, 2>(a, stream);
+  return launch_sk<4, 2, BF4, 2>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                            int64_t N, int64_t K, int fmt, hipStream_t stream) {
+  SkArgs a{};
+  a.A = (const uint8_t*)A;
+  a.SA = SA;
+  a.B = (const uint8_t*)B;
+  a.SB = SB;
+  a.C = C;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.lda = K;
+  a.ldb = (fmt == 0) ? K : K / 2;
+  a.nslices = (int)((K + 127) / 128);
+  return (fmt == 0) ? launch_by_m<false>(a, stream) : launch_by_m<true>(a, stream);
+}
+
+}  // namespace mxg

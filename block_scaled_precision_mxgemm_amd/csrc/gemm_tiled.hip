@@ -1,0 +1,464 @@
+// gemm_tiled.hip - LDS-tiled GEMM kernels for large M: the scaled-MFMA MX
+// GEMM (the product path), the dense fp16 comparison GEMM and the
+// dequantize-to-fp16 ablation.  All three share one skeleton:
+//
+//   * a workgroup of 4 waves owns a BM x BN tile of C; each wave owns a
+//     (BM/WM) x (BN/WN) sub-tile held in MFMA accumulators;
+//   * the K loop walks slices of 128 K elements (MX operands: 128 bytes of
+//     fp8 codes or 64 bytes of packed fp4 per row) or of 64 K elements (fp16:
+//     128 bytes per row) through two LDS stages: the copy of slice s+1 (direct
+//     global->LDS 16-byte loads, no register staging) overlaps the MFMAs on
+//     slice s; one barrier per slice;
+//   * LDS rows are 16-byte-chunk XOR-swizzled so that both the tile copies and
+//     the fragment reads are bank-conflict free;
+//   * the scale planes (4 UE8M0 bytes per row per slice) travel through
+//     registers into LDS next to their data, sliced together with it as the
+//     WWDC26 session 330 summary describes for multi-plane tensors (section
+//     "スライスと量子化行列乗算");
+//   * the MFMA's first source is the B fragment, so each lane's 4 accumulator
+//     values are 4 consecutive columns of one C row: the epilogue stores
+//     16-byte vectors.
+//
+// The tiled loop with zero-padded edge tiles and a barrier per tile follows
+// "Treinar LLM em Swift", sections "Passo 4" (threadgroup tiling) and
+// "Passo 7" (register tiling and double-buffered prefetch), re-designed for
+// 64-wide waves, 160 KiB of LDS and the CDNA4 MFMA units.
+#include "mxg_device.h"
+#include "mxg_internal.h"
+
+namespace mxg {
+namespace {
+
+enum Kind { kMX = 0, kF16 = 1, kDEQ = 2 };
+
+template <int KIND, int BM_, int BN_, int WM_, int WN_, bool AF4_, bool BF4_, bool BKN_>
+struct Cfg {
+  static constexpr int KIND_ = KIND;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool AF4 = AF4_, BF4 = BF4_, BKN = BKN_;
+  static constexpr bool SCALED = (KIND != kF16);
+  static constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
+  static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
+  static constexpr int RA = AF4 ? 64 : 128;          // LDS bytes per A row per slice
+  static constexpr int RB = BF4 ? 64 : 128;
+  static constexpr int KSLICE = (KIND == kF16) ? 64 : 128;  // K elements per slice
+  static constexpr int SZA = BM * RA, SZB = BN * RB;
+  static constexpr int SZSA = SCALED ? BM * 4 : 0, SZSB = SCALED ? BN * 4 : 0;
+  static constexpr int STAGE = SZA + SZB + SZSA + SZSB;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int NQA = SZA / 1024, NQB = SZB / 1024;  // 1 KiB wave copies per slice
+  static_assert(WM * WN == 4, "4 waves per workgroup");
+  static_assert(NQA % 4 == 0 && NQB % 4 == 0, "tile copies split evenly over 4 waves");
+  static_assert(BM <= 256 && BN <= 256, "one scale row per thread");
+  static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
+};
+
+struct Args {
+  const uint8_t* A;
+  const uint8_t* SA;
+  const uint8_t* B;
+  const uint8_t* SB;
+  float* C;
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int64_t lda, ldb;     // row strides in bytes of A and B (B: of its K x N rows when BKN)
+  int nsteps;           // slices, the last one possibly partial
+  int tail_a, tail_b;   // valid bytes per row in the last slice (== RA/RB when full)
+  int scale_aligned;    // scale rows are 4-byte aligned and K % 128 == 0
+};
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+template <class T>
+struct Kernel {
+  // ---- copy of one operand slice: BM rows x R bytes, direct to LDS --------
+  template <int R, int NQ>
+  static __device__ __forceinline__ void issue_rows(const uint8_t* __restrict__ g, int64_t ld, int row0,
+                                                    int rows_valid, int64_t col_byte, uint8_t* lds, int wave,
+                                                    int lane) {
+#pragma unroll
+    for (int t = 0; t < NQ / 4; t++) {
+      const int q = wave + 4 * t;
+      const int o = q * 1024 + lane * 16;
+      const int row = o / R;
+      const int pch = (o % R) >> 4;
+      const int c = pch ^ (R == 128 ? swz8(row) : swz4(row));
+      const int grow = min(row0 + row, rows_valid - 1);
+      // a chunk reaching past the end of the row (partial last slice) reads
+      // the slice's first chunk instead, which is always in bounds; it is
+      // zeroed before use
+      const int cc = (col_byte + c * 16 + 16 <= ld) ? c : 0;
+      copy16_to_lds(g + (int64_t)grow * ld + col_byte + cc * 16, lds + q * 1024);
+    }
+  }
+  // In a partial last slice, chunks past K were copied from in-bounds but
+  // meaningless bytes; each lane overwrites the chunks it copied with zeros.
+  template <int R, int NQ>
+  static __device__ __forceinline__ void zero_tail(int valid_bytes, uint8_t* lds, int wave, int lane) {
+#pragma unroll
+    for (int t = 0; t < NQ / 4; t++) {
+      const int q = wave + 4 * t;
+      const int o = q * 1024 + lane * 16;
+      const int row = o / R;
+      const int pch = (o % R) >> 4;
+      const int c = pch ^ (R == 128 ? swz8(row) : swz4(row));
+      if (c * 16 >= valid_bytes) *reinterpret_cast<v4i*>(lds + o) = v4i{0, 0, 0, 0};
+    }
+  }
+  // ---- scale bytes of one slice: 4 per row, through a register -----------
+  static __device__ __forceinline__ uint32_t load_scales(const uint8_t* __restrict__ s, int rows_valid, int row0,
+                                                         int nrows, int tid, int K, int step, bool aligned) {
+    if (tid >= nrows) return 0u;
+    const int grow = min(row0 + tid, rows_valid - 1);
+    const int nb = K >> 5;
+    const uint8_t* p = s + (int64_t)grow * nb + step * 4;
+    if (aligned) return *reinterpret_cast<const uint32_t*>(p);
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint32_t b = (step * 4 + i < nb) ? (uint32_t)p[i] : 127u;  // pad blocks: 2^0 times zero codes
+      v |= b << (8 * i);
+    }
+    return v;
+  }
+
+  // ---- fp16 right operand stored K x N: register transpose into N x K ----
+  struct KNRegs {
+    v4i v[2][4];
+  };
+  static __device__ __forceinline__ void load_kn(const Args& a, int n0, int step, int tid, KNRegs& r) {
+    // blocks of 4 (k) x 8 (n) halves; 16 * BN/8 blocks per slice
+    constexpr int NBLK = 16 * (T::BN / 8);
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int blk = tid + 256 * j;
+      if (blk >= NBLK) break;
+      const int kb4 = blk & 15, nb8 = blk >> 4;
+      const int n = n0 + nb8 * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) {
+        const int k = step * 64 + kb4 * 4 + kk;
+        v4i val = {0, 0, 0, 0};
+        if (k < a.K) {
+          const uint16_t* row = B + (int64_t)k * a.N;
+          if (n + 7 < a.N && (a.N & 7) == 0) {
+            val = *reinterpret_cast<const v4i*>(row + n);
+          } else {
+            uint16_t h[8];
+#pragma unroll
+            for (int t = 0; t < 8; t++) h[t] = (n + t < a.N) ? row[n + t] : (uint16_t)0;
+#pragma unroll
+            for (int t = 0; t < 4; t++) val[t] = (int)((uint32_t)h[2 * t] | ((uint32_t)h[2 * t + 1] << 16));
+          }
+        }
+        r.v[j][kk] = val;
+      }
+    }
+  }
+  static __device__ __forceinline__ void commit_kn(const KNRegs& r, uint8_t* ldsB, int tid) {
+    constexpr int NBLK = 16 * (T::BN / 8);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int blk = tid + 256 * j;
+      if (blk >= NBLK) break;
+      const int kb4 = blk & 15, nb8 = blk >> 4;
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        // column t of the 4 x 8 block: halves (k0..k0+3, n = nb8*8 + t)
+        uint32_t h[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+          const uint32_t w = (uint32_t)r.v[j][kk][t >> 1];
+          h[kk] = (t & 1) ? (w >> 16) : (w & 0xffffu);
+        }
+        const int row = nb8 * 8 + t;
+        const int chunk = kb4 >> 1;
+        const int off = row * 128 + ((chunk ^ swz8(row)) << 4) + (kb4 & 1) * 8;
+        *reinterpret_cast<v2i*>(ldsB + off) = v2i{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16))};
+      }
+    }
+  }
+
+  // ---- fragment reads ------------------------------------------------------
+  // fp8 / fp16 rows: chunks g and 4 + g; fp4 rows: chunk g.
+  template <int R>
+  static __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row, int g) {
+    v8i f;
+    if (R == 128) {
+      const int s = swz8(row);
+      const v4i lo = *reinterpret_cast<const v4i*>(lds + row * 128 + ((g ^ s) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(lds + row * 128 + (((4 + g) ^ s) << 4));
+      f = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const v4i lo = *reinterpret_cast<const v4i*>(lds + row * 64 + ((g ^ swz4(row)) << 4));
+      f = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+    return f;
+  }
+
+  // E4M3 byte pair -> two fp16 values times 2^(scale-127), rounded to fp16.
+  static __device__ __forceinline__ uint32_t deq_pair(uint32_t two, uint32_t sbyte) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const uint32_t c = (two >> (8 * i)) & 0xffu;
+      // s.eeee.mmm << 7 is the binary16 pattern of (E4M3 value) * 2^-8,
+      // subnormals included
+      const uint16_t hb = (uint16_t)(((c & 0x80u) << 8) | ((c & 0x7fu) << 7));
+      float v = (float)__builtin_bit_cast(_Float16, hb);
+      v = __builtin_ldexpf(v, (int)sbyte - 119);
+      if ((c & 0x7fu) == 0x7fu || sbyte == 255u) v = __builtin_nanf("");
+      const _Float16 h = (_Float16)v;
+      out |= (uint32_t)__builtin_bit_cast(uint16_t, h) << (16 * i);
+    }
+    return out;
+  }
+  // 32 E4M3 codes of one lane (two 16-byte chunks) -> 4 x 8 fp16 values;
+  // chunk 0 belongs to block g/2, chunk 1 to block 2 + g/2 of the slice.
+  static __device__ __forceinline__ void deq_frag(const v8i& f, uint32_t sdw, int g, v8h out[4]) {
+    const uint32_t s0 = (sdw >> (8 * (g >> 1))) & 0xffu;
+    const uint32_t s1 = (sdw >> (8 * (2 + (g >> 1)))) & 0xffu;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint32_t sb = (q < 2) ? s0 : s1;
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const uint32_t word = (uint32_t)f[2 * q + t];
+        w[2 * t] = deq_pair(word & 0xffffu, sb);
+        w[2 * t + 1] = deq_pair(word >> 16, sb);
+      }
+      out[q] = __builtin_bit_cast(v8h, v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+    }
+  }
+
+  static __device__ __forceinline__ void run(const Args& a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int wi = wave / T::WN, wj = wave % T::WN;
+    int tm, tn;
+    tile_of_block(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+    v4f acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; i++)
+#pragma unroll
+      for (int j = 0; j < T::FN; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t sa_reg = 0, sb_reg = 0;
+    KNRegs kn;
+
+    auto stage_ptr = [&](int st) { return smem + st * T::STAGE; };
+    auto issue = [&](int step, int st) {
+      uint8_t* base = stage_ptr(st);
+      issue_rows<T::RA, T::NQA>(a.A, a.lda, m0, a.M, (int64_t)step * T::RA, base, wave, lane);
+      if (T::BKN)
+        load_kn(a, n0, step, tid, kn);
+      else
+        issue_rows<T::RB, T::NQB>(a.B, a.ldb, n0, a.N, (int64_t)step * T::RB, base + T::SZA, wave, lane);
+      if (T::SCALED) {
+        sa_reg = load_scales(a.SA, a.M, m0, T::BM, tid, a.K, step, a.scale_aligned);
+        sb_reg = load_scales(a.SB, a.N, n0, T::BN, tid, a.K, step, a.scale_aligned);
+      }
+    };
+    auto commit = [&](int step, int st) {
+      uint8_t* base = stage_ptr(st);
+      if (step == a.nsteps - 1) {
+        if (a.tail_a < T::RA) zero_tail<T::RA, T::NQA>(a.tail_a, base, wave, lane);
+        if (!T::BKN && a.tail_b < T::RB) zero_tail<T::RB, T::NQB>(a.tail_b, base + T::SZA, wave, lane);
+      }
+      if (T::BKN) commit_kn(kn, base + T::SZA, tid);
+      if (T::SCALED) {
+        if (tid < T::BM) reinterpret_cast<uint32_t*>(base + T::SZA + T::SZB)[tid] = sa_reg;
+        if (tid < T::BN) reinterpret_cast<uint32_t*>(base + T::SZA + T::SZB + T::SZSA)[tid] = sb_reg;
+      }
+    };
+
+    issue(0, 0);
+    for (int step = 0; step < a.nsteps; step++) {
+      const int st = step & 1;
+      wait_vmem();
+      commit(step, st);
+      __syncthreads();
+      if (step + 1 < a.nsteps) issue(step + 1, st ^ 1);
+
+      const uint8_t* la = stage_ptr(st);
+      const uint8_t* lb = la + T::SZA;
+      const uint32_t* lsa = reinterpret_cast<const uint32_t*>(lb + T::SZB);
+      const uint32_t* lsb = lsa + T::BM;
+
+      if constexpr (T::KIND_ == kMX) {
+        v8i af[T::FM], bf[T::FN];
+        int sa[T::FM], sb[T::FN];
+#pragma unroll
+        for (int i = 0; i < T::FM; i++) {
+          const int row = wi * T::TM + i * 16 + r;
+          af[i] = read_frag<T::RA>(la, row, g);
+          sa[i] = (int)(lsa[row] >> (8 * g));
+        }
+#pragma unroll
+        for (int j = 0; j < T::FN; j++) {
+          const int row = wj * T::TN + j * 16 + r;
+          bf[j] = read_frag<T::RB>(lb, row, g);
+          sb[j] = (int)(lsb[row] >> (8 * g));
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; i++)
+#pragma unroll
+          for (int j = 0; j < T::FN; j++)
+            acc[i][j] = mfma_scaled_16x16x128<T::BF4 ? kFmtFp4 : kFmtFp8, T::AF4 ? kFmtFp4 : kFmtFp8>(
+                bf[j], af[i], acc[i][j], sb[j], sa[i]);
+      } else if constexpr (T::KIND_ == kF16) {
+        v8i af[T::FM], bf[T::FN];
+#pragma unroll
+        for (int i = 0; i < T::FM; i++) af[i] = read_frag<128>(la, wi * T::TM + i * 16 + r, g);
+#pragma unroll
+        for (int j = 0; j < T::FN; j++) bf[j] = read_frag<128>(lb, wj * T::TN + j * 16 + r, g);
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int i = 0; i < T::FM; i++)
+#pragma unroll
+            for (int j = 0; j < T::FN; j++) {
+              const v4i bq = h ? v4i{bf[j][4], bf[j][5], bf[j][6], bf[j][7]} : v4i{bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
+              const v4i aq = h ? v4i{af[i][4], af[i][5], af[i][6], af[i][7]} : v4i{af[i][0], af[i][1], af[i][2], af[i][3]};
+              acc[i][j] = mfma_f16_16x16x32(__builtin_bit_cast(v8h, bq), __builtin_bit_cast(v8h, aq), acc[i][j]);
+            }
+      } else {  // kDEQ
+        v8h ah[T::FM][4], bh[T::FN][4];
+#pragma unroll
+        for (int i = 0; i < T::FM; i++) {
+          const int row = wi * T::TM + i * 16 + r;
+          deq_frag(read_frag<128>(la, row, g), lsa[row], g, ah[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < T::FN; j++) {
+          const int row = wj * T::TN + j * 16 + r;
+          deq_frag(read_frag<128>(lb, row, g), lsb[row], g, bh[j]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int i = 0; i < T::FM; i++)
+#pragma unroll
+            for (int j = 0; j < T::FN; j++) acc[i][j] = mfma_f16_16x16x32(bh[j][q], ah[i][q], acc[i][j]);
+      }
+    }
+
+    // ---- epilogue: lane (g, r) holds C[m][n .. n+3] -------------------------
+    const bool vec_ok = (a.N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < T::FM; i++) {
+      const int m = m0 + wi * T::TM + i * 16 + r;
+      if (m >= a.M) continue;
+      float* crow = a.C + (int64_t)m * a.N;
+#pragma unroll
+      for (int j = 0; j < T::FN; j++) {
+        const int n = n0 + wj * T::TN + j * 16 + 4 * g;
+        if (vec_ok && n + 3 < a.N) {
+          *reinterpret_cast<v4f*>(crow + n) = acc[i][j];
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; t++)
+            if (n + t < a.N) crow[n + t] = acc[i][j][t];
+        }
+      }
+    }
+  }
+};
+
+template <class T, int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void tiled_kernel(Args a) {
+  Kernel<T>::run(a);
+}
+
+template <class T, int WPE>
+hipError_t launch(const Args& a0, hipStream_t stream) {
+  Args a = a0;
+  a.tiles_m = (a.M + T::BM - 1) / T::BM;
+  a.tiles_n = (a.N + T::BN - 1) / T::BN;
+  a.nsteps = (a.K + T::KSLICE - 1) / T::KSLICE;
+  const int rem = a.K - (a.nsteps - 1) * T::KSLICE;  // K elements in the last slice
+  auto bytes = [&](bool f4, bool f16, int elems) { return f16 ? elems * 2 : (f4 ? elems / 2 : elems); };
+  a.tail_a = bytes(T::AF4, !T::SCALED, rem);
+  a.tail_b = bytes(T::BF4, !T::SCALED, rem);
+  const int64_t nt = (int64_t)a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((tiled_kernel<T, WPE>), dim3((unsigned)nt), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+Args make_args(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M, int64_t N,
+               int64_t K) {
+  Args a{};
+  a.A = (const uint8_t*)A;
+  a.SA = SA;
+  a.B = (const uint8_t*)B;
+  a.SB = SB;
+  a.C = C;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  return a;
+}
+
+// Configurations: 256 x 256 tiles (one workgroup per CU, 128 x 128 per wave)
+// for large outputs, 128 x 128 (two workgroups per CU) otherwise.
+using MxBig88 = Cfg<kMX, 256, 256, 2, 2, false, false, false>;
+using MxBig84 = Cfg<kMX, 256, 256, 2, 2, false, true, false>;
+using MxBig44 = Cfg<kMX, 256, 256, 2, 2, true, true, false>;
+using MxMid88 = Cfg<kMX, 128, 128, 2, 2, false, false, false>;
+using MxMid84 = Cfg<kMX, 128, 128, 2, 2, false, true, false>;
+using MxMid44 = Cfg<kMX, 128, 128, 2, 2, true, true, false>;
+using F16Big = Cfg<kF16, 256, 256, 2, 2, false, false, false>;
+using F16Mid = Cfg<kF16, 128, 128, 2, 2, false, false, false>;
+using F16MidKN = Cfg<kF16, 128, 128, 2, 2, false, false, true>;
+using DeqMid = Cfg<kDEQ, 128, 128, 2, 2, false, false, false>;
+
+bool use_big_tiles(int64_t M, int64_t N) {
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return big_tiles >= 256;
+}
+
+}  // namespace
+
+hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                           int64_t N, int64_t K, int fmt, hipStream_t stream) {
+  Args a = make_args(A, SA, B, SB, C, M, N, K);
+  const bool af4 = (fmt == 2), bf4 = (fmt != 0);
+  a.lda = af4 ? K / 2 : K;
+  a.ldb = bf4 ? K / 2 : K;
+  a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
+  const bool big = use_big_tiles(M, N);
+  if (fmt == 0) return big ? launch<MxBig88, 1>(a, stream) : launch<MxMid88, 2>(a, stream);
+  if (fmt == 1) return big ? launch<MxBig84, 1>(a, stream) : launch<MxMid84, 2>(a, stream);
+  return big ? launch<MxBig44, 1>(a, stream) : launch<MxMid44, 2>(a, stream);
+}
+
+hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
+                            int b_is_nk, hipStream_t stream) {
+  Args a = make_args(A, nullptr, B, nullptr, C, M, N, K);
+  a.lda = K * 2;
+  if (!b_is_nk) {
+    a.ldb = N * 2;
+    return launch<F16MidKN, 2>(a, stream);
+  }
+  a.ldb = K * 2;
+  return use_big_tiles(M, N) ? launch<F16Big, 1>(a, stream) : launch<F16Mid, 2>(a, stream);
+}
+
+hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream) {
+  Args a = make_args(A, SA, B, SB, C, M, N, K);
+  a.lda = K;
+  a.ldb = K;
+  a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
+  return launch<DeqMid, 2>(a, stream);
+}
+
+}  // namespace mxg

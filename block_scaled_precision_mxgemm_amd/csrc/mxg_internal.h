@@ -1,0 +1,26 @@
+// mxg_internal.h - host-side launchers behind the C ABI (not exported).
+// Every launcher assumes validated arguments and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S,
+                           hipStream_t stream);
+
+// fmt: 0 = fp8 x fp8, 1 = fp8 x fp4, 2 = fp4 x fp4
+hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                           int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                            int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
+                            int b_is_nk, hipStream_t stream);
+hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream);
+
+// Largest M served by the split-K streaming kernel.
+constexpr int64_t kSkinnyMaxM = 64;
+
+}  // namespace mxg

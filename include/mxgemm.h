@@ -1,0 +1,157 @@
+/*
+ * mxgemm.h - C ABI of the MI355X (gfx950) block-scaled matrix multiply library.
+ *
+ * The operation:  C[i][j] = sum_b 2^(sA[i][b]-127) * 2^(sB[j][b]-127)
+ *                           * sum_{k in block b} a[i][k] * b[j][k]
+ * with A (M x K) and B (N x K) stored as low-precision codes (FP8 E4M3, or FP4
+ * E2M1 packed two per byte) plus one UE8M0 scale byte per 32 consecutive
+ * K elements, and C (M x N) in fp32.  Operand model: "Metal tensors でカスタム
+ * 機械学習オペレーションを最適化する" (WWDC26 session 330 summary), sections
+ * "多平面 tensor" and "Scale Factor 付き量子化 tensor を作成する" - a data plane
+ * plus an E8M0 scale plane with one scale per block of 32 along the innermost
+ * (reduction) dimension; section "スライスと量子化行列乗算" - the quantized
+ * matmul consumes both planes, dequantization included.  The same session's
+ * transcript, "Metal 텐서로 맞춤형 머신 러닝 연산 최적화하기", chapters
+ * "Multi-plane tensors" and "Quantized matrix multiplication".
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) owned
+ *     by the caller; the library never allocates, frees or retains them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously in stream order; nothing synchronizes.  A
+ *     fault inside a kernel surfaces at the caller's next synchronization.
+ *   - Arguments are validated before anything is launched; on error nothing is
+ *     enqueued and a nonzero MXG_* status is returned.  No exceptions cross the
+ *     ABI and nothing is printed.
+ *   - Layouts are row-major.  Every operand row runs along K (K contiguous),
+ *     so A is M x K and B is N x K ("transposed right operand"); the scale
+ *     planes are M x K/32 and N x K/32 bytes, row-major, and use the same row
+ *     order as their data planes.
+ *   - E4M3 is the OCP "FN" variant (bias 7, max 448, NaN = S.1111.111, no
+ *     infinity).  E2M1 codes are packed with the even K index in the low
+ *     nibble.  UE8M0 byte e means 2^(e-127); e = 255 is NaN and propagates.
+ *   - Data pointers (codes, fp16, fp32) must be 16-byte aligned (the kernels
+ *     move operands with 16-byte loads); scale pointers need no alignment.
+ *     The 128-byte row alignment the RIGEL summary reports for Metal inline
+ *     tensors ("Resumo Técnico: RIGEL", section 3) is not required here.
+ *   - The library runs on gfx950 only; other devices get MXG_EUNSUPPORTED.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MXG_OK 0
+#define MXG_EINVAL 1         /* null pointer, non-positive or oversized dim, K % 32 != 0, bad enum */
+#define MXG_EALIGN 2         /* a data pointer is not 16-byte aligned */
+#define MXG_EUNSUPPORTED 3   /* current device is not gfx950 */
+#define MXG_EHIP 4           /* the HIP runtime reported an error at launch */
+
+/* Element formats (values equal the MFMA operand-format ids). */
+#define MXG_ELEM_E4M3 0
+#define MXG_ELEM_E2M1 4
+
+/* Operand-format pairs for mxgemm_run: (A element, B element). */
+#define MXG_FMT_FP8_FP8 0
+#define MXG_FMT_FP8_FP4 1
+#define MXG_FMT_FP4_FP4 2
+
+/* Largest accepted M, N (rows) and K. */
+#define MXG_MAX_DIM (1 << 20)
+
+/*
+ * mxgemm_quantize - fp32 rows -> block-scaled codes plus UE8M0 scales.
+ *
+ * For every row r and every block b of 32 consecutive elements along K:
+ *   amax = max |X[r][32b .. 32b+31]|;
+ *   e    = floor(log2(amax)) - emax  (emax = 8 for E4M3, 2 for E2M1),
+ *          clamped to [-127, 127]; e = -127 when amax = 0;
+ *   S[r][b] = e + 127;
+ *   Q[r][k] = round-to-nearest-even(X[r][k] * 2^-e), saturated to +-448
+ *             (E4M3) or +-6 (E2M1), sign kept (-0 -> 0x80 / 0x8).
+ * A block holding a NaN or an infinity gets S = 255 (NaN) and zero codes.
+ * E4M3 saturating rather than overflowing follows "Resumo Técnico: RIGEL",
+ * section 3 (saturation); one E8M0 scale per 32 elements follows the WWDC26
+ * session 330 summary, section "Scale Factor 付き量子化 tensor を作成する".
+ * The exponent rule is the OCP Microscaling convention.
+ *
+ *   X     device, rows x K fp32, row-major, 16-byte aligned (read only)
+ *   rows  >= 1;  K >= 32, K % 32 == 0
+ *   elem  MXG_ELEM_E4M3 (Q: rows x K bytes) or MXG_ELEM_E2M1 (Q: rows x K/2
+ *         bytes, even k in the low nibble); Q 16-byte aligned (written)
+ *   S     device, rows x K/32 bytes (written)
+ * Returns MXG_OK or an error status.  The output is bit-for-bit deterministic.
+ */
+int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
+                    void *Q, uint8_t *S, void *stream);
+
+/*
+ * mxgemm_run - C = (A * 2^sA)(B * 2^sB)^T in fp32 on the scaled MFMA path.
+ *
+ *   A, scaleA  device; A is M x K codes (E4M3: M*K bytes; E2M1: M*K/2 bytes),
+ *              scaleA is M x K/32 UE8M0 bytes
+ *   B, scaleB  device; B is N x K codes, scaleB is N x K/32 bytes
+ *   C          device, M x N fp32 row-major, 16-byte aligned; overwritten
+ *   M, N       >= 1 (any value; edges are masked); K >= 32, K % 32 == 0
+ *   fmt        MXG_FMT_FP8_FP8, MXG_FMT_FP8_FP4 or MXG_FMT_FP4_FP4
+ * Each 32-element block product is formed by CDNA4's scaled fp8/fp4 MFMA,
+ * which applies the E8M0 scales itself; partial sums accumulate in fp32.
+ * Small M (M <= 64) takes a split-K streaming kernel for decode shapes.
+ * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the
+ * workloads this library is tested on (the MFMA's internal alignment of
+ * wide-range products is the dominant error term; see the design notes).
+ * Returns MXG_OK or an error status.  The result is deterministic.
+ */
+int mxgemm_run(const void *A, const uint8_t *scaleA,
+               const void *B, const uint8_t *scaleB,
+               float *C, int64_t M, int64_t N, int64_t K, int fmt, void *stream);
+
+/*
+ * fp16gemm_run - dense fp16 comparison GEMM, fp32 accumulate and output.
+ *
+ *   A  device, M x K binary16 (uint16 bits), row-major, 16-byte aligned
+ *   B  device, binary16; K x N row-major when b_is_nk == 0,
+ *      N x K row-major (same layout as the MX operands) when b_is_nk == 1
+ *   C  device, M x N fp32 row-major, 16-byte aligned; overwritten
+ *   M, N >= 1; K >= 8, K % 8 == 0
+ * This is the half-precision rung of "Treinar LLM em Swift: multiplicação de
+ * matrizes do Gflop/s ao Tflop/s", section "Passo 6" (FP16 instead of FP32),
+ * and the fp16 baseline against which "Resumo Técnico: RIGEL", section
+ * "Metodologia: O Harness RIGEL", judges low precision as accelerated
+ * (>= 1.5x fp16 throughput) or emulated.
+ */
+int fp16gemm_run(const uint16_t *A, const uint16_t *B, float *C,
+                 int64_t M, int64_t N, int64_t K, int b_is_nk, void *stream);
+
+/*
+ * mxgemm_run_dequant_fp16 - ablation of mxgemm_run (same arguments, fmt must
+ * be MXG_FMT_FP8_FP8): each operand fragment is dequantized in registers to
+ * fp16 (code * 2^(scale-127), rounded to nearest-even fp16) and multiplied
+ * with the fp16 MFMA.  This is the register-resident custom-dequantization
+ * route of the WWDC26 session 330 transcript, chapter "Quantized matrix
+ * multiplication" (dequantize into a cooperative tensor instead of bouncing
+ * through threadgroup memory).  Exact only while every code * 2^(scale-127)
+ * is an fp16 value (E4M3 scale bytes within [112, 134]); outside that range
+ * fp16 rounding, overflow or underflow adds error.  Kept for measurement.
+ */
+int mxgemm_run_dequant_fp16(const void *A, const uint8_t *scaleA,
+                            const void *B, const uint8_t *scaleB,
+                            float *C, int64_t M, int64_t N, int64_t K, int fmt,
+                            void *stream);
+
+/* 1 if the current HIP device is gfx950, 0 if not, negative MXG_* on error. */
+int mxgemm_device_supported(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *mxgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

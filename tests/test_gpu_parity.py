@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Quantizer: bit-exact.  GEMMs: every element within |C - C_ref| <= K * 2^-24 *
+sum_k |a_ik b_jk| (fp8/fp4 products times power-of-two scales, and fp16
+products, are exact in fp32, so the bound is that of fp32 accumulation), and
+NaN positions identical.  The fp16 and dequantize-ablation paths meet that
+bound everywhere; the scaled-MFMA path meets it on every full-size workload
+(test_gpu_workloads.py) and gets the per-dtype MFMA_ALIGNMENT_TERMS allowance
+in the small edge cases below.  Outputs start as NaN canaries, so unwritten
+tiles fail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_precision_mxgemm_amd import inputs as mxin
+from gpu_util import (DEV, FMT_ELEMS, binding, gpu_mx, gpu_quantize, mx_case, mx_sources, nan_canary, say,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    b = binding()
+    assert b.mxgemm_device_supported(), "device is not gfx950"
+    yield
+
+
+# ------------------------------------------------------------------ quantizer
+
+@pytest.mark.parametrize("elem", [oracle.E4M3, oracle.E2M1])
+@pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (256, 256), (513, 4096)])
+def test_quantize_bitexact_normal(elem, rows, K):
+    say("quantize", elem, rows, K)
+    rng = np.random.default_rng(rows * 7 + K)
+    x = (rng.standard_normal((rows, K)) * np.exp2(rng.integers(-20, 20, size=(rows, K // 32))).repeat(32, 1)
+         ).astype(np.float32)
+    q, s = gpu_quantize(x, elem)
+    qo, so = oracle.quantize(x, elem)
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("elem", [oracle.E4M3, oracle.E2M1])
+def test_quantize_bitexact_bit_patterns(elem):
+    """Random fp32 bit patterns (all exponents, subnormals, signed zeros) with a
+    fixed block maximum, so every element is rounded at a known scale; plus
+    blocks made only of subnormals, zeros, NaN and infinity."""
+    say("quantize bit patterns", elem)
+    rng = np.random.default_rng(1234 + elem)
+    rows = 4096
+    bits = rng.integers(0, 2 ** 32, size=(rows, 64), dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32).copy()
+    # keep finite patterns, cap magnitude below the block maximum of each block
+    bad = ~np.isfinite(x)
+    x[bad] = 0.0
+    amax = np.float32(256.0 * 2.0 ** 20) if elem == oracle.E4M3 else np.float32(4.0 * 2.0 ** 20)
+    x = np.clip(x, -amax, amax)
+    x[:, 0] = amax
+    x[:, 32] = -amax
+    # rows of subnormals only, zero rows, non-finite rows
+    x[100:200] = (rng.integers(0, 2 ** 23, size=(100, 64), dtype=np.uint64).astype(np.uint32)
+                  | (rng.integers(0, 2, size=(100, 64)).astype(np.uint32) << 31)).view(np.float32)
+    x[200:210] = 0.0
+    x[210:215] = -0.0
+    x[215, 3] = np.nan
+    x[216, 40] = np.inf
+    x[217, 0] = -np.inf
+    # a dense grid of values up to the block maximum
+    grid = np.linspace(-amax, amax, 64 * 100, dtype=np.float32).reshape(100, 64)
+    x[300:400] = grid
+    x[300:400, 0] = amax
+    x[300:400, 32] = amax
+    q, s = gpu_quantize(x, elem)
+    qo, so = oracle.quantize(x, elem)
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_all_e4m3_ties():
+    """Every midpoint between adjacent E4M3 values (and its fp32 neighbours)
+    at scale 2^0: the ties-to-even decisions must match the oracle."""
+    say("quantize ties")
+    vals = np.unique(torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy())
+    mids = (vals[:-1] + vals[1:]) / 2
+    cand = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1000), vals, [460, 464, 470, 480]])
+    cand = cand.astype(np.float32)
+    n = (len(cand) + 30) // 31
+    x = np.zeros((n, 32), dtype=np.float32)
+    x[:, 0] = 256.0
+    flat = np.zeros(n * 31, dtype=np.float32)
+    flat[:len(cand)] = cand
+    x[:, 1:] = flat.reshape(n, 31)
+    x = np.concatenate([x, -x])
+    q, s = gpu_quantize(x, oracle.E4M3)
+    qo, so = oracle.quantize(x, oracle.E4M3)
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+# ------------------------------------------------------------ MX GEMM, small
+
+SMALL_SHAPES = [
+    (256, 256, 256),   # the 256^3 workload's size
+    (37, 45, 96),      # ragged in M, N and K (K % 128 != 0)
+    (129, 200, 160),
+    (300, 257, 384),   # spans several 128-tiles plus tails
+    (520, 530, 1056),  # several 256-tiles when large tiles are chosen
+    (65, 1000, 512),   # just above the skinny limit
+]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+def test_mx_gemm_small_full(fmt, M, N, K):
+    say("mx small", fmt, M, N, K)
+    a32, b32 = mx_sources("mxfp8_256", M, N, K, seed=M * 1000 + N + K + fmt)
+    r, _ = mx_case(a32, b32, fmt)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 512), (16, 1000, 1024), (17, 64, 96), (33, 500, 4096),
+                                   (64, 129, 256), (5, 28, 32)])
+def test_mx_gemm_skinny_full(fmt, M, N, K):
+    say("mx skinny", fmt, M, N, K)
+    a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=M + N + K)
+    r, _ = mx_case(a32, b32, fmt)
+    assert r["ok"], r
+
+
+def test_mx_gemm_large_tiles_full():
+    """A shape that takes the 256 x 256 tile kernel (>= 256 tiles), checked in full."""
+    say("mx large tiles")
+    M, N, K = 4096, 4096, 256
+    a32, b32 = mx_sources("mxfp8_256", M, N, K, seed=77)
+    r, _ = mx_case(a32, b32, 0)
+    assert r["ok"], r
+
+
+def test_mx_blockpow2_recipe_full():
+    """Per-block magnitudes 2^U{-6..6}: scales vary block to block."""
+    say("mx blockpow2")
+    a32, b32 = mx_sources("mxfp8_2048", 256, 384, 512)
+    r, _ = mx_case(a32, b32, 0)
+    assert r["ok"], r
+
+
+def test_accumulator_width_on_gpu():
+    """The RIGEL accumulator example through the GPU quantizer and GEMM: one
+    448 and 127 terms of 2^-4 against ones must give exactly 455.9375."""
+    from conftest import read_golden_kv
+
+    say("accumulator width")
+    g = read_golden_kv("accumulator_width.txt")
+    K = int(g["K"])
+    a = np.zeros((16, K), dtype=np.float32)
+    a[:, 0] = g["terms_large"]
+    a[:, 1:1 + int(g["count_small"])] = g["terms_small"]
+    b = np.ones((16, K), dtype=np.float32)
+    for M in (16, 100):   # skinny and tiled kernels
+        aa = np.repeat(a[:1], M, axis=0)
+        qa, sa = gpu_quantize(aa, oracle.E4M3)
+        qb, sb = gpu_quantize(b, oracle.E4M3)
+        c = gpu_mx(qa, sa, qb, sb, 0, M, 16).cpu().numpy()
+        assert (c == np.float32(g["expected_total"])).all(), c[:2, :4]
+
+
+def test_nan_propagation():
+    say("nan propagation")
+    rng = np.random.default_rng(5)
+    for M in (8, 200):
+        N, K = 40, 256
+        a32 = rng.standard_normal((M, K)).astype(np.float32)
+        b32 = rng.standard_normal((N, K)).astype(np.float32)
+        qa, sa = gpu_quantize(a32, oracle.E4M3)
+        qb, sb = gpu_quantize(b32, oracle.E4M3)
+        sa[3, 2] = 255      # NaN scale in A row 3
+        qb[7, 100] = 0x7F   # NaN code in B row 7
+        c = gpu_mx(qa, sa, qb, sb, 0, M, N).cpu().numpy()
+        ref, ab = oracle.mx_gemm(qa.cpu().numpy(), sa.cpu().numpy(), 0, qb.cpu().numpy(), sb.cpu().numpy(), 0,
+                                 M, N, K)
+        r = oracle.gate(c, ref, ab, K)
+        assert r["ok"], r
+        assert np.isnan(c[3]).all() and np.isnan(c[:, 7]).all()
+
+
+def test_deterministic():
+    say("determinism")
+    a32, b32 = mx_sources("mxfp8_256", 300, 520, 1024, seed=9)
+    qa, sa = gpu_quantize(a32, 0)
+    qb, sb = gpu_quantize(b32, 0)
+    c1 = gpu_mx(qa, sa, qb, sb, 0, 300, 520).cpu().numpy()
+    c2 = gpu_mx(qa, sa, qb, sb, 0, 300, 520).cpu().numpy()
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+    q16, s16 = gpu_quantize(a32[:16], 0)
+    d1 = gpu_mx(q16, s16, qb, sb, 0, 16, 520).cpu().numpy()
+    d2 = gpu_mx(q16, s16, qb, sb, 0, 16, 520).cpu().numpy()
+    assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+
+
+# -------------------------------------------------------------- fp16 GEMM
+
+def _fp16_case(a16, b16, b_is_nk, points=None):
+    b = binding()
+    M, K = a16.shape
+    N = b16.shape[0] if b_is_nk else b16.shape[1]
+    out = nan_canary(M, N)
+    b.fp16gemm_run(to_dev(a16), to_dev(b16), b_is_nk, out=out)
+    torch.cuda.synchronize()
+    c = out.cpu().numpy()
+    ref, ab = oracle.fp16_gemm(a16.view(np.uint16), b16.view(np.uint16), M, N, K, int(b_is_nk), points=points)
+    got = c if points is None else c[points[0], points[1]]
+    return oracle.gate(got, ref, ab, K)
+
+
+def test_fp16_gemm_1024_full():
+    """The dense fp16 1024^3 workload (row-major A and B), every element."""
+    say("fp16 1024")
+    w = mxin.WORKLOADS["fp16_1024"]
+    a16, b16 = mxin.fp16_sources(w, b_is_nk=False)
+    r = _fp16_case(a16, b16, False)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("b_is_nk", [False, True])
+@pytest.mark.parametrize("M,N,K", [(37, 45, 72), (129, 200, 136), (300, 260, 512), (520, 530, 1032)])
+def test_fp16_gemm_ragged(b_is_nk, M, N, K):
+    say("fp16 ragged", b_is_nk, M, N, K)
+    w = mxin.WORKLOADS["fp16_1024"]
+    a16, b16 = mxin.fp16_sources(w, b_is_nk, M, N, K, seed=M + N + K)
+    r = _fp16_case(a16, b16, b_is_nk)
+    assert r["ok"], r
+
+
+def test_fp16_gemm_large_tiles_nk():
+    say("fp16 large tiles")
+    w = mxin.WORKLOADS["mxfp8_2048"]
+    a16, b16 = mxin.fp16_sources(w, True, 4096, 4096, 256, seed=3)
+    pts = mxin.sample_points(4096, 4096, 20000)
+    r = _fp16_case(a16, b16, True, points=pts)
+    assert r["ok"], r
+
+
+# ---------------------------------------------------- dequant ablation
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (129, 200, 160), (300, 257, 384)])
+def test_dequant_ablation_parity(M, N, K):
+    """N(0, 1) data keeps every scale byte within [112, 134], where the fp16
+    dequantization is exact, so the ablation meets the same bound."""
+    say("dequant", M, N, K)
+    a32, b32 = mx_sources("mxfp8_256", M, N, K, seed=M + 2 * N + K)
+    r, _ = mx_case(a32, b32, 0, dequant=True)
+    assert r["ok"], r

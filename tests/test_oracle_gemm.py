@@ -229,3 +229,24 @@ def test_gate_accepts_fp32_rounding_and_rejects_corruption():
     c_nan[0, 0] = np.nan
     r = oracle.gate(c_nan, C, ABS, K)
     assert not r["ok"] and r["nan_mismatch"] == 1
+
+
+def test_gate_allowance_keeps_detection():
+    """The scaled-MFMA allowance (extra terms in the bound) still rejects a
+    wrong scale byte and a flipped code on a realistic operand pair."""
+    rng = np.random.default_rng(13)
+    M, N, K = 32, 32, 1024
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((N, K)).astype(np.float32)
+    aq, as_ = oracle.quantize(a, oracle.E4M3)
+    bq, bs = oracle.quantize(b, oracle.E4M3)
+    C, ABS = oracle.mx_gemm(aq, as_, oracle.E4M3, bq, bs, oracle.E4M3, M, N, K)
+    assert oracle.gate(C.astype(np.float32), C, ABS, K, extra_terms=2048)["ok"]
+    as2 = as_.copy()
+    as2[4, 9] += 1
+    C2, _ = oracle.mx_gemm(aq, as2, oracle.E4M3, bq, bs, oracle.E4M3, M, N, K)
+    assert not oracle.gate(C2.astype(np.float32), C, ABS, K, extra_terms=2048)["ok"]
+    bq2 = bq.copy()
+    bq2[3, 100] ^= 0x40
+    C3, _ = oracle.mx_gemm(aq, as_, oracle.E4M3, bq2, bs, oracle.E4M3, M, N, K)
+    assert not oracle.gate(C3.astype(np.float32), C, ABS, K, extra_terms=2048)["ok"]
