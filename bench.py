@@ -1,0 +1,319 @@
+"""Benchmark of the MX GEMM path on one MI355X.
+
+Prints ONE JSON line on stdout.  The step is one mxgemm_run of the MXFP8
+8192 x 8192 x 8192 workload (E4M3 codes, UE8M0 scale per 32 K elements, fp32
+output) on operands already resident in HBM; `value` is its throughput in
+TFLOP/s (2*M*N*K per step).  The same run also measures the paired fp16 GEMM
+(fp8/fp16 ratio), the 2048^3 pair, the LLM-prefill shape, the MXFP4 decode
+shape (GB/s, weights rotated through more copies than the 256 MB MALL holds),
+the quantizer and the dequantize-to-fp16 ablation, and times the CPU oracle
+on a bounded sample of the headline workload.
+
+Timing: W untimed warm-up launches, then K launches between two HIP events
+recorded on the stream the kernels are launched on (torch's current stream),
+with a device synchronization before and after.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 GEMM TFLOP/s (% of fp8 peak) at 8192³; fp8/fp16 ratio; decode GB/s"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["block_scaled_precision_mxgemm_amd/csrc/gemm_tiled.hip",
+                  "block_scaled_precision_mxgemm_amd/csrc/gemm_skinny.hip",
+                  "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Average milliseconds per launch of fn() over `steps` launches."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(steps):
+        fn(i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def mx_operands(name, dev, elem_b=None):
+    import torch
+
+    from block_scaled_precision_mxgemm_amd import inputs as mxin
+    from block_scaled_precision_mxgemm_amd import mxgemm as mx
+
+    w = mxin.WORKLOADS[name]
+    a32, b32 = mxin.mx_sources(w)
+    ta = torch.from_numpy(a32).to(dev)
+    tb = torch.from_numpy(b32).to(dev)
+    del a32, b32
+    qa, sa = mx.mxgemm_quantize(ta, mx.E4M3)
+    qb, sb = mx.mxgemm_quantize(tb, mx.E2M1 if elem_b == "e2m1" else mx.E4M3)
+    torch.cuda.synchronize()
+    return w, ta, tb, qa, sa, qb, sb
+
+
+def cpu_baseline(qa, sa, qb, sb, w, budget_s: float):
+    """Time the oracle on a bounded sample of output points of the workload."""
+    import oracle
+    from block_scaled_precision_mxgemm_amd import inputs as mxin
+
+    a_q, a_s, b_q, b_s = (t.cpu().numpy() for t in (qa, sa, qb, sb))
+    rng = np.random.default_rng(11)
+    # calibrate: grow the sample until one pass takes >= 1 s, then scale to the budget
+    probe = 256
+    while True:
+        I = rng.integers(0, w.M, probe)
+        J = rng.integers(0, w.N, probe)
+        t0 = time.perf_counter()
+        oracle.mx_gemm(a_q, a_s, 0, b_q, b_s, 0, w.M, w.N, w.K, points=(I, J))
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or probe >= 4_000_000:
+            break
+        probe *= 4
+    npts = int(max(probe, min(16_000_000, probe * budget_s / max(dt, 1e-6))))
+    I = rng.integers(0, w.M, npts)
+    J = rng.integers(0, w.N, npts)
+    t0 = time.perf_counter()
+    oracle.mx_gemm(a_q, a_s, 0, b_q, b_s, 0, w.M, w.N, w.K, points=(I, J))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * w.K * npts
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d random output elements of the %dx%dx%d MXFP8 product (each a full K=%d float64 dot "
+                  "product over decoded E4M3 codes and UE8M0 scales), %.1f s wall" % (npts, w.M, w.N, w.K, w.K, dt),
+        "gflops": flops / dt / 1e9,
+    }
+
+
+def traffic_entry():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("mx_gemm_8192_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["all", "headline", "decode", "fp16"], default="all",
+                    help="run a subset (for profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_scaled_precision_mxgemm_amd import inputs as mxin
+    from block_scaled_precision_mxgemm_amd import mxgemm as mx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if not mx.mxgemm_device_supported():
+        raise SystemExit("device is not gfx950")
+    extra = {}
+
+    # ---------------- headline: MXFP8 8192^3 ---------------------------------
+    log("headline: generating and quantizing 8192^3 operands")
+    w, ta, tb, qa, sa, qb, sb = mx_operands("mxfp8_8192", dev)
+    M, N, K = w.M, w.N, w.K
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    flops = 2.0 * M * N * K
+    ms = time_launches(lambda i=0: mx.mxgemm_run(qa, sa, qb, sb, mx.FMT_FP8_FP8, out=c), args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log("mxfp8 8192^3: %.3f ms, %.1f TFLOP/s" % (ms, tflops))
+
+    if args.only in ("all", "headline"):
+        # quantizer: fp32 -> E4M3 codes + scales for the 8192 x 8192 A operand
+        qms = time_launches(lambda i=0: mx.mxgemm_quantize(ta, mx.E4M3, q=qa, s=sa), 20, 3)
+        qbytes = M * K * (4 + 1 + 1 / 32)
+        extra["quantize_8192x8192_e4m3"] = {"ms": qms, "GB/s": qbytes / (qms * 1e-3) / 1e9,
+                                            "hbm_frac": qbytes / (qms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    del ta, tb
+
+    if args.only in ("all", "fp16"):
+        # paired fp16 run on the same fp32 sources, N x K layout like the MX operands
+        a16, b16 = mxin.fp16_sources(w, b_is_nk=True)
+        ta16 = torch.from_numpy(a16).to(dev)
+        tb16 = torch.from_numpy(b16).to(dev)
+        del a16, b16
+        fms = time_launches(lambda i=0: mx.fp16gemm_run(ta16, tb16, True, out=c), max(5, args.steps // 2),
+                            max(2, args.warmup // 2))
+        f_tflops = flops / (fms * 1e-3) / 1e12
+        ratio = tflops / f_tflops
+        extra["fp16_8192"] = {"ms": fms, "TFLOP/s": f_tflops, "fp16_peak_frac": f_tflops / PEAK_FP16_TFLOPS}
+        extra["fp8_fp16_ratio_8192"] = ratio
+        extra["fp8_verdict_8192"] = "accelerated" if ratio >= 1.5 else "emulated"
+        log("fp16 8192^3: %.3f ms, %.1f TFLOP/s, ratio %.2f" % (fms, f_tflops, ratio))
+        del ta16, tb16
+
+    if args.only == "all":
+        # dequantize-to-fp16 ablation on the headline operands
+        dms = time_launches(lambda i=0: mx.mxgemm_run_dequant_fp16(qa, sa, qb, sb, mx.FMT_FP8_FP8, out=c), 5, 2)
+        extra["ablation_dequant_fp16_8192"] = {"ms": dms, "TFLOP/s": flops / (dms * 1e-3) / 1e12,
+                                               "scaled_mfma_speedup": dms / ms}
+
+    cpu = None
+    if not args.no_cpu_baseline and args.only == "all":
+        log("cpu baseline: timing the oracle on a sample")
+        cpu = cpu_baseline(qa, sa, qb, sb, w, args.cpu_seconds)
+    del c, qa, sa, qb, sb
+    torch.cuda.empty_cache()
+
+    if args.only == "all":
+        # 2048^3 pair (the RIGEL ratio point) ---------------------------------
+        w3, ta, tb, qa3, sa3, qb3, sb3 = mx_operands("mxfp8_2048", dev)
+        c3 = torch.empty((w3.M, w3.N), dtype=torch.float32, device=dev)
+        f3 = 2.0 * w3.M * w3.N * w3.K
+        ms3 = time_launches(lambda i=0: mx.mxgemm_run(qa3, sa3, qb3, sb3, 0, out=c3), 200, 20)
+        a16, b16 = mxin.fp16_sources(w3, b_is_nk=True)
+        ta16, tb16 = torch.from_numpy(a16).to(dev), torch.from_numpy(b16).to(dev)
+        fms3 = time_launches(lambda i=0: mx.fp16gemm_run(ta16, tb16, True, out=c3), 200, 20)
+        extra["mxfp8_2048"] = {"ms": ms3, "TFLOP/s": f3 / (ms3 * 1e-3) / 1e12}
+        extra["fp16_2048"] = {"ms": fms3, "TFLOP/s": f3 / (fms3 * 1e-3) / 1e12}
+        extra["fp8_fp16_ratio_2048"] = fms3 / ms3
+        del ta, tb, qa3, sa3, qb3, sb3, ta16, tb16, c3
+
+        # fp16 1024^3, row-major A and B ---------------------------------------
+        w2 = mxin.WORKLOADS["fp16_1024"]
+        a16, b16 = mxin.fp16_sources(w2, b_is_nk=False)
+        ta16, tb16 = torch.from_numpy(a16).to(dev), torch.from_numpy(b16).to(dev)
+        c2 = torch.empty((w2.M, w2.N), dtype=torch.float32, device=dev)
+        ms2 = time_launches(lambda i=0: mx.fp16gemm_run(ta16, tb16, False, out=c2), 500, 50)
+        extra["fp16_1024_kn"] = {"ms": ms2, "TFLOP/s": 2.0 * 1024 ** 3 / (ms2 * 1e-3) / 1e12}
+        del ta16, tb16, c2
+
+        # MXFP8 256^3 -----------------------------------------------------------
+        w1, ta, tb, qa1, sa1, qb1, sb1 = mx_operands("mxfp8_256", dev)
+        c1 = torch.empty((256, 256), dtype=torch.float32, device=dev)
+        ms1 = time_launches(lambda i=0: mx.mxgemm_run(qa1, sa1, qb1, sb1, 0, out=c1), 500, 50)
+        extra["mxfp8_256"] = {"ms": ms1, "TFLOP/s": 2.0 * 256 ** 3 / (ms1 * 1e-3) / 1e12,
+                              "note": "launch-latency bound"}
+        del ta, tb, qa1, sa1, qb1, sb1, c1
+
+        # LLM prefill 8192 x 14336 x 4096 --------------------------------------
+        w4, ta, tb, qa4, sa4, qb4, sb4 = mx_operands("prefill_8192x14336x4096", dev)
+        del ta, tb
+        c4 = torch.empty((w4.M, w4.N), dtype=torch.float32, device=dev)
+        f4 = 2.0 * w4.M * w4.N * w4.K
+        ms4 = time_launches(lambda i=0: mx.mxgemm_run(qa4, sa4, qb4, sb4, 0, out=c4), 20, 5)
+        extra["prefill_8192x14336x4096"] = {"ms": ms4, "TFLOP/s": f4 / (ms4 * 1e-3) / 1e12,
+                                            "fp8_peak_frac": f4 / (ms4 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        del qa4, sa4, qb4, sb4, c4
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "decode"):
+        extra["decode_16x28672x8192"] = bench_decode(dev, args)
+
+    roof = {
+        "bound": "mfma",
+        "achieved": tflops,
+        "peak": PEAK_FP8_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": tflops / PEAK_FP8_TFLOPS,
+        "traffic": traffic_entry(),
+        "kernel": "tiled_kernel<MX fp8 x fp8, 256x256>",
+    }
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (UE8M0 per 32 K), fp32 accumulate",
+        "data": "synthetic (seeded numpy PCG64, N(0,1) operands)",
+        "config": {"workload": "mxfp8_8192", "M": M, "N": N, "K": K, "fmt": "E4M3 x E4M3",
+                   "scale": "UE8M0 per 32 K", "out": "fp32"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(dev, args):
+    """MXFP8 activations x MXFP4 weights, 16 x 28672 x 8192, weights rotated
+    over copies larger in total than the MALL so every launch reads HBM."""
+    import torch
+
+    from block_scaled_precision_mxgemm_amd import inputs as mxin
+    from block_scaled_precision_mxgemm_amd import mxgemm as mx
+
+    w = mxin.WORKLOADS["decode_16x28672x8192"]
+    a32, _ = mxin.mx_sources(w, N=1)
+    qa, sa = mx.mxgemm_quantize(torch.from_numpy(a32).to(dev), mx.E4M3)
+    copies = 5
+    weights = []
+    for b32 in mxin.decode_weight_copies(w, copies):
+        tb = torch.from_numpy(b32).to(dev)
+        del b32
+        weights.append(mx.mxgemm_quantize(tb, mx.E2M1))
+        del tb
+    torch.cuda.synchronize()
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    nbytes = (w.M * w.K + w.M * w.K // 32 + w.N * w.K // 2 + w.N * w.K // 32 + w.M * w.N * 4)
+    cold = time_launches(lambda i=0: mx.mxgemm_run(qa, sa, weights[i % copies][0], weights[i % copies][1],
+                                                    mx.FMT_FP8_FP4, out=c), 200, 20)
+    warm = time_launches(lambda i=0: mx.mxgemm_run(qa, sa, weights[0][0], weights[0][1], mx.FMT_FP8_FP4, out=c),
+                         200, 20)
+    gbps = nbytes / (cold * 1e-3) / 1e9
+    log("decode: cold %.2f us (%.0f GB/s), warm %.2f us" % (cold * 1e3, gbps, warm * 1e3))
+    return {"us": cold * 1e3, "GB/s": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "algorithmic_bytes": nbytes,
+            "weight_copies_rotated": copies, "warm_us_mall_resident": warm * 1e3,
+            "warm_GB/s": nbytes / (warm * 1e-3) / 1e9}
+
+
+if __name__ == "__main__":
+    main()

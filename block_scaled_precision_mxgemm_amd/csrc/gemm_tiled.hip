@@ -47,9 +47,9 @@ struct Cfg {
   static constexpr int STAGE = SZA + SZB + SZSA + SZSB;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int NQA = SZA / 1024, NQB = SZB / 1024;  // 1 KiB wave copies per slice
-  static_assert(WM * WN == 4, "4 waves per workgroup");
-  static_assert(NQA % 4 == 0 && NQB % 4 == 0, "tile copies split evenly over 4 waves");
-  static_assert(BM <= 256 && BN <= 256, "one scale row per thread");
+  static constexpr int NW = WM * WN, NTHR = NW * 64;         // waves, threads per workgroup
+  static_assert(NQA % NW == 0 && NQB % NW == 0, "tile copies split evenly over the waves");
+  static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
 };
 
@@ -77,8 +77,8 @@ struct Kernel {
                                                     int rows_valid, int64_t col_byte, uint8_t* lds, int wave,
                                                     int lane) {
 #pragma unroll
-    for (int t = 0; t < NQ / 4; t++) {
-      const int q = wave + 4 * t;
+    for (int t = 0; t < NQ / T::NW; t++) {
+      const int q = wave + T::NW * t;
       const int o = q * 1024 + lane * 16;
       const int row = o / R;
       const int pch = (o % R) >> 4;
@@ -96,8 +96,8 @@ struct Kernel {
   template <int R, int NQ>
   static __device__ __forceinline__ void zero_tail(int valid_bytes, uint8_t* lds, int wave, int lane) {
 #pragma unroll
-    for (int t = 0; t < NQ / 4; t++) {
-      const int q = wave + 4 * t;
+    for (int t = 0; t < NQ / T::NW; t++) {
+      const int q = wave + T::NW * t;
       const int o = q * 1024 + lane * 16;
       const int row = o / R;
       const int pch = (o % R) >> 4;
@@ -124,15 +124,15 @@ struct Kernel {
 
   // ---- fp16 right operand stored K x N: register transpose into N x K ----
   struct KNRegs {
-    v4i v[2][4];
+    v4i v[(16 * (T::BN / 8) + T::NTHR - 1) / T::NTHR][4];
   };
   static __device__ __forceinline__ void load_kn(const Args& a, int n0, int step, int tid, KNRegs& r) {
     // blocks of 4 (k) x 8 (n) halves; 16 * BN/8 blocks per slice
     constexpr int NBLK = 16 * (T::BN / 8);
     const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B);
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int blk = tid + 256 * j;
+    for (int j = 0; j < (NBLK + T::NTHR - 1) / T::NTHR; j++) {
+      const int blk = tid + T::NTHR * j;
       if (blk >= NBLK) break;
       const int kb4 = blk & 15, nb8 = blk >> 4;
       const int n = n0 + nb8 * 8;
@@ -159,8 +159,8 @@ struct Kernel {
   static __device__ __forceinline__ void commit_kn(const KNRegs& r, uint8_t* ldsB, int tid) {
     constexpr int NBLK = 16 * (T::BN / 8);
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int blk = tid + 256 * j;
+    for (int j = 0; j < (NBLK + T::NTHR - 1) / T::NTHR; j++) {
+      const int blk = tid + T::NTHR * j;
       if (blk >= NBLK) break;
       const int kb4 = blk & 15, nb8 = blk >> 4;
 #pragma unroll
@@ -279,6 +279,7 @@ struct Kernel {
       }
     };
 
+    if constexpr (T::KIND_ == kMX) mfma_fence_init(acc);
     issue(0, 0);
     for (int step = 0; step < a.nsteps; step++) {
       const int st = step & 1;
@@ -293,26 +294,34 @@ struct Kernel {
       const uint32_t* lsb = lsa + T::BM;
 
       if constexpr (T::KIND_ == kMX) {
-        v8i af[T::FM], bf[T::FN];
-        int sa[T::FM], sb[T::FN];
+        // all A fragments stay in registers; B fragments stream through a
+        // two-deep register buffer, one B column block per group of FM MFMAs
+        v8i af[T::FM];
+        int sa[T::FM];
 #pragma unroll
         for (int i = 0; i < T::FM; i++) {
           const int row = wi * T::TM + i * 16 + r;
           af[i] = read_frag<T::RA>(la, row, g);
           sa[i] = (int)(lsa[row] >> (8 * g));
         }
+        v8i bcur = read_frag<T::RB>(lb, wj * T::TN + r, g);
+        int sbcur = (int)(lsb[wj * T::TN + r] >> (8 * g));
 #pragma unroll
         for (int j = 0; j < T::FN; j++) {
-          const int row = wj * T::TN + j * 16 + r;
-          bf[j] = read_frag<T::RB>(lb, row, g);
-          sb[j] = (int)(lsb[row] >> (8 * g));
+          v8i bnext = bcur;
+          int sbnext = sbcur;
+          if (j + 1 < T::FN) {
+            const int row = wj * T::TN + (j + 1) * 16 + r;
+            bnext = read_frag<T::RB>(lb, row, g);
+            sbnext = (int)(lsb[row] >> (8 * g));
+          }
+#pragma unroll
+          for (int i = 0; i < T::FM; i++)
+            mfma_scaled_acc<T::BF4 ? kFmtFp4 : kFmtFp8, T::AF4 ? kFmtFp4 : kFmtFp8>(acc[i][j], bcur, af[i], sbcur,
+                                                                                    sa[i]);
+          bcur = bnext;
+          sbcur = sbnext;
         }
-#pragma unroll
-        for (int i = 0; i < T::FM; i++)
-#pragma unroll
-          for (int j = 0; j < T::FN; j++)
-            acc[i][j] = mfma_scaled_16x16x128<T::BF4 ? kFmtFp4 : kFmtFp8, T::AF4 ? kFmtFp4 : kFmtFp8>(
-                bf[j], af[i], acc[i][j], sb[j], sa[i]);
       } else if constexpr (T::KIND_ == kF16) {
         v8i af[T::FM], bf[T::FN];
 #pragma unroll
@@ -350,6 +359,8 @@ struct Kernel {
       }
     }
 
+    if constexpr (T::KIND_ == kMX) mfma_drain(acc);
+
     // ---- epilogue: lane (g, r) holds C[m][n .. n+3] -------------------------
     const bool vec_ok = (a.N & 3) == 0;
 #pragma unroll
@@ -373,7 +384,8 @@ struct Kernel {
 };
 
 template <class T, int WAVES_PER_EU>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+__global__ __attribute__((amdgpu_flat_work_group_size(T::NTHR, T::NTHR),
+                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void tiled_kernel(Args a) {
   Kernel<T>::run(a);
 }
@@ -389,7 +401,7 @@ hipError_t launch(const Args& a0, hipStream_t stream) {
   a.tail_a = bytes(T::AF4, !T::SCALED, rem);
   a.tail_b = bytes(T::BF4, !T::SCALED, rem);
   const int64_t nt = (int64_t)a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((tiled_kernel<T, WPE>), dim3((unsigned)nt), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((tiled_kernel<T, WPE>), dim3((unsigned)nt), dim3(T::NTHR), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -33,14 +33,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that
-// the fragment reads (16 consecutive lanes = 16 consecutive rows, same
-// logical chunk) and the row-major tile writes hit distinct banks both when
-// 8 lanes and when 16 lanes are served per LDS cycle.
+// XOR swizzle of the 16-byte chunk index inside an LDS row.  Fragment reads
+// have 16 consecutive lanes read 16 consecutive rows at the same logical
+// chunk; without a swizzle they conflict 3-way on gfx950.  The swizzle was
+// chosen by measurement on MI355X (ds_read_b128 throughput and the
+// SQ_LDS_BANK_CONFLICT counter): (row >> 1) & 7 and row & 7 are
+// conflict-free, while (row ^ (row >> 3)) & 7 still conflicts 2-way.  Tile
+// copies write LDS linearly (1 KiB per wave instruction) whatever the
+// swizzle, because the swizzle is applied to the global source address.
 // Rows of 8 chunks (128 bytes): fp8 and fp16 operands.
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 // Rows of 4 chunks (64 bytes): packed fp4 operands.
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz4(int row) { return (row >> 1) & 3; }
 
 // Direct global -> LDS copy of 16 bytes per lane.  The LDS destination of
 // lane i is lds_base + 16 * i; lds_base must be wave-uniform.
@@ -72,6 +76,58 @@ template <int FA, int FB>
 __device__ __forceinline__ v4f mfma_scaled_16x16x128(const v8i& a, const v8i& b, const v4f& c, int scale_a,
                                                       int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, scale_a, 0, scale_b);
+}
+
+// Scaled MFMA with the accumulator tied in place (dst == srcC, AGPRs).  The
+// builtin form lets the register allocator pick dst != srcC for this
+// instruction, which on this compiler adds accumulator copies and hazard
+// NOPs inside the K loop and halves the MFMA issue rate (measured: 16 chained
+// accumulators reach ~4.5 PFLOP/s tied versus ~2.5 in the K loop with the
+// builtin).  The hardware interlocks on the srcA/srcB/scale VGPRs written by
+// LDS loads through the waitcnt the compiler inserts for the asm operands;
+// accumulators are only touched by these instructions until mfma_drain().
+template <int FA, int FB>
+__device__ __forceinline__ void mfma_scaled_acc(v4f& c, const v8i& a, const v8i& b, int scale_a, int scale_b) {
+  if constexpr (FA == kFmtFp8 && FB == kFmtFp8) {
+    asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+        : "+a"(c) : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+  } else if constexpr (FA == kFmtFp4 && FB == kFmtFp8) {
+    const v4i a4 = {a[0], a[1], a[2], a[3]};
+    asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4"
+        : "+a"(c) : "v"(a4), "v"(b), "v"(scale_a), "v"(scale_b));
+  } else if constexpr (FA == kFmtFp8 && FB == kFmtFp4) {
+    const v4i b4 = {b[0], b[1], b[2], b[3]};
+    asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] blgp:4"
+        : "+a"(c) : "v"(a), "v"(b4), "v"(scale_a), "v"(scale_b));
+  } else {
+    const v4i a4 = {a[0], a[1], a[2], a[3]};
+    const v4i b4 = {b[0], b[1], b[2], b[3]};
+    asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+        : "+a"(c) : "v"(a4), "v"(b4), "v"(scale_a), "v"(scale_b));
+  }
+}
+
+// Wait states between the last MFMA writing an accumulator and any other
+// instruction reading it (the compiler does not model the inline MFMA's
+// latency): 3 x 16 idle cycles cover the 16-pass worst case; the empty asm
+// ties every accumulator to this point so no read is scheduled above it.
+template <int NI, int NJ>
+__device__ __forceinline__ void mfma_drain(v4f (&acc)[NI][NJ]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NI; i++)
+#pragma unroll
+    for (int j = 0; j < NJ; j++) asm volatile("" : "+a"(acc[i][j]));
+}
+// Wait states between writing the accumulators' initial zeros and the first
+// inline MFMA reading them.
+template <int NI, int NJ>
+__device__ __forceinline__ void mfma_fence_init(v4f (&acc)[NI][NJ]) {
+#pragma unroll
+  for (int i = 0; i < NI; i++)
+#pragma unroll
+    for (int j = 0; j < NJ; j++) asm volatile("" : "+a"(acc[i][j]));
+  asm volatile("s_nop 7" ::: "memory");
 }
 
 __device__ __forceinline__ v4f mfma_f16_16x16x32(const v8h& a, const v8h& b, const v4f& c) {

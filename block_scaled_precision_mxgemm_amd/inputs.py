@@ -105,14 +105,13 @@ def mx_sources(w: Workload, M: int | None = None, N: int | None = None,
 
 def decode_weight_copies(w: Workload, copies: int, N: int | None = None, K: int | None = None):
     """Independent fp32 weight sets for the decode workload (seeds seed*1000+c),
-    used to rotate weights so that repeated launches stream them from HBM."""
+    used to rotate weights so that repeated launches stream them from HBM.
+    A generator: one set is held in host memory at a time."""
     N = w.N if N is None else N
     K = w.K if K is None else K
-    out = []
     for c in range(copies):
         rng = np.random.default_rng(w.seed * 1000 + c)
-        out.append(_normal(rng, (N, K), 0.02))
-    return out
+        yield _normal(rng, (N, K), 0.02)
 
 
 def fp16_sources(w: Workload, b_is_nk: bool, M: int | None = None, N: int | None = None,
