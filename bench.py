@@ -33,6 +33,7 @@ PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["block_scaled_precision_mxgemm_amd/csrc/gemm_tiled.hip",
+                  "block_scaled_precision_mxgemm_amd/csrc/gemm_pingpong.hip",
                   "block_scaled_precision_mxgemm_amd/csrc/gemm_skinny.hip",
                   "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"]
 
@@ -259,7 +260,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": tflops / PEAK_FP8_TFLOPS,
         "traffic": traffic_entry(),
-        "kernel": "tiled_kernel<MX fp8 x fp8, 256x256>",
+        "kernel": "pingpong_kernel<MX fp8 x fp8, 256x256, 8 waves>",
     }
     out = {
         "metric": METRIC,

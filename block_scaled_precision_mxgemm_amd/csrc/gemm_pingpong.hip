@@ -1,0 +1,347 @@
+// gemm_pingpong.hip - the large-tile GEMM for gfx950: 8 waves, 256 x 256 C
+// tile, two waves per SIMD alternating between a load phase and a compute
+// phase ("ping-pong").
+//
+// Only full tiles take this kernel (M and N multiples of 256; K a multiple of
+// the slice): every copy then stays inside the operands and the copy
+// addresses reduce to wave-uniform bases plus two lane offsets, which keeps
+// the register budget of two waves per SIMD without spills.  (A spill would
+// be fatal here: the accumulators are written by inline MFMAs whose latency
+// the compiler does not know, so a spill store could read them too early.)
+//
+// Why: with one wave per SIMD, every stall of that wave (issuing global->LDS
+// copies when the address unit is busy, waiting for LDS fragment reads, the
+// barrier) idles the SIMD's matrix core; per 128-K slice the single-wave kernel
+// spent ~4350 cycles in its MFMA section against 2048 of MFMA work plus ~1300
+// cycles issuing copies.  Here the 8 waves form two groups of 4 (waves 0-3 and
+// 4-7; waves w and w+4 share a SIMD on gfx950): while one group runs its 32
+// MFMAs, the other group reads its next fragments from LDS and issues the next
+// global->LDS copies, and a workgroup barrier swaps the roles.  The matrix core
+// of every SIMD is fed by one of its two waves in every phase.
+//
+// Work split: group 0 computes C rows 0..127 of the tile, group 1 rows
+// 128..255; wave s (0..3) of a group computes columns 64s..64s+63, i.e. a
+// 128 x 64 sub-tile = 8 x 4 fragments of 16 x 16, 32 accumulators.
+//
+// LDS (two stages per region): A_top (tile rows 0..127, read by group 0 only),
+// A_bot (rows 128..255, group 1 only), B (256 rows, both groups) and their
+// scale rows.  Splitting A by reader lets its copies be issued three phases
+// before use.  Copy schedule (phase 2s-1: group 0 loads slice s; phase 2s:
+// group 1 loads slice s):
+//   phase 2s-1 (issued by group 0): B(s+1)
+//   phase 2s   (issued by group 1): A_top(s+2), A_bot(s+1)
+// so every phase issues half a slice of copies and each region's copy has at
+// least two phases between issue and first read; each group waits for its own
+// copies at the end of its compute phase, before the barrier that publishes
+// them.
+//
+// The tiled loop with double-buffered prefetch and register tiling follows
+// "Treinar LLM em Swift", section "Passo 7"; data and scale planes are sliced
+// together per tile as the WWDC26 session 330 summary describes (section
+// "スライスと量子化行列乗算").
+#include <utility>
+
+#include "mxg_device.h"
+#include "mxg_internal.h"
+
+namespace mxg {
+namespace {
+
+enum PPKind { kPPMX = 0, kPPF16 = 1 };
+
+template <int KIND, bool AF4, bool BF4>
+struct PPCfg {
+  static constexpr bool SCALED = (KIND == kPPMX);
+  static constexpr bool A_FP4 = AF4, B_FP4 = BF4;
+  static constexpr int RA = AF4 ? 64 : 128;   // bytes per A row per slice
+  static constexpr int RB = BF4 ? 64 : 128;
+  static constexpr int SZ_AH = 128 * RA;       // one A half, one stage
+  static constexpr int SZ_B = 256 * RB;
+  static constexpr int SZ_SAH = SCALED ? 128 * 4 : 0;
+  static constexpr int SZ_SB = SCALED ? 256 * 4 : 0;
+  static constexpr int OFF_ATOP = 0;
+  static constexpr int OFF_ABOT = OFF_ATOP + 2 * SZ_AH;
+  static constexpr int OFF_B = OFF_ABOT + 2 * SZ_AH;
+  static constexpr int OFF_SATOP = OFF_B + 2 * SZ_B;
+  static constexpr int OFF_SABOT = OFF_SATOP + 2 * SZ_SAH;
+  static constexpr int OFF_SB = OFF_SABOT + 2 * SZ_SAH;
+  static constexpr int LDS = OFF_SB + 2 * SZ_SB;
+  static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
+};
+
+struct PPArgs {
+  const uint8_t* A;
+  const uint8_t* SA;
+  const uint8_t* B;
+  const uint8_t* SB;
+  float* C;
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int64_t lda, ldb;  // bytes per row
+  int nslices;       // K / KSLICE (exact)
+};
+
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Barrier without a global-memory wait: the issuing group's copies stay in
+// flight across it.  LDS reads of this wave complete first, so a stage read
+// before the barrier may be overwritten by copies issued after it.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <class T>
+struct PPKernel {
+  // Lane offset of the 1 KiB tile copies.  A copy of 128-byte rows covers 8
+  // rows; lane l writes LDS bytes 16l..16l+15 of it, i.e. row l/8, physical
+  // chunk l%8, so it must fetch logical chunk (l%8) ^ swz8(row).  Copy q of a
+  // region starts at row 8q, so swz8 = 4*(q&1) + l/16; wave sw issues copies
+  // q = sw, sw+4, ..., all of parity sw&1, so one offset per wave serves all
+  // its copies.  64-byte rows: 16 rows per copy, swz4 = (l/8)&3 for every q.
+  template <int R>
+  static __device__ __forceinline__ uint32_t lane_offset(int64_t ld, int lane, int sw) {
+    if (R == 128) {
+      const int c = (lane & 7) ^ ((lane >> 4) + 4 * (sw & 1));
+      return (uint32_t)((lane >> 3) * ld + c * 16);
+    }
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);
+    return (uint32_t)((lane >> 2) * ld + c * 16);
+  }
+  // Copies of ROWS rows x R bytes of one slice, rows row0.. of the tile
+  // region addressed by `rs` (a buffer resource whose base is the tile's first
+  // row), split over the 4 waves of a group: wave sw issues copies sw, sw+4,
+  // ...  The lane part of the address is the one loop-invariant VGPR `off`;
+  // the row / slice part is a scalar offset, so no per-copy vector address
+  // stays live across the K loop.
+  template <int R, int ROWS>
+  static __device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int row0, int slice,
+                                                   uint8_t* lds, int sw, uint32_t off) {
+    constexpr int RPC = 1024 / R;  // rows per copy
+    constexpr int NQ = ROWS / RPC;
+    static_assert(NQ % 4 == 0, "copies split evenly over 4 waves");
+#pragma unroll
+    for (int k = 0; k < NQ / 4; k++) {
+      const int q = sw + 4 * k;
+      const uint32_t soff = (uint32_t)(row0 + q * RPC) * ld + (uint32_t)(slice * R);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + q * 1024), 16, off, soff, 0, 0);
+    }
+  }
+  // Scale bytes of one slice: 4 per row (one per 32-element block), 64 rows
+  // per dword copy; ROWS / 64 copies (2 or 4) taken by waves 0.. of the group.
+  template <int ROWS>
+  static __device__ __forceinline__ void copy_scales(__amdgpu_buffer_rsrc_t rs, uint32_t nb, int row0, int slice,
+                                                     uint8_t* lds, int sw, uint32_t off) {
+    constexpr int NQ = ROWS / 64;
+    static_assert(NQ <= 4, "one scale copy per wave at most");
+    if (sw < NQ) {
+      const uint32_t soff = (uint32_t)(row0 + sw * 64) * nb + (uint32_t)(slice * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + sw * 256), 4, off, soff, 0, 0);
+    }
+  }
+
+  template <int R>
+  static __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row, int g) {
+    v8i f;
+    if (R == 128) {
+      const int s = swz8(row);
+      const v4i lo = *reinterpret_cast<const v4i*>(lds + row * 128 + ((g ^ s) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(lds + row * 128 + (((4 + g) ^ s) << 4));
+      f = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const v4i lo = *reinterpret_cast<const v4i*>(lds + row * 64 + ((g ^ swz4(row)) << 4));
+      f = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+    return f;
+  }
+
+  // The 32 scaled MFMAs of one slice, B fragment j outer; the scale byte
+  // index must be an immediate, hence the index sequence.
+  template <int... I>
+  static __device__ __forceinline__ void compute_scaled(v4f (&acc)[8][4], const v8i (&af)[8], const v8i (&bf)[4],
+                                                        const int (&sa)[2], int sb, std::integer_sequence<int, I...>) {
+    constexpr int FB = T::B_FP4 ? kFmtFp4 : kFmtFp8, FA = T::A_FP4 ? kFmtFp4 : kFmtFp8;
+    (mfma_scaled_acc_pk<FB, FA, I / 8, (I % 8) & 3>(acc[I % 8][I / 8], bf[I / 8], af[I % 8], sb, sa[(I % 8) >> 2]),
+     ...);
+  }
+
+  static __device__ __forceinline__ void run(const PPArgs& a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform role: scalar registers and scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, sw = wave & 3;
+    const int lg = lane >> 4, r = lane & 15;
+    int tm, tn;
+    tile_of_block(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * 256, n0 = tn * 256;
+    const int S = a.nslices;
+    const int nb = a.K >> 5;
+
+    const uint32_t oa = lane_offset<T::RA>(a.lda, lane, sw);
+    const uint32_t ob = lane_offset<T::RB>(a.ldb, lane, sw);
+    const uint32_t os = (uint32_t)(lane * nb);
+    // buffer resources over this tile's 256 rows of A, B and their scales
+    // (word 3: the raw-buffer format of gfx9-class resources)
+    constexpr int kRsrcWord3 = 0x00020000;
+    const uint32_t lda = (uint32_t)a.lda, ldb = (uint32_t)a.ldb;
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)(a.A + (int64_t)m0 * lda), 0, 256 * lda, kRsrcWord3);
+    const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)n0 * ldb), 0, 256 * ldb, kRsrcWord3);
+    const auto rs_sa = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SA + (int64_t)m0 * nb), 0, 256 * nb, kRsrcWord3);
+    const auto rs_sb = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)n0 * nb), 0, 256 * nb, kRsrcWord3);
+    // copies of slice t of each region (issued by the 4 waves of the calling group)
+    auto copy_atop = [&](int t) {
+      copy_rows<T::RA, 128>(rs_a, lda, 0, t, smem + T::OFF_ATOP + (t & 1) * T::SZ_AH, sw, oa);
+      if (T::SCALED) copy_scales<128>(rs_sa, nb, 0, t, smem + T::OFF_SATOP + (t & 1) * T::SZ_SAH, sw, os);
+    };
+    auto copy_abot = [&](int t) {
+      copy_rows<T::RA, 128>(rs_a, lda, 128, t, smem + T::OFF_ABOT + (t & 1) * T::SZ_AH, sw, oa);
+      if (T::SCALED) copy_scales<128>(rs_sa, nb, 128, t, smem + T::OFF_SABOT + (t & 1) * T::SZ_SAH, sw, os);
+    };
+    auto copy_b = [&](int t) {
+      copy_rows<T::RB, 256>(rs_b, ldb, 0, t, smem + T::OFF_B + (t & 1) * T::SZ_B, sw, ob);
+      if (T::SCALED) copy_scales<256>(rs_sb, nb, 0, t, smem + T::OFF_SB + (t & 1) * T::SZ_SB, sw, os);
+    };
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    mfma_fence_init(acc);
+
+    // prologue: slices needed before the first copies of the steady state
+    // (B(0), A_top(0), A_top(1), A_bot(0)), issued by both groups
+    if (grp == 0) {
+      copy_b(0);
+    } else {
+      copy_atop(0);
+      if (S > 1) copy_atop(1);
+      copy_abot(0);
+    }
+    vm_wait_all();
+    phase_barrier();
+
+    // Each wave runs: load slice s (LDS -> registers, issue its share of the
+    // next copies), barrier, compute slice s, barrier.  Group 1 starts one
+    // phase late (an extra barrier first, none after its last compute), so at
+    // every phase one group loads while the other computes.  Both groups pass
+    // 2S barriers.
+    if (grp == 1) phase_barrier();
+    for (int s = 0; s < S; s++) {
+      const int st = s & 1;
+      v8i af[8], bf[4];
+      // scale bytes packed four to a register: byte i&3 of sa[i>>2] belongs
+      // to A fragment i, byte j of sb to B fragment j
+      int sa[2] = {0, 0}, sb = 0;
+      {
+        const uint8_t* la = smem + (grp ? T::OFF_ABOT : T::OFF_ATOP) + st * T::SZ_AH;
+        const uint8_t* lb = smem + T::OFF_B + st * T::SZ_B;
+#pragma unroll
+        for (int i = 0; i < 8; i++) af[i] = read_frag<T::RA>(la, i * 16 + r, lg);
+#pragma unroll
+        for (int j = 0; j < 4; j++) bf[j] = read_frag<T::RB>(lb, sw * 64 + j * 16 + r, lg);
+        if (T::SCALED) {
+          const uint8_t* lsa = smem + (grp ? T::OFF_SABOT : T::OFF_SATOP) + st * T::SZ_SAH;
+          const uint8_t* lsb = smem + T::OFF_SB + st * T::SZ_SB;
+          uint32_t x[8], y[4];
+#pragma unroll
+          for (int i = 0; i < 8; i++) x[i] = lsa[(i * 16 + r) * 4 + lg];
+#pragma unroll
+          for (int j = 0; j < 4; j++) y[j] = lsb[(sw * 64 + j * 16 + r) * 4 + lg];
+          sa[0] = (int)(x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24));
+          sa[1] = (int)(x[4] | (x[5] << 8) | (x[6] << 16) | (x[7] << 24));
+          sb = (int)(y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24));
+        }
+        if (grp == 0) {
+          if (s + 1 < S) copy_b(s + 1);
+        } else {
+          if (s + 2 < S) copy_atop(s + 2);
+          if (s + 1 < S) copy_abot(s + 1);
+        }
+      }
+      phase_barrier();
+      if constexpr (T::SCALED) {
+        // The packed scales come from VALU instructions, and an MFMA may read
+        // a VGPR only some cycles after a VALU wrote it; the compiler does not
+        // see the inline MFMAs' operands, so the wait is made explicit and the
+        // asm ties the scale registers to it.
+        asm volatile("s_nop 4" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sb));
+        compute_scaled(acc, af, bf, sa, sb, std::make_integer_sequence<int, 32>{});
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const v4i bq = h ? v4i{bf[j][4], bf[j][5], bf[j][6], bf[j][7]} : v4i{bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
+              const v4i aq = h ? v4i{af[i][4], af[i][5], af[i][6], af[i][7]} : v4i{af[i][0], af[i][1], af[i][2], af[i][3]};
+              mfma_f16_acc_v(acc[i][j], bq, aq);
+            }
+      }
+      vm_wait_all();  // this group's copies issued in this slice's load phase
+      if (grp == 0 || s + 1 < S) phase_barrier();
+    }
+    mfma_drain(acc);
+
+    // ---- epilogue: lane (lg, r) holds C[m][n .. n+3]; full tiles only -------
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      float* crow = a.C + (int64_t)(m0 + grp * 128 + i * 16 + r) * a.N;
+#pragma unroll
+      for (int j = 0; j < 4; j++) *reinterpret_cast<v4f*>(crow + n0 + sw * 64 + j * 16 + 4 * lg) = acc[i][j];
+    }
+  }
+};
+
+template <class T>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void pingpong_kernel(PPArgs a) {
+  PPKernel<T>::run(a);
+}
+
+template <class T>
+hipError_t launch_pp(PPArgs a, int kslice, hipStream_t stream) {
+  a.tiles_m = (a.M + 255) / 256;
+  a.tiles_n = (a.N + 255) / 256;
+  a.nslices = a.K / kslice;
+  hipLaunchKernelGGL((pingpong_kernel<T>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool pingpong_mx_ok(const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N, int64_t K) {
+  return (M % 256) == 0 && (N % 256) == 0 && (K % 128) == 0 && (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
+}
+
+hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                              int64_t N, int64_t K, int fmt, hipStream_t stream) {
+  PPArgs a{};
+  a.A = (const uint8_t*)A;
+  a.SA = SA;
+  a.B = (const uint8_t*)B;
+  a.SB = SB;
+  a.C = C;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.lda = (fmt == 2) ? K / 2 : K;
+  a.ldb = (fmt == 0) ? K : K / 2;
+  if (fmt == 0) return launch_pp<PPCfg<kPPMX, false, false>>(a, 128, stream);
+  if (fmt == 1) return launch_pp<PPCfg<kPPMX, false, true>>(a, 128, stream);
+  return launch_pp<PPCfg<kPPMX, true, true>>(a, 128, stream);
+}
+
+hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream) {
+  PPArgs a{};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.C = C;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.lda = K * 2;
+  a.ldb = K * 2;
+  return launch_pp<PPCfg<kPPF16, false, false>>(a, 64, stream);
+}
+
+}  // namespace mxg

@@ -296,16 +296,21 @@ struct Kernel {
       if constexpr (T::KIND_ == kMX) {
         // all A fragments stay in registers; B fragments stream through a
         // two-deep register buffer, one B column block per group of FM MFMAs
+        // Scale bytes are read from LDS one byte each, straight into the
+        // MFMA's scale registers: a VALU instruction (a shift) writing them
+        // would need wait states before the inline MFMA reads them.
+        const uint8_t* lsa8 = reinterpret_cast<const uint8_t*>(lsa);
+        const uint8_t* lsb8 = reinterpret_cast<const uint8_t*>(lsb);
         v8i af[T::FM];
         int sa[T::FM];
 #pragma unroll
         for (int i = 0; i < T::FM; i++) {
           const int row = wi * T::TM + i * 16 + r;
           af[i] = read_frag<T::RA>(la, row, g);
-          sa[i] = (int)(lsa[row] >> (8 * g));
+          sa[i] = lsa8[row * 4 + g];
         }
         v8i bcur = read_frag<T::RB>(lb, wj * T::TN + r, g);
-        int sbcur = (int)(lsb[wj * T::TN + r] >> (8 * g));
+        int sbcur = lsb8[(wj * T::TN + r) * 4 + g];
 #pragma unroll
         for (int j = 0; j < T::FN; j++) {
           v8i bnext = bcur;
@@ -313,7 +318,7 @@ struct Kernel {
           if (j + 1 < T::FN) {
             const int row = wj * T::TN + (j + 1) * 16 + r;
             bnext = read_frag<T::RB>(lb, row, g);
-            sbnext = (int)(lsb[row] >> (8 * g));
+            sbnext = lsb8[row * 4 + g];
           }
 #pragma unroll
           for (int i = 0; i < T::FM; i++)
@@ -447,6 +452,7 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
   a.ldb = bf4 ? K / 2 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
   const bool big = use_big_tiles(M, N);
+  if (big && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, C, M, N, K, fmt, stream);
   if (fmt == 0) return big ? launch<MxBig88, 1>(a, stream) : launch<MxMid88, 2>(a, stream);
   if (fmt == 1) return big ? launch<MxBig84, 1>(a, stream) : launch<MxMid84, 2>(a, stream);
   return big ? launch<MxBig44, 1>(a, stream) : launch<MxMid44, 2>(a, stream);
@@ -461,6 +467,7 @@ hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int6
     return launch<F16MidKN, 2>(a, stream);
   }
   a.ldb = K * 2;
+  if (use_big_tiles(M, N) && M % 256 == 0 && N % 256 == 0 && K % 64 == 0) return launch_f16_pingpong(A, B, C, M, N, K, stream);
   return use_big_tiles(M, N) ? launch<F16Big, 1>(a, stream) : launch<F16Mid, 2>(a, stream);
 }
 

@@ -107,6 +107,42 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& c, const v8i& a, const v8i&
   }
 }
 
+// Scaled MFMA taking its scales from byte BA of scale_a and byte BB of
+// scale_b (the op_sel / op_sel_hi pair selects the byte), so that the scales
+// of four fragments share one VGPR.  Accumulator tied as above; volatile, so
+// the MFMAs keep program order with respect to other volatile asm (barriers,
+// waits) and stay inside the phase that issues them.
+template <int FA, int FB, int BA, int BB>
+__device__ __forceinline__ void mfma_scaled_acc_pk(v4f& c, const v8i& a, const v8i& b, int scale_a, int scale_b) {
+  static_assert(BA >= 0 && BA < 4 && BB >= 0 && BB < 4, "scale byte index");
+  if constexpr (FA == kFmtFp8 && FB == kFmtFp8) {
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                 : "+a"(c)
+                 : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1));
+  } else if constexpr (FA == kFmtFp4 && FB == kFmtFp8) {
+    const v4i a4 = {a[0], a[1], a[2], a[3]};
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] cbsz:4"
+                 : "+a"(c)
+                 : "v"(a4), "v"(b), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1));
+  } else if constexpr (FA == kFmtFp8 && FB == kFmtFp4) {
+    const v4i b4 = {b[0], b[1], b[2], b[3]};
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] blgp:4"
+                 : "+a"(c)
+                 : "v"(a), "v"(b4), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1));
+  } else {
+    const v4i a4 = {a[0], a[1], a[2], a[3]};
+    const v4i b4 = {b[0], b[1], b[2], b[3]};
+    asm volatile(
+        "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] cbsz:4 blgp:4"
+        : "+a"(c)
+        : "v"(a4), "v"(b4), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1));
+  }
+}
+// fp16 16x16x32 MFMA, accumulator tied in AGPRs; a and b hold 8 halves each.
+__device__ __forceinline__ void mfma_f16_acc_v(v4f& c, const v4i& a, const v4i& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // Wait states between the last MFMA writing an accumulator and any other
 // instruction reading it (the compiler does not model the inline MFMA's
 // latency): 3 x 16 idle cycles cover the 16-pass worst case; the empty asm

@@ -20,6 +20,15 @@ hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int6
 hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
                             int64_t N, int64_t K, hipStream_t stream);
 
+// 8-wave ping-pong kernels for full 256 x 256 tiles (M, N multiples of 256;
+// MX: K % 128 == 0 and 4-byte aligned scale planes; fp16: K % 64 == 0 and an
+// N x K right operand).
+bool pingpong_mx_ok(const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N, int64_t K);
+hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                              int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream);
+
 // Largest M served by the split-K streaming kernel.
 constexpr int64_t kSkinnyMaxM = 64;
 

@@ -1,0 +1,104 @@
+"""Static checks of the compiled gfx950 kernels (CPU only: hipcc cross-compiles).
+
+The GEMM kernels issue MFMAs as inline asm, whose operands the compiler's
+hazard recognizer does not track, so spills and missing wait states around
+them would give wrong results without any error.  These tests compile every
+kernel source to assembly and check it with tests/asm_hazards.py; the
+synthetic cases first show that each rule of the checker fires.
+"""
+import glob
+import os
+import shutil
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import asm_hazards as H  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _wrap(body: str) -> str:
+    # every synthetic instruction counts as inline asm, as the kernels' MFMAs are
+    out = []
+    for ln in body.strip().splitlines():
+        ln = ln.strip()
+        out.append(ln if ln.startswith(".LBB") else "\t;;#ASMSTART\n\t" + ln + "\n\t;;#ASMEND")
+    return "_Zkernel:\n" + "\n".join(out) + "\n.Lfunc_end0:\n"
+
+
+def _problems(body: str):
+    fs = H.parse_functions(_wrap(body))
+    assert len(fs) == 1
+    return H.check_function(fs[0])
+
+
+MFMA = "v_mfma_scale_f32_16x16x128_f8f6f4 a[0:3], v[0:7], v[8:15], a[0:3], v16, v17 op_sel_hi:[0,0,0]"
+
+
+def test_valu_write_then_mfma_read_is_flagged():
+    assert _problems("v_lshrrev_b32_e32 v16, 8, v16\n" + MFMA + "\ns_endpgm")
+    assert not _problems("v_lshrrev_b32_e32 v16, 8, v16\ns_nop 1\n" + MFMA + "\ns_endpgm")
+
+
+def test_lds_load_into_mfma_operand_is_not_valu():
+    assert not _problems("ds_read_u8 v16, v20\ns_waitcnt lgkmcnt(0)\n" + MFMA + "\ns_endpgm")
+
+
+def test_accumulator_read_too_early_is_flagged():
+    assert _problems(MFMA + "\ns_nop 7\nv_accvgpr_read_b32 v30, a2\ns_endpgm")
+    assert not _problems(MFMA + "\ns_nop 15\ns_nop 15\nv_accvgpr_read_b32 v30, a2\ns_endpgm")
+
+
+def test_accumulator_overwrite_and_store_too_early_are_flagged():
+    assert _problems(MFMA + "\nv_accvgpr_write_b32 a1, 0\ns_endpgm")
+    assert _problems(MFMA + "\nglobal_store_dwordx4 v[40:41], a[0:3], off\ns_endpgm")
+
+
+def test_hazard_reached_through_a_branch_is_flagged():
+    body = MFMA + "\ns_cbranch_scc1 .LBB0_2\ns_nop 15\ns_nop 15\n.LBB0_2:\nv_accvgpr_read_b32 v30, a0\ns_endpgm"
+    assert _problems(body)
+
+
+def test_accumulation_chain_rules():
+    same = MFMA + "\n" + MFMA + "\ns_endpgm"
+    assert not _problems(same)
+    partial = MFMA + "\nv_mfma_scale_f32_16x16x128_f8f6f4 a[2:5], v[0:7], v[8:15], a[2:5], v16, v17\ns_endpgm"
+    assert _problems(partial)
+    as_source = MFMA.replace("a[0:3], v[0:7]", "a[0:3], v[20:27]") + \
+        "\nv_mfma_f32_16x16x32_f16 a[8:11], a[0:3], v[4:7], a[8:11]\ns_endpgm"
+    assert _problems(as_source)
+
+
+def test_spill_in_mfma_kernel_is_flagged():
+    assert _problems(MFMA + "\ns_nop 15\ns_nop 15\nscratch_store_dwordx4 off, a[0:3], off\ns_endpgm")
+
+
+def test_compiler_generated_pairs_are_left_to_the_compiler():
+    asm = "_Zkernel:\n\t" + MFMA + "\n\tv_accvgpr_read_b32 v30, a2\n\ts_endpgm\n.Lfunc_end0:\n"
+    assert not H.check_function(H.parse_functions(asm)[0])
+
+
+def test_checker_sees_the_right_operands():
+    ins = H._parse_instr("v_mfma_scale_f32_16x16x128_f8f6f4 a[112:115], v[88:95], v[8:15], a[112:115], v109, "
+                         "v107 op_sel:[0,1,0] op_sel_hi:[0,0,0]")
+    assert ins.writes == {("a", r) for r in range(112, 116)}
+    assert ins.srcc == ins.writes
+    assert ("v", 109) in ins.srcab and ("v", 107) in ins.srcab and ("v", 95) in ins.srcab
+    ld = H._parse_instr("buffer_load_dwordx4 v98, s[16:19], s6 offen lds")
+    assert not ld.writes and ("v", 98) in ld.reads
+
+
+@pytest.mark.skipif(shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")) is None, reason="hipcc not found")
+@pytest.mark.parametrize("src", sorted(glob.glob(os.path.join(ROOT, "block_scaled_precision_mxgemm_amd", "csrc",
+                                                              "*.hip"))), ids=os.path.basename)
+def test_kernel_source_is_hazard_free(src):
+    from block_scaled_precision_mxgemm_amd import build as B
+    asm = H.compile_to_asm(src, B.FLAGS, B.HIPCC)
+    funcs = H.parse_functions(asm)
+    assert funcs, "no functions parsed from " + src
+    problems = []
+    for f in funcs:
+        problems += H.check_function(f)
+    assert not problems, "\n".join(problems[:20])
