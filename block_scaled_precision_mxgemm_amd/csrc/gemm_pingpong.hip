@@ -168,23 +168,31 @@ struct PPKernel {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, sw = wave & 3;
     const int lg = lane >> 4, r = lane & 15;
-    int tm, tn;
-    tile_of_block(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-    const int m0 = tm * 256, n0 = tn * 256;
     const int S = a.nslices;
     const int nb = a.K >> 5;
+    const int total = a.tiles_m * a.tiles_n;
 
     const uint32_t oa = lane_offset<T::RA>(a.lda, lane, sw);
     const uint32_t ob = lane_offset<T::RB>(a.ldb, lane, sw);
     const uint32_t os = (uint32_t)(lane * nb);
-    // buffer resources over this tile's 256 rows of A, B and their scales
-    // (word 3: the raw-buffer format of gfx9-class resources)
+    // Buffer resources over the current tile's 256 rows of A, B and their
+    // scales (word 3: the raw-buffer format of gfx9-class resources).
     constexpr int kRsrcWord3 = 0x00020000;
     const uint32_t lda = (uint32_t)a.lda, ldb = (uint32_t)a.ldb;
-    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)(a.A + (int64_t)m0 * lda), 0, 256 * lda, kRsrcWord3);
-    const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)n0 * ldb), 0, 256 * ldb, kRsrcWord3);
-    const auto rs_sa = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SA + (int64_t)m0 * nb), 0, 256 * nb, kRsrcWord3);
-    const auto rs_sb = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)n0 * nb), 0, 256 * nb, kRsrcWord3);
+    int m0 = 0, n0 = 0;
+    __amdgpu_buffer_rsrc_t rs_a, rs_b, rs_sa, rs_sb;
+    auto set_tile = [&](int tile) {
+      int tm, tn;
+      tile_of_block(tile, a.tiles_m, a.tiles_n, tm, tn);
+      m0 = tm * 256;
+      n0 = tn * 256;
+      rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)(a.A + (int64_t)m0 * lda), 0, 256 * lda, kRsrcWord3);
+      rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)n0 * ldb), 0, 256 * ldb, kRsrcWord3);
+      if (T::SCALED) {
+        rs_sa = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SA + (int64_t)m0 * nb), 0, 256 * nb, kRsrcWord3);
+        rs_sb = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)n0 * nb), 0, 256 * nb, kRsrcWord3);
+      }
+    };
     // copies of slice t of each region (issued by the 4 waves of the calling group)
     auto copy_atop = [&](int t) {
       copy_rows<T::RA, 128>(rs_a, lda, 0, t, smem + T::OFF_ATOP + (t & 1) * T::SZ_AH, sw, oa);
@@ -199,15 +207,14 @@ struct PPKernel {
       if (T::SCALED) copy_scales<256>(rs_sb, nb, 0, t, smem + T::OFF_SB + (t & 1) * T::SZ_SB, sw, os);
     };
 
-    v4f acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    mfma_fence_init(acc);
-
-    // prologue: slices needed before the first copies of the steady state
-    // (B(0), A_top(0), A_top(1), A_bot(0)), issued by both groups
+    // The workgroup is persistent: it takes tiles blockIdx.x, + gridDim.x, ...
+    // (the grid is at most one workgroup per CU), so there is no dispatch gap
+    // between tiles, and the copies that start a tile are issued by group 0
+    // while group 1 still runs the previous tile's last compute phase.
+    int tile = blockIdx.x;
+    set_tile(tile);
+    // prologue of the first tile: the slices needed before the copies of the
+    // steady state (B(0), A_top(0), A_top(1), A_bot(0)), issued by both groups
     if (grp == 0) {
       copy_b(0);
     } else {
@@ -217,6 +224,14 @@ struct PPKernel {
     }
     vm_wait_all();
     phase_barrier();
+
+    v4f acc[8][4];
+    for (;;) {
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    mfma_fence_init(acc);
 
     // Each wave runs: load slice s (LDS -> registers, issue its share of the
     // next copies), barrier, compute slice s, barrier.  Group 1 starts one
@@ -256,13 +271,17 @@ struct PPKernel {
           if (s + 1 < S) copy_abot(s + 1);
         }
       }
-      phase_barrier();
       if constexpr (T::SCALED) {
-        // The packed scales come from VALU instructions, and an MFMA may read
-        // a VGPR only some cycles after a VALU wrote it; the compiler does not
-        // see the inline MFMAs' operands, so the wait is made explicit and the
-        // asm ties the scale registers to it.
-        asm volatile("s_nop 4" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sb));
+        // The barrier asm takes the packed scales as operands, so the packing
+        // (VALU) stays in the load phase instead of being sunk into the
+        // compute phase; the s_nop keeps the wait states an MFMA needs after
+        // a VALU write of its operand, which the compiler does not insert for
+        // inline MFMAs.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_nop 4" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sb)::"memory");
+      } else {
+        phase_barrier();
+      }
+      if constexpr (T::SCALED) {
         compute_scaled(acc, af, bf, sa, sb, std::make_integer_sequence<int, 32>{});
       } else {
 #pragma unroll
@@ -288,6 +307,26 @@ struct PPKernel {
 #pragma unroll
       for (int j = 0; j < 4; j++) *reinterpret_cast<v4f*>(crow + n0 + sw * 64 + j * 16 + 4 * lg) = acc[i][j];
     }
+    const int next = tile + (int)gridDim.x;
+    if (next >= total) break;
+    tile = next;
+    set_tile(tile);
+    // Group 0 finished its part of the tile one phase before group 1; every
+    // LDS read of the finished tile and every copy into LDS has completed
+    // (each group waited for its copies and passed the barrier after group
+    // 1's last load phase), so group 0 issues the next tile's prologue copies
+    // now, over group 1's last compute phase.  Its wait also covers its C
+    // stores; group 1's C stores are covered by its first wait of the next
+    // tile.
+    if (grp == 0) {
+      copy_b(0);
+      copy_atop(0);
+      if (S > 1) copy_atop(1);
+      copy_abot(0);
+      vm_wait_all();
+    }
+    phase_barrier();
+    }
   }
 };
 
@@ -302,7 +341,14 @@ hipError_t launch_pp(PPArgs a, int kslice, hipStream_t stream) {
   a.tiles_m = (a.M + 255) / 256;
   a.tiles_n = (a.N + 255) / 256;
   a.nslices = a.K / kslice;
-  hipLaunchKernelGGL((pingpong_kernel<T>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(512), 0, stream, a);
+  // one persistent workgroup per CU (the LDS use allows one), at most one per tile
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int grid = (cus > 0 && cus < tiles) ? cus : tiles;
+  hipLaunchKernelGGL((pingpong_kernel<T>), dim3((unsigned)grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
