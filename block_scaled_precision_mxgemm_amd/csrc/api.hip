@@ -86,6 +86,8 @@ int mxgemm_run(const void* A, const uint8_t* scaleA, const void* B, const uint8_
   s = check_device();
   if (s != MXG_OK) return s;
   hipStream_t st = (hipStream_t)stream;
+  if (mxg::decode_ok(M, K, fmt, scaleA, scaleB))
+    return to_status(mxg::launch_mx_decode(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
   if (M <= mxg::kSkinnyMaxM && fmt != MXG_FMT_FP4_FP4)
     return to_status(mxg::launch_mx_skinny(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
   return to_status(mxg::launch_mx_tiled(A, scaleA, B, scaleB, C, M, N, K, fmt, st));

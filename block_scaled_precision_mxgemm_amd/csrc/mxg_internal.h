@@ -29,6 +29,13 @@ hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, c
 hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream);
 
+// Decode kernel for M <= 16 (MX fp8 x fp8 or fp8 x fp4): K one of 2048,
+// 4096, 8192 (A's k range per wave is held in registers), 4-byte aligned
+// scale planes.
+bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB);
+hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
+                            int64_t N, int64_t K, int fmt, hipStream_t stream);
+
 // Largest M served by the split-K streaming kernel.
 constexpr int64_t kSkinnyMaxM = 64;
 
