@@ -25,6 +25,8 @@
 //   * a fragment's 8 per-wave partial sums go to LDS and one wave adds them
 //     in a fixed order one stage later, so the result is deterministic and
 //     needs no atomics.
+#include <utility>
+
 #include "mxg_device.h"
 #include "mxg_internal.h"
 
@@ -45,15 +47,6 @@ struct DecArgs {
   int nfrags;  // ceil(N / 16)
 };
 
-// Wait until this wave has at most 15 (steady state: the copies of the
-// kDecStages - 2 younger stages, 3 per stage) or 0 global->LDS copies in
-// flight; the count is an immediate.
-__device__ __forceinline__ void wait_copies(bool all) {
-  if (all)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-}
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <bool BF4, int KA>
@@ -63,14 +56,14 @@ struct Decode {
   static constexpr int NQ = KA / MPW;              // stages per fragment
   static constexpr int SROW = BF4 ? 64 : 32;       // scale bytes per row per stage
   static constexpr int SZ_ST = 16 * kStageRowBytes;
-  static constexpr int SZ_SC = 16 * SROW;
+  static constexpr int SC_WAVE = 256;               // scale slot per wave per stage (64 lanes x 4 B)
+  static constexpr int SZ_SC = kDecWaves * SC_WAVE;
   static constexpr int OFF_ST = 0;
   static constexpr int OFF_SC = OFF_ST + kDecStages * SZ_ST;
   static constexpr int OFF_PART = OFF_SC + kDecStages * SZ_SC;
   static constexpr int LDS = OFF_PART + 2 * kDecWaves * 64 * 16;
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
   static_assert(NQ >= 1 && KA % MPW == 0, "whole stages per fragment");
-  static_assert(3 * (kDecStages - 2) == 15, "wait_copies immediate");
 
   // fp8 operand of the MFMA covering k0 .. k0+127 of row `p` (p at k0):
   // lane group g holds k0 + 16g .. +15 and k0 + 64 + 16g .. +15
@@ -101,128 +94,194 @@ struct Decode {
     }
   }
 
+  // Per-workgroup state shared by the stage functions (all in registers
+  // once inlined).
+  struct State {
+    const DecArgs* a;
+    uint8_t* smem;
+    int lane, wave, g, r;
+    int f_begin, nf, S;
+    uint32_t rb, nb;  // bytes per B row, scale bytes per row
+    uint32_t vo0, vo1, sbyte_l;
+    int srow_l;
+    v8i av[KA];   // A operands of this wave's MFMAs
+    uint32_t sa[KA];  // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
+    v4f acc[MPW];
+  };
+
+  // Vector-memory instructions per A load group (stage q of the A registers):
+  // lo and hi 16-byte halves per MFMA plus one load of the MPW scale dwords.
+  static constexpr int LA = 2 * MPW + 1;
+  static constexpr int kYoung = 3 * (kDecStages - 2);  // copies of the younger stages in flight
+
+  template <int N>
+  static __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+  }
+  static __device__ __forceinline__ void order_fence() { asm volatile("" ::: "memory"); }
+
+  // Copies of stage s: wave w fetches stage rows 2w and 2w+1 (lane l writes
+  // physical chunk l of the row and fetches logical chunk l ^ (row & 15)) and
+  // the scale bytes of the same two rows into its own 256-byte slot, 4 bytes
+  // per lane (global->LDS copies of fewer than 4 bytes still write one dword
+  // per lane): row 2w at slot byte 0, row 2w+1 at SROW; the remaining lanes
+  // fetch a valid address again into the slot's unused tail.  Every wave
+  // issues exactly 3 copies per stage, all lanes active, which the wait
+  // counts rely on (a copy under a lane condition could be skipped, and the
+  // compiler would then count conservatively).
+  static __device__ __forceinline__ void issue(State& t, int s) {
+    constexpr int kRsrcWord3 = 0x00020000;
+    const DecArgs& a = *t.a;
+    // past the workgroup's last stage, that stage's source again: the copy
+    // lands in a buffer no real stage still needs, and the copy count per
+    // stage stays fixed
+    const int buf = s % kDecStages;
+    const int sv = min(s, t.S - 1);
+    const int f = sv / NQ, q = sv - f * NQ;
+    const int row0 = (t.f_begin + f) * 16;
+    const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * t.rb), 0, 16 * t.rb, kRsrcWord3);
+    const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * t.nb), 0, 16 * t.nb, kRsrcWord3);
+    uint8_t* st = t.smem + OFF_ST + buf * SZ_ST;
+    const int r0 = min(row0 + 2 * t.wave, a.N - 1) - row0;  // rows past N: the last row again
+    const int r1 = min(row0 + 2 * t.wave + 1, a.N - 1) - row0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + (2 * t.wave) * kStageRowBytes), 16, t.vo0,
+                                             (uint32_t)r0 * t.rb + (uint32_t)q * kStageRowBytes, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + (2 * t.wave + 1) * kStageRowBytes), 16, t.vo1,
+                                             (uint32_t)r1 * t.rb + (uint32_t)q * kStageRowBytes, 0, 0);
+    const uint32_t sr = (uint32_t)(min(row0 + t.srow_l, a.N - 1) - row0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(t.smem + OFF_SC + buf * SZ_SC + t.wave * SC_WAVE), 4,
+                                             sr * t.nb + t.sbyte_l, (uint32_t)q * SROW, 0, 0);
+  }
+
+  // A for the stage-q MFMAs of this wave (rows clamped to M-1; rows >= M are
+  // computed and discarded): local MFMA u -> global MFMA j = q * MPS +
+  // wave * MPW + u covering k 128j .. 128j+127; its scale is byte g of the
+  // dword of blocks 4j .. 4j+3.
+  template <int Q>
+  static __device__ __forceinline__ void load_a(State& t) {
+    const DecArgs& a = *t.a;
+    const int m = min(t.r, a.M - 1);
+    const uint8_t* row = a.A + (int64_t)m * a.K;
+    const uint8_t* srow = a.SA + (int64_t)m * t.nb;
+    const int j0 = Q * MPS + t.wave * MPW;
+#pragma unroll
+    for (int u = 0; u < MPW; u++) t.av[Q * MPW + u] = load_fp8_op(row + (int64_t)(j0 + u) * 128, t.g);
+    // the scale dwords stay raw until the MFMA: extracting the byte here would
+    // wait for this load in the middle of the prologue
+    if constexpr (MPW == 2) {
+      const v2i d = *reinterpret_cast<const v2i*>(srow + 4 * j0);  // one 8-byte load
+      t.sa[Q * MPW] = (uint32_t)d[0];
+      t.sa[Q * MPW + MPW - 1] = (uint32_t)d[1];
+    } else {
+      t.sa[Q * MPW] = *reinterpret_cast<const uint32_t*>(srow + 4 * j0);
+    }
+  }
+
+  // Prologue, in this issue order: stage p's copies then A(p), for p = 0 ..;
+  // stages up to kDecStages - 2, A up to NQ - 1.
+  template <int... P>
+  static __device__ __forceinline__ void prologue(State& t, std::integer_sequence<int, P...>) {
+    (
+        [&] {
+          if (P < kDecStages - 1) issue(t, P);
+          order_fence();
+          if constexpr (P < NQ) load_a<P>(t);
+          order_fence();
+        }(),
+        ...);
+  }
+
+  // Stage q of fragment f (s = f * NQ + q).
+  template <int Q, bool FIRST>
+  static __device__ __forceinline__ void stage(State& t, int f) {
+    const DecArgs& a = *t.a;
+    const int s = f * NQ + Q, buf = s % kDecStages;
+    // This wave's copies of stage s are complete once at most the younger
+    // vector-memory instructions are outstanding (the counter completes in
+    // issue order).  Younger than stage s's copies: the copies of the
+    // kDecStages - 2 younger stages (always issued, see issue()) and, in the
+    // first fragment, the A loads of stages q .. NQ-1 when stage q was a
+    // prologue stage.  Stores of C issued since are younger still and only
+    // make the wait stricter.
+    if (FIRST && Q < kDecStages - 1)
+      wait_vm<kYoung + (Q < kDecStages - 1 ? LA * (NQ - Q) : 0)>();
+    else
+      wait_vm<kYoung>();
+    stage_barrier();                       // publishes every wave's copies of stage s
+    issue(t, s + kDecStages - 1);          // into the buffer read at stage s-1
+    // the previous fragment's partials were published by the barrier
+    if (!FIRST && Q == 0 && t.wave == (f - 1) % kDecWaves)
+      reduce_store(a, t.smem, t.f_begin + f - 1, (f - 1) & 1, t.lane, t.g, t.r);
+    const uint8_t* st = t.smem + OFF_ST + buf * SZ_ST;
+    const uint8_t* sc = t.smem + OFF_SC + buf * SZ_SC;
+    const int g = t.g, r = t.r;
+#pragma unroll
+    for (int u = 0; u < MPW; u++) {
+      const int lj = t.wave * MPW + u;  // MFMA index inside the stage
+      v8i bv;
+      if (BF4) {
+        const int ch = (lj * 4 + g) ^ r;  // 16-byte chunk, swizzled
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + ch * 16);
+        bv = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+      } else {
+        const int cl = (lj * 8 + g) ^ r, chh = (lj * 8 + 4 + g) ^ r;
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + cl * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + chh * 16);
+        bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      const int sb = sc[(r >> 1) * SC_WAVE + (r & 1) * SROW + lj * 4 + g];
+      t.acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, t.av[Q * MPW + u], t.acc[u],
+                                                                  BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8, 0, sb, 0,
+                                                                  (int)__builtin_amdgcn_ubfe(t.sa[Q * MPW + u], 8 * g, 8));
+    }
+  }
+
+  template <bool FIRST, int... Q>
+  static __device__ __forceinline__ void fragment(State& t, int f, std::integer_sequence<int, Q...>) {
+    (stage<Q, FIRST>(t, f), ...);
+    v4f p = t.acc[0];
+#pragma unroll
+    for (int u = 1; u < MPW; u++) p += t.acc[u];
+    reinterpret_cast<v4f*>(t.smem + OFF_PART)[((f & 1) * kDecWaves + t.wave) * 64 + t.lane] = p;
+#pragma unroll
+    for (int u = 0; u < MPW; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+
   static __device__ __forceinline__ void run(const DecArgs& a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, r = lane & 15;
-    // balanced contiguous split of the fragments over the workgroups
-    const int f_begin = (int)((int64_t)a.nfrags * blockIdx.x / gridDim.x);
-    const int nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - f_begin;
-    const int S = nf * NQ;  // stages of this workgroup
-    const uint32_t rb = BF4 ? (uint32_t)(a.K >> 1) : (uint32_t)a.K;  // bytes per B row
-    const uint32_t nb = (uint32_t)(a.K >> 5);                         // scale bytes per row
-
-    // Copies: wave w fetches stage rows 2w and 2w+1 (lane l writes physical
-    // chunk l of the row and fetches logical chunk l ^ (row & 15)) and the
-    // scale bytes of the same two rows, 4 bytes per lane on the first
-    // 2 * SROW / 4 lanes (global->LDS copies of fewer than 4 bytes still
-    // write one dword per lane).  Every wave issues exactly 3 copies per
-    // stage, which the wait counts rely on.
-    constexpr int kRsrcWord3 = 0x00020000;
+    State t;
+    t.a = &a;
+    t.smem = smem;
+    const int tid = threadIdx.x;
+    t.lane = tid & 63;
+    t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    t.g = t.lane >> 4;
+    t.r = t.lane & 15;
+    // balanced contiguous split of the fragments over the workgroups (each
+    // has at least one: the grid is at most the fragment count)
+    t.f_begin = (int)((int64_t)a.nfrags * blockIdx.x / gridDim.x);
+    t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
+    t.S = t.nf * NQ;
+    t.rb = BF4 ? (uint32_t)(a.K >> 1) : (uint32_t)a.K;
+    t.nb = (uint32_t)(a.K >> 5);
     constexpr int SL = SROW / 4;  // scale lanes per row
-    const uint32_t vo0 = (uint32_t)((lane ^ ((2 * wave) & 15)) * 16);
-    const uint32_t vo1 = (uint32_t)((lane ^ ((2 * wave + 1) & 15)) * 16);
-    const int srow_l = 2 * wave + (lane / SL) % 2;  // scale row of this lane
-    const uint32_t sbyte_l = (uint32_t)((lane % SL) * 4);
-    auto issue = [&](int s) {
-      const int f = s / NQ, q = s - f * NQ, buf = s % kDecStages;
-      const int row0 = (f_begin + f) * 16;
-      const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * rb), 0, 16 * rb, kRsrcWord3);
-      const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * nb), 0, 16 * nb, kRsrcWord3);
-      uint8_t* st = smem + OFF_ST + buf * SZ_ST;
-      const int r0 = min(row0 + 2 * wave, a.N - 1) - row0;  // rows past N: the last row again
-      const int r1 = min(row0 + 2 * wave + 1, a.N - 1) - row0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + (2 * wave) * kStageRowBytes), 16, vo0,
-                                               (uint32_t)r0 * rb + (uint32_t)q * kStageRowBytes, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + (2 * wave + 1) * kStageRowBytes), 16, vo1,
-                                               (uint32_t)r1 * rb + (uint32_t)q * kStageRowBytes, 0, 0);
-      const uint32_t sr = (uint32_t)(min(row0 + srow_l, a.N - 1) - row0);
-      if (lane < 2 * SL)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(smem + OFF_SC + buf * SZ_SC + wave * 2 * SROW), 4,
-                                                 sr * nb + sbyte_l, (uint32_t)q * SROW, 0, 0);
-    };
+    t.vo0 = (uint32_t)((t.lane ^ ((2 * t.wave) & 15)) * 16);
+    t.vo1 = (uint32_t)((t.lane ^ ((2 * t.wave + 1) & 15)) * 16);
+    const int sl = t.lane < 2 * SL ? t.lane : 2 * SL - 1;  // lanes past the two rows repeat the last one
+    t.srow_l = 2 * t.wave + sl / SL;
+    t.sbyte_l = (uint32_t)((sl % SL) * 4);
 
-    // Prologue: stage 0, then A, then stages 1 .. kDecStages-2.  The vector
-    // memory counter completes in issue order, so waiting for stage 0 and A
-    // at the first stage leaves the younger stages in flight.
-    if (S > 0) issue(0);
+    prologue(t, std::make_integer_sequence<int, (kDecStages - 1 > NQ ? kDecStages - 1 : NQ)>{});
+#pragma unroll
+    for (int u = 0; u < MPW; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // A (rows clamped to M-1; rows >= M are computed and discarded): the k
-    // ranges of this wave's MFMAs, stage q, local MFMA t -> global MFMA
-    // j = q * MPS + wave * MPW + t; its scale is the byte of block 4j + g
-    v8i av[KA];
-    int sa[KA];
-    {
-      const int m = min(r, a.M - 1);
-      const uint8_t* row = a.A + (int64_t)m * a.K;
-      const uint8_t* srow = a.SA + (int64_t)m * nb;
-#pragma unroll
-      for (int q = 0; q < NQ; q++)
-#pragma unroll
-        for (int t = 0; t < MPW; t++) {
-          const int j = q * MPS + wave * MPW + t;
-          av[q * MPW + t] = load_fp8_op(row + (int64_t)j * 128, g);
-          const uint32_t s4 = *reinterpret_cast<const uint32_t*>(srow + 4 * j);
-          sa[q * MPW + t] = (int)__builtin_amdgcn_ubfe(s4, 8 * g, 8);
-        }
-    }
-
-#pragma unroll
-    for (int s = 1; s < kDecStages - 1; s++)
-      if (s < S) issue(s);
-
-    v4f acc[MPW];
-#pragma unroll
-    for (int t = 0; t < MPW; t++) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // stage s = f * NQ + q; the q loop is unrolled so that A and its scales
-    // stay in registers (a runtime index would put them in scratch memory)
-    for (int f = 0; f < nf; f++) {
-#pragma unroll
-      for (int q = 0; q < NQ; q++) {
-        const int s = f * NQ + q, buf = s % kDecStages;
-        // This wave's copies of stage s are done once at most the younger
-        // stages' copies are in flight (all of them near the end, where
-        // fewer younger stages were issued); the barrier publishes every
-        // wave's.
-        wait_copies(s + kDecStages - 2 > S - 1);
-        stage_barrier();
-        if (s + kDecStages - 1 < S) issue(s + kDecStages - 1);  // into the buffer read at stage s-1
-        // the previous fragment's partials were published by the barrier
-        if (q == 0 && f > 0 && wave == (f - 1) % kDecWaves)
-          reduce_store(a, smem, f_begin + f - 1, (f - 1) & 1, lane, g, r);
-        const uint8_t* st = smem + OFF_ST + buf * SZ_ST;
-        const uint8_t* sc = smem + OFF_SC + buf * SZ_SC;
-#pragma unroll
-        for (int t = 0; t < MPW; t++) {
-          const int lj = wave * MPW + t;  // MFMA index inside the stage
-          v8i bv;
-          if (BF4) {
-            const int ch = (lj * 4 + g) ^ r;  // 16-byte chunk, swizzled
-            const v4i lo = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + ch * 16);
-            bv = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-          } else {
-            const int cl = (lj * 8 + g) ^ r, chh = (lj * 8 + 4 + g) ^ r;
-            const v4i lo = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + cl * 16);
-            const v4i hi = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + chh * 16);
-            bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-          const int sb = sc[r * SROW + lj * 4 + g];
-          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av[q * MPW + t], acc[t],
-                                                                    BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8, 0, sb, 0,
-                                                                    sa[q * MPW + t]);
-        }
-      }
-      v4f p = acc[0];
-#pragma unroll
-      for (int t = 1; t < MPW; t++) p += acc[t];
-      reinterpret_cast<v4f*>(smem + OFF_PART)[((f & 1) * kDecWaves + wave) * 64 + lane] = p;
-#pragma unroll
-      for (int t = 0; t < MPW; t++) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+    // the first fragment (exact wait counts while A is arriving), then the rest
+    fragment<true>(t, 0, std::make_integer_sequence<int, NQ>{});
+    for (int f = 1; f < t.nf; f++) fragment<false>(t, f, std::make_integer_sequence<int, NQ>{});
     stage_barrier();
-    if (nf > 0 && wave == (nf - 1) % kDecWaves) reduce_store(a, smem, f_begin + nf - 1, (nf - 1) & 1, lane, g, r);
+    if (t.wave == (t.nf - 1) % kDecWaves) reduce_store(a, smem, t.f_begin + t.nf - 1, (t.nf - 1) & 1, t.lane, t.g, t.r);
+    wait_vm<0>();  // no copy into LDS may still be in flight when the workgroup ends
   }
 };
 
