@@ -32,19 +32,26 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["block_scaled_precision_mxgemm_amd/csrc/gemm_tiled.hip",
-                  "block_scaled_precision_mxgemm_amd/csrc/gemm_pingpong.hip",
-                  "block_scaled_precision_mxgemm_amd/csrc/gemm_skinny.hip",
-                  "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"]
+# Sources each committed counter entry depends on (dispatch + kernel): the
+# traffic numbers are reported only while these are unchanged.
+KERNEL_SOURCES = {
+    "mx_gemm_8192": ["block_scaled_precision_mxgemm_amd/csrc/api.hip",
+                     "block_scaled_precision_mxgemm_amd/csrc/gemm_tiled.hip",
+                     "block_scaled_precision_mxgemm_amd/csrc/gemm_pingpong.hip",
+                     "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"],
+    "decode_16x28672x8192": ["block_scaled_precision_mxgemm_amd/csrc/api.hip",
+                             "block_scaled_precision_mxgemm_amd/csrc/gemm_decode.hip",
+                             "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
+def source_digest(entry: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[entry]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -121,17 +128,19 @@ def cpu_baseline(qa, sa, qb, sb, w, budget_s: float):
     }
 
 
-def traffic_entry():
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+def traffic_entry(entry: str):
+    """HBM bytes per launch of one workload's kernel from the committed
+    rocprofv3 counter runs, if they were taken on the current sources of that
+    kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_digest") != source_digest():
+    e = t.get("entries", {}).get(entry)
+    if not e or e.get("source_digest") != source_digest(entry):
         return None
-    return t.get("mx_gemm_8192_bytes_per_launch")
+    return e.get("bytes_per_launch")
 
 
 def main():
@@ -259,7 +268,7 @@ def main():
         "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s",
         "frac": tflops / PEAK_FP8_TFLOPS,
-        "traffic": traffic_entry(),
+        "traffic": traffic_entry("mx_gemm_8192"),
         "kernel": "pingpong_kernel<MX fp8 x fp8, 256x256, 8 waves>",
     }
     out = {
@@ -311,7 +320,9 @@ def bench_decode(dev, args):
                          200, 20)
     gbps = nbytes / (cold * 1e-3) / 1e9
     log("decode: cold %.2f us (%.0f GB/s), warm %.2f us" % (cold * 1e3, gbps, warm * 1e3))
-    return {"us": cold * 1e3, "GB/s": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "algorithmic_bytes": nbytes,
+    return {"kernel": "decode_kernel<fp8 x fp4, K=8192> (LDS-staged weight stream)", "us": cold * 1e3, "GB/s": gbps,
+            "hbm_frac": gbps / PEAK_HBM_GBPS, "algorithmic_bytes": nbytes,
+            "traffic": traffic_entry("decode_16x28672x8192"),
             "weight_copies_rotated": copies, "warm_us_mall_resident": warm * 1e3,
             "warm_GB/s": nbytes / (warm * 1e-3) / 1e9}
 
