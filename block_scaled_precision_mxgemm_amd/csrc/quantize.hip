@@ -16,7 +16,8 @@
 //
 // Work mapping: 8 lanes per block, 4 elements (one 16-byte load) per lane; a
 // wave covers 8 consecutive blocks = 1 KiB of input with fully coalesced loads
-// and 256 B (E4M3) / 128 B (E2M1) of contiguous code stores.  The kernel is
+// and 256 B (E4M3) / 128 B (E2M1) of contiguous code stores; each lane keeps
+// four such loads in flight.  The kernel is
 // bound by HBM bandwidth: 4 bytes read and 1 + 1/32 (E4M3) or 1/2 + 1/32
 // (E2M1) bytes written per element.
 #include "mxg_device.h"
@@ -107,44 +108,65 @@ __device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
   return code | sign;
 }
 
+// One block of 32: lanes sub = 0..7 of the block hold its elements 4*sub ..
+// 4*sub+3 in x; writes the block's codes and (lane 0) its scale byte.
+template <int ELEM>
+__device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int sub, uint8_t* __restrict__ Q,
+                                               uint8_t* __restrict__ S) {
+  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : 2;
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; i++) amax = max(amax, (uint32_t)x[i] & 0x7fffffffu);
+  // the 8 lanes of a block are consecutive lanes of one wave
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
+  const bool bad = amax >= 0x7f800000u;  // infinity or NaN present
+  int e = -127;
+  if (amax != 0u) {
+    const Mag m = split_abs(amax);
+    e = floor_log2_u(m.s) + m.ex - 23 - kEmax;
+    e = min(max(e, -127), 127);
+  }
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    c[i] = bad ? 0u : ((ELEM == kFmtFp8) ? encode_e4m3((uint32_t)x[i], e) : encode_e2m1((uint32_t)x[i], e));
+  }
+  const int64_t off = blk * 32 + sub * 4;  // element index
+  if (ELEM == kFmtFp8) {
+    *reinterpret_cast<uint32_t*>(Q + off) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  } else {
+    *reinterpret_cast<uint16_t*>(Q + (off >> 1)) = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
+  }
+  if (sub == 0) S[blk] = bad ? (uint8_t)255 : (uint8_t)(e + 127);
+}
+
+// Rows are contiguous with K % 32 == 0, so block blk (row r, block b) starts
+// at element r*K + 32b = 32*blk, and its scale byte is S[blk]: the matrix is
+// processed as one flat sequence of blocks.  Each lane keeps kUnroll 16-byte
+// loads in flight (grid-stride, all loads issued before any block is
+// encoded).
+constexpr int kUnroll = 4;
+
 template <int ELEM>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ X, uint8_t* __restrict__ Q,
-                                                       uint8_t* __restrict__ S, int64_t rows, int64_t K) {
-  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : 2;
-  const int64_t nb = K >> 5;
-  const int64_t total = rows * nb;
+                                                       uint8_t* __restrict__ S, int64_t total) {
   const int sub = threadIdx.x & 7;
   const int64_t step = ((int64_t)gridDim.x * blockDim.x) >> 3;
-  for (int64_t blk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3; blk < total; blk += step) {
-    const int64_t r = blk / nb;
-    const int64_t b = blk - r * nb;
-    const int64_t off = r * K + b * 32 + sub * 4;
-    const v4i x = *reinterpret_cast<const v4i*>(X + off);
-    uint32_t amax = 0u;
+  for (int64_t blk0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3; blk0 < total;
+       blk0 += kUnroll * step) {
+    v4i x[kUnroll];
 #pragma unroll
-    for (int i = 0; i < 4; i++) amax = max(amax, (uint32_t)x[i] & 0x7fffffffu);
-    // the 8 lanes of a block are consecutive lanes of one wave
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
-    const bool bad = amax >= 0x7f800000u;  // infinity or NaN present
-    int e = -127;
-    if (amax != 0u) {
-      const Mag m = split_abs(amax);
-      e = floor_log2_u(m.s) + m.ex - 23 - kEmax;
-      e = min(max(e, -127), 127);
+    for (int u = 0; u < kUnroll; u++) {
+      const int64_t blk = blk0 + u * step;
+      x[u] = (blk < total) ? *reinterpret_cast<const v4i*>(X + blk * 32 + sub * 4) : v4i{0, 0, 0, 0};
     }
-    uint32_t c[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      c[i] = bad ? 0u : ((ELEM == kFmtFp8) ? encode_e4m3((uint32_t)x[i], e) : encode_e2m1((uint32_t)x[i], e));
+    for (int u = 0; u < kUnroll; u++) {
+      const int64_t blk = blk0 + u * step;
+      if (blk < total) quantize_block<ELEM>(x[u], blk, sub, Q, S);
     }
-    if (ELEM == kFmtFp8) {
-      *reinterpret_cast<uint32_t*>(Q + off) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    } else {
-      *reinterpret_cast<uint16_t*>(Q + (off >> 1)) = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
-    }
-    if (sub == 0) S[blk] = bad ? (uint8_t)255 : (uint8_t)(e + 127);
   }
 }
 
@@ -152,15 +174,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S,
                            hipStream_t stream) {
-  const int64_t total_threads = rows * (K >> 5) * 8;
-  int64_t grid = (total_threads + 255) / 256;
+  const int64_t total = rows * (K >> 5);  // blocks of 32
+  int64_t grid = (total * 8 + 255) / 256;
   if (grid > 256 * 32) grid = 256 * 32;
   if (elem == kFmtFp8)
     hipLaunchKernelGGL(quantize_kernel<kFmtFp8>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
-                       rows, K);
+                       total);
   else
     hipLaunchKernelGGL(quantize_kernel<kFmtFp4>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
-                       rows, K);
+                       total);
   return hipGetLastError();
 }
 
