@@ -65,8 +65,15 @@ struct PPCfg {
   static constexpr int OFF_SATOP = OFF_B + 2 * SZ_B;
   static constexpr int OFF_SABOT = OFF_SATOP + 2 * SZ_SAH;
   static constexpr int OFF_SB = OFF_SABOT + 2 * SZ_SAH;
-  static constexpr int LDS = OFF_SB + 2 * SZ_SB;
+  static constexpr int LDS_MAIN = OFF_SB + 2 * SZ_SB;
+  // Epilogue staging of C (4 KiB per wave): a dedicated area when it fits,
+  // else B stage 1, which is free at every tile end (see the epilogue).
+  static constexpr int SZ_CST = 8 * 4096;
+  static constexpr bool CST_OWN = LDS_MAIN + SZ_CST <= 160 * 1024;
+  static constexpr int OFF_CST = CST_OWN ? LDS_MAIN : OFF_B + SZ_B;
+  static constexpr int LDS = CST_OWN ? LDS_MAIN + SZ_CST : LDS_MAIN;
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
+  static_assert(CST_OWN || SZ_B >= SZ_CST, "C staging fits in B stage 1");
 };
 
 struct PPArgs {
@@ -300,12 +307,41 @@ struct PPKernel {
     }
     mfma_drain(acc);
 
-    // ---- epilogue: lane (lg, r) holds C[m][n .. n+3]; full tiles only -------
+    // ---- epilogue (full tiles only) -----------------------------------------
+    // Lane (lg, r) holds C[m][n .. n+3] of fragment (i, j): row m = i*16 + r
+    // of this wave's 128 rows, columns n = j*16 + 4*lg of its 64.  Stored as
+    // is, every store instruction would write 64 bytes to each of 16 rows,
+    // half cache lines, when all CUs write their tiles at the same moment.
+    // Each 16 x 64 block (one i) therefore goes through this wave's 4 KiB of
+    // LDS (16-byte chunks XOR-swizzled by row: conflict-free both ways) and
+    // comes back row-contiguous: each store writes 256 bytes to each of 4
+    // rows.  The staging area is either unused by the tile loop or B stage 1:
+    // every read of the finished tile's B stages has completed (group 1's last
+    // load phase ended with a barrier before either group gets here), the next
+    // tile's first copies go to B stage 0 and the A regions, and its first
+    // copy into B stage 1 is issued after the barrier that ends this epilogue.
+    {
+      uint8_t* cst = smem + T::OFF_CST + wave * 4096;
+      // the epilogue's lane-dependent addresses are derived here, from a lane
+      // index the compiler cannot see through, so they are not hoisted out of
+      // the tile loop and kept live (in registers the K loop needs)
+      int le = lane;
+      asm volatile("" : "+v"(le));
+      const int lr = le & 15, llg = le >> 4;     // the fragment layout's (r, lg)
+      const int rr = le >> 4, cc = le & 15;      // read-back: row-in-quad, 16-byte chunk
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      float* crow = a.C + (int64_t)(m0 + grp * 128 + i * 16 + r) * a.N;
+      for (int i = 0; i < 8; i++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) *reinterpret_cast<v4f*>(crow + n0 + sw * 64 + j * 16 + 4 * lg) = acc[i][j];
+        for (int j = 0; j < 4; j++)
+          *reinterpret_cast<v4f*>(cst + lr * 256 + (((j * 4 + llg) ^ lr) << 4)) = acc[i][j];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int row = q * 4 + rr;
+          const v4f v = *reinterpret_cast<const v4f*>(cst + row * 256 + ((cc ^ row) << 4));
+          float* crow = a.C + (int64_t)(m0 + grp * 128 + i * 16 + row) * a.N;
+          *reinterpret_cast<v4f*>(crow + n0 + sw * 64 + cc * 4) = v;
+        }
+      }
     }
     const int next = tile + (int)gridDim.x;
     if (next >= total) break;
