@@ -142,6 +142,19 @@ def test_mx_gemm_large_tiles_full():
     assert r["ok"], r
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_mx_gemm_persistent_two_tiles_full(fmt):
+    """More 256 x 256 tiles (16 x 17 = 272) than the grid's one workgroup per
+    CU, so some workgroups run a second tile after the tile transition (next
+    tile's copies issued during the last compute phase, C staged through LDS);
+    block scales vary.  Checked in full."""
+    say("mx persistent two tiles", fmt)
+    M, N, K = 4096, 4352, 1024
+    a32, b32 = mx_sources("mxfp8_2048", M, N, K, seed=101 + fmt)
+    r, _ = mx_case(a32, b32, fmt)
+    assert r["ok"], r
+
+
 def test_mx_blockpow2_recipe_full():
     """Per-block magnitudes 2^U{-6..6}: scales vary block to block."""
     say("mx blockpow2")
@@ -258,6 +271,17 @@ def test_fp16_gemm_large_tiles_nk():
     w = mxin.WORKLOADS["mxfp8_2048"]
     a16, b16 = mxin.fp16_sources(w, True, 4096, 4096, 256, seed=3)
     pts = mxin.sample_points(4096, 4096, 20000)
+    r = _fp16_case(a16, b16, True, points=pts)
+    assert r["ok"], r
+
+
+def test_fp16_gemm_persistent_two_tiles():
+    """fp16 through the persistent kernel with more tiles than CUs, so some
+    workgroups run two tiles; sampled."""
+    say("fp16 persistent two tiles")
+    w = mxin.WORKLOADS["mxfp8_2048"]
+    a16, b16 = mxin.fp16_sources(w, True, 4096, 4352, 1024, seed=5)
+    pts = mxin.sample_points(4096, 4352, 40000)
     r = _fp16_case(a16, b16, True, points=pts)
     assert r["ok"], r
 
