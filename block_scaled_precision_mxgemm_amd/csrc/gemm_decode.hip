@@ -8,23 +8,22 @@
 //
 // Design (gfx950):
 //   * one persistent workgroup of 8 waves per CU owns a contiguous range of
-//     16-row blocks of B ("fragments") and streams them through LDS in
-//     stages of 16 rows x 1 KiB (a quarter row for the 8192-wide fp4 weights)
-//     with direct global->LDS copies.  Each copy instruction reads one row's
-//     contiguous 1 KiB, the access pattern that measured fastest on MI355X
-//     (5.8 TB/s for a 112 MiB read, against 4.3 TB/s when every instruction
-//     takes 64 bytes from each of 16 rows);
-//   * inside a stage row the 16-byte chunks are XOR-swizzled with the row
-//     index (applied on the global side, so the copy still writes LDS
+//     16-row blocks of B ("fragments");
+//   * wave w owns the k range [w K/8, (w+1) K/8) of every fragment and holds
+//     the matching A operands (16 rows) in registers for the whole kernel;
+//   * each wave streams its own k band of the fragment rows through a private
+//     LDS ring of kDecStages stages (16 rows x 128 bytes) with direct
+//     global->LDS copies of 8 rows x 128 bytes per instruction (whole cache
+//     lines; this pattern streams as fast as 1 KiB row segments on MI355X,
+//     5.7 TB/s for a 112 MiB read).  A wave waits only for its own copies:
+//     the stages need no workgroup barrier;
+//   * inside a 128-byte stage row the 16-byte chunks are XOR-swizzled with
+//     (row >> 1) & 7 (applied on the global side, so the copy still writes LDS
 //     linearly), which makes the MFMA fragment reads conflict-free;
-//   * a ring of kDecStages stages keeps the copies of the next stages in
-//     flight while the current one is multiplied; one barrier per stage;
-//   * every wave takes 1/8 of each stage's MFMAs (2 for fp4, 1 for fp8) and
-//     holds the matching k range of A (16 rows) in registers for the whole
-//     kernel;
-//   * a fragment's 8 per-wave partial sums go to LDS and one wave adds them
-//     in a fixed order one stage later, so the result is deterministic and
-//     needs no atomics.
+//   * a fragment's 8 per-wave partial sums meet in LDS after one barrier per
+//     fragment; one wave adds them in a fixed order, so the result is
+//     deterministic and needs no atomics, and keeps the sum in registers: C
+//     is stored after the stream.
 #include <utility>
 
 #include "mxg_device.h"
@@ -34,8 +33,15 @@ namespace mxg {
 namespace {
 
 constexpr int kDecWaves = 8;
-constexpr int kDecStages = 7;
-constexpr int kStageRowBytes = 1024;  // bytes of one B row per stage
+constexpr int kDecStages = 8;                 // per-wave ring depth (a power of two)
+constexpr int kBand = 128;                    // bytes of each weight row per stage and wave
+constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
+// Reduced output fragments a wave keeps in registers until its copies are
+// done.  A store issued inside the stream would sit among the copies in the
+// in-order vector-memory counter and make the next stage waits of that wave
+// also wait for the store and for one more stage; with the barrier per
+// fragment every wave would then lose that time.
+constexpr int kHeld = 4;
 
 struct DecArgs {
   const uint8_t* A;
@@ -47,23 +53,28 @@ struct DecArgs {
   int nfrags;  // ceil(N / 16)
 };
 
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <bool BF4, int KA>
+// KW: MFMAs (128 k each) per wave per fragment, K / 1024.
+template <bool BF4, int KW>
 struct Decode {
-  static constexpr int MPW = BF4 ? 2 : 1;          // MFMAs per wave per stage
-  static constexpr int MPS = MPW * kDecWaves;      // MFMAs per stage (128 k each)
-  static constexpr int NQ = KA / MPW;              // stages per fragment
-  static constexpr int SROW = BF4 ? 64 : 32;       // scale bytes per row per stage
-  static constexpr int SZ_ST = 16 * kStageRowBytes;
-  static constexpr int SC_WAVE = 256;               // scale slot per wave per stage (64 lanes x 4 B)
-  static constexpr int SZ_SC = kDecWaves * SC_WAVE;
-  static constexpr int OFF_ST = 0;
-  static constexpr int OFF_SC = OFF_ST + kDecStages * SZ_ST;
-  static constexpr int OFF_PART = OFF_SC + kDecStages * SZ_SC;
+  static constexpr int D = kDecStages;
+  static constexpr int MPS = BF4 ? 2 : 1;                // MFMAs per stage (128 bytes of a row)
+  static constexpr int NQ = KW / MPS;                    // stages per fragment
+  static constexpr int WB = BF4 ? KW * 64 : KW * 128;    // bytes of a weight row per wave
+  static constexpr int SBW = 4 * KW;                     // scale bytes of a row per wave
+  static constexpr int LPR = SBW / 4;                    // scale copy lanes per row (4 bytes each)
+  static constexpr int NSI = (16 * LPR + 63) / 64;       // scale copies per fragment
+  // scale slots: a fragment's slot is refilled only after its last stage
+  static constexpr int NSL = (NQ - 1 + D + NQ - 1) / NQ;
+  static constexpr int SZ_SC = NSI * 256;
+  static constexpr int SZ_WAVE = D * kStageBytes + NSL * SZ_SC;
+  static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
   static constexpr int LDS = OFF_PART + 2 * kDecWaves * 64 * 16;
+  static constexpr int NSA = KW > 4 ? 2 : 1;             // loads of this wave's A scale dwords
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
-  static_assert(NQ >= 1 && KA % MPW == 0, "whole stages per fragment");
+  static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
+  static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
 
   // fp8 operand of the MFMA covering k0 .. k0+127 of row `p` (p at k0):
   // lane group g holds k0 + 16g .. +15 and k0 + 64 + 16g .. +15
@@ -73,13 +84,17 @@ struct Decode {
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 
-  static __device__ __forceinline__ void reduce_store(const DecArgs& a, const uint8_t* smem, int frag, int slot,
-                                                      int lane, int g, int r) {
+  // Sum of the 8 per-wave partials of a fragment, in wave order.  Lane (g, r)
+  // holds C[r][16 frag + 4g .. 4g+3].
+  static __device__ __forceinline__ v4f reduce(const uint8_t* smem, int slot, int lane) {
     const v4f* part = reinterpret_cast<const v4f*>(smem + OFF_PART) + (size_t)slot * kDecWaves * 64;
     v4f s = part[lane];
 #pragma unroll
     for (int w = 1; w < kDecWaves; w++) s += part[w * 64 + lane];
-    // lane (g, r) holds C[r][16 frag + 4g .. 4g+3]
+    return s;
+  }
+
+  static __device__ __forceinline__ void store_c(const DecArgs& a, int frag, v4f s, int g, int r) {
     const int m = r;
     const int n = frag * 16 + 4 * g;
     if (m < a.M) {
@@ -94,97 +109,119 @@ struct Decode {
     }
   }
 
-  // Per-workgroup state shared by the stage functions (all in registers
-  // once inlined).
+  // Per-wave state (all in registers once inlined).
   struct State {
     const DecArgs* a;
-    uint8_t* smem;
+    uint8_t* smem;  // workgroup LDS
+    uint8_t* wsm;   // this wave's ring and scale slots
     int lane, wave, g, r;
-    int f_begin, nf, S;
-    uint32_t rb, nb;  // bytes per B row, scale bytes per row
-    uint32_t vo0, vo1, sbyte_l;
-    int srow_l;
-    v8i av[KA];   // A operands of this wave's MFMAs
-    uint32_t sa[KA];  // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
-    v4f acc[MPW];
+    int f_begin, nf;
+    uint32_t rb, nb;      // bytes per B row, scale bytes per row
+    int brow;             // lane's row in a copy of 8 rows
+    uint32_t bch[2];      // lane's swizzled chunk offset, rows 0-7 / 8-15
+    int srow[NSI];        // lane's row in each scale copy
+    uint32_t scol[NSI];   // and its byte in that row's band
+    v8i av[KW];           // A operands of this wave's MFMAs
+    uint32_t sa[KW];      // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
+    v4f acc[MPS];
+    v4f held[kHeld];      // reduced fragments w, w + 8, ..., stored at the end
   };
 
-  // Vector-memory instructions per A load group (stage q of the A registers):
-  // lo and hi 16-byte halves per MFMA plus one load of the MPW scale dwords.
-  static constexpr int LA = 2 * MPW + 1;
-  static constexpr int kYoung = 3 * (kDecStages - 2);  // copies of the younger stages in flight
+  // Vector-memory instructions of the A loads that stage q of the first
+  // fragment needs: lo and hi halves per MFMA, and the scale dwords with q = 0.
+  static constexpr int la(int q) { return 2 * MPS + (q == 0 ? NSA : 0); }
+  static constexpr int la_from(int q) { return q >= NQ ? 0 : la(q) + la_from(q + 1); }
+  // Copies issued after stage s's copies and before its wait: the copies of
+  // stages s+1 .. s+D-2 (2 weight copies each, plus the scale copies at every
+  // fragment start) and, in the first fragment, the A loads of stages
+  // q .. NQ-1 issued by the prologue after stage q's copies.
+  static constexpr int younger(int q, bool first) {
+    return 2 * (D - 2) + NSI * ((q + D - 2) / NQ) + (first && q <= D - 2 ? la_from(q) : 0);
+  }
 
   template <int N>
   static __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
   }
+  // the copies wait, plus every LDS access issued so far: the buffer and the
+  // scale slot that the next copies refill were read at the previous stage
+  template <int N>
+  static __device__ __forceinline__ void wait_stage() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"i"(N) : "memory");
+  }
   static __device__ __forceinline__ void order_fence() { asm volatile("" ::: "memory"); }
 
-  // Copies of stage s: wave w fetches stage rows 2w and 2w+1 (lane l writes
-  // physical chunk l of the row and fetches logical chunk l ^ (row & 15)) and
-  // the scale bytes of the same two rows into its own 256-byte slot, 4 bytes
-  // per lane (global->LDS copies of fewer than 4 bytes still write one dword
-  // per lane): row 2w at slot byte 0, row 2w+1 at SROW; the remaining lanes
-  // fetch a valid address again into the slot's unused tail.  Every wave
-  // issues exactly 3 copies per stage, all lanes active, which the wait
-  // counts rely on (a copy under a lane condition could be skipped, and the
-  // compiler would then count conservatively).
-  static __device__ __forceinline__ void issue(State& t, int s) {
+  // Copies of stage q of fragment fs (fs may run past the workgroup's last
+  // fragment: then the last stage's source is read again into a buffer no
+  // live stage uses, which keeps the number of copies per stage fixed, as the
+  // wait counts require).  Rows past N read row N-1 again.  Every copy is
+  // issued by all lanes, unconditionally.
+  // (q is a constant at every call site once inlined)
+  static __device__ __forceinline__ void issue(State& t, int fs, int q) {
     constexpr int kRsrcWord3 = 0x00020000;
     const DecArgs& a = *t.a;
-    // past the workgroup's last stage, that stage's source again: the copy
-    // lands in a buffer no real stage still needs, and the copy count per
-    // stage stays fixed
-    const int buf = s % kDecStages;
-    const int sv = min(s, t.S - 1);
-    const int f = sv / NQ, q = sv - f * NQ;
-    const int row0 = (t.f_begin + f) * 16;
+    const bool past = fs >= t.nf;
+    const int fv = past ? t.nf - 1 : fs;
+    const int qv = past ? NQ - 1 : q;
+    const int row0 = (t.f_begin + fv) * 16;
+    const int last = a.N - 1 - row0;
+    if (q == 0) {
+      const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * t.nb), 0, 16 * t.nb,
+                                                          kRsrcWord3);
+      uint8_t* sc = t.wsm + D * kStageBytes + (fs % NSL) * SZ_SC;
+#pragma unroll
+      for (int i = 0; i < NSI; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(sc + i * 256), 4,
+                                                 (uint32_t)min(t.srow[i], last) * t.nb + t.scol[i],
+                                                 (uint32_t)(t.wave * SBW), 0, 0);
+    }
     const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * t.rb), 0, 16 * t.rb, kRsrcWord3);
-    const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * t.nb), 0, 16 * t.nb, kRsrcWord3);
-    uint8_t* st = t.smem + OFF_ST + buf * SZ_ST;
-    const int r0 = min(row0 + 2 * t.wave, a.N - 1) - row0;  // rows past N: the last row again
-    const int r1 = min(row0 + 2 * t.wave + 1, a.N - 1) - row0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + (2 * t.wave) * kStageRowBytes), 16, t.vo0,
-                                             (uint32_t)r0 * t.rb + (uint32_t)q * kStageRowBytes, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + (2 * t.wave + 1) * kStageRowBytes), 16, t.vo1,
-                                             (uint32_t)r1 * t.rb + (uint32_t)q * kStageRowBytes, 0, 0);
-    const uint32_t sr = (uint32_t)(min(row0 + t.srow_l, a.N - 1) - row0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(t.smem + OFF_SC + buf * SZ_SC + t.wave * SC_WAVE), 4,
-                                             sr * t.nb + t.sbyte_l, (uint32_t)q * SROW, 0, 0);
+    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * kStageBytes;
+    const uint32_t soff = (uint32_t)(t.wave * WB + qv * kBand);
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), 16,
+                                               (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0, 0);
   }
 
-  // A for the stage-q MFMAs of this wave (rows clamped to M-1; rows >= M are
-  // computed and discarded): local MFMA u -> global MFMA j = q * MPS +
-  // wave * MPW + u covering k 128j .. 128j+127; its scale is byte g of the
-  // dword of blocks 4j .. 4j+3.
+  // A operands for stage q of this wave (rows clamped to M-1; rows >= M are
+  // computed and discarded): wave MFMA j = q * MPS + u covers k 128 (w KW + j)
+  // .. +127; its scale is byte g of the dword of blocks 4 (w KW + j) .. +3.
   template <int Q>
   static __device__ __forceinline__ void load_a(State& t) {
     const DecArgs& a = *t.a;
     const int m = min(t.r, a.M - 1);
-    const uint8_t* row = a.A + (int64_t)m * a.K;
-    const uint8_t* srow = a.SA + (int64_t)m * t.nb;
-    const int j0 = Q * MPS + t.wave * MPW;
+    const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.wave * KW * 128;
 #pragma unroll
-    for (int u = 0; u < MPW; u++) t.av[Q * MPW + u] = load_fp8_op(row + (int64_t)(j0 + u) * 128, t.g);
-    // the scale dwords stay raw until the MFMA: extracting the byte here would
-    // wait for this load in the middle of the prologue
-    if constexpr (MPW == 2) {
-      const v2i d = *reinterpret_cast<const v2i*>(srow + 4 * j0);  // one 8-byte load
-      t.sa[Q * MPW] = (uint32_t)d[0];
-      t.sa[Q * MPW + MPW - 1] = (uint32_t)d[1];
-    } else {
-      t.sa[Q * MPW] = *reinterpret_cast<const uint32_t*>(srow + 4 * j0);
+    for (int u = 0; u < MPS; u++) t.av[Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
+    if constexpr (Q == 0) {
+      // the scale dwords stay raw until the MFMA: extracting a byte here would
+      // wait for this load in the middle of the prologue
+      const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
+      if constexpr (KW == 2) {
+        const v2i d = *reinterpret_cast<const v2i*>(srow);
+        t.sa[0] = (uint32_t)d[0];
+        t.sa[1] = (uint32_t)d[1];
+      } else {
+#pragma unroll
+        for (int i = 0; i < NSA; i++) {
+          const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
+#pragma unroll
+          for (int e = 0; e < 4; e++) t.sa[4 * i + e] = (uint32_t)d[e];
+        }
+      }
     }
   }
 
   // Prologue, in this issue order: stage p's copies then A(p), for p = 0 ..;
-  // stages up to kDecStages - 2, A up to NQ - 1.
+  // stages up to D - 2, A up to NQ - 1.
   template <int... P>
   static __device__ __forceinline__ void prologue(State& t, std::integer_sequence<int, P...>) {
     (
         [&] {
-          if (P < kDecStages - 1) issue(t, P);
+          if constexpr (P <= D - 2) issue(t, P / NQ, P % NQ);
           order_fence();
           if constexpr (P < NQ) load_a<P>(t);
           order_fence();
@@ -192,48 +229,36 @@ struct Decode {
         ...);
   }
 
-  // Stage q of fragment f (s = f * NQ + q).
+  // Stage q of fragment f.
   template <int Q, bool FIRST>
   static __device__ __forceinline__ void stage(State& t, int f) {
-    const DecArgs& a = *t.a;
-    const int s = f * NQ + Q, buf = s % kDecStages;
-    // This wave's copies of stage s are complete once at most the younger
+    // this wave's copies of the stage are complete once at most the younger
     // vector-memory instructions are outstanding (the counter completes in
-    // issue order).  Younger than stage s's copies: the copies of the
-    // kDecStages - 2 younger stages (always issued, see issue()) and, in the
-    // first fragment, the A loads of stages q .. NQ-1 when stage q was a
-    // prologue stage.  Stores of C issued since are younger still and only
-    // make the wait stricter.
-    if (FIRST && Q < kDecStages - 1)
-      wait_vm<kYoung + (Q < kDecStages - 1 ? LA * (NQ - Q) : 0)>();
-    else
-      wait_vm<kYoung>();
-    stage_barrier();                       // publishes every wave's copies of stage s
-    issue(t, s + kDecStages - 1);          // into the buffer read at stage s-1
-    // the previous fragment's partials were published by the barrier
-    if (!FIRST && Q == 0 && t.wave == (f - 1) % kDecWaves)
-      reduce_store(a, t.smem, t.f_begin + f - 1, (f - 1) & 1, t.lane, t.g, t.r);
-    const uint8_t* st = t.smem + OFF_ST + buf * SZ_ST;
-    const uint8_t* sc = t.smem + OFF_SC + buf * SZ_SC;
+    // issue order; stores of C issued since are younger still and only make
+    // the wait stricter)
+    wait_stage<younger(Q, FIRST)>();
+    // stage s + D - 1, into the buffer read at stage s - 1
+    issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ);
+    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * kStageBytes;
+    const uint8_t* sc = t.wsm + D * kStageBytes + (f % NSL) * SZ_SC;
     const int g = t.g, r = t.r;
+    const int sw = (r >> 1) & 7;
 #pragma unroll
-    for (int u = 0; u < MPW; u++) {
-      const int lj = t.wave * MPW + u;  // MFMA index inside the stage
+    for (int u = 0; u < MPS; u++) {
+      const int j = Q * MPS + u;  // this wave's MFMA index inside the fragment
       v8i bv;
       if (BF4) {
-        const int ch = (lj * 4 + g) ^ r;  // 16-byte chunk, swizzled
-        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + ch * 16);
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 * u + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
       } else {
-        const int cl = (lj * 8 + g) ^ r, chh = (lj * 8 + 4 + g) ^ r;
-        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + cl * 16);
-        const v4i hi = *reinterpret_cast<const v4i*>(st + r * kStageRowBytes + chh * 16);
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + ((g ^ sw) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      const int sb = sc[(r >> 1) * SC_WAVE + (r & 1) * SROW + lj * 4 + g];
-      t.acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, t.av[Q * MPW + u], t.acc[u],
-                                                                  BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8, 0, sb, 0,
-                                                                  (int)__builtin_amdgcn_ubfe(t.sa[Q * MPW + u], 8 * g, 8));
+      const int sb = sc[r * SBW + 4 * j + g];
+      t.acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, t.av[j], t.acc[u], BF4 ? kFmtFp4 : kFmtFp8,
+                                                                  kFmtFp8, 0, sb, 0,
+                                                                  (int)__builtin_amdgcn_ubfe(t.sa[j], 8 * g, 8));
     }
   }
 
@@ -242,10 +267,25 @@ struct Decode {
     (stage<Q, FIRST>(t, f), ...);
     v4f p = t.acc[0];
 #pragma unroll
-    for (int u = 1; u < MPW; u++) p += t.acc[u];
+    for (int u = 1; u < MPS; u++) p += t.acc[u];
     reinterpret_cast<v4f*>(t.smem + OFF_PART)[((f & 1) * kDecWaves + t.wave) * 64 + t.lane] = p;
 #pragma unroll
-    for (int u = 0; u < MPW; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < MPS; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    // every wave's partial of fragment f is in LDS after the barrier; the
+    // slot is written again two fragments later, after the next barrier,
+    // which the reducing wave reaches only once it has read it
+    wg_barrier();
+    if (t.wave == f % kDecWaves) {
+      const v4f c = reduce(t.smem, f & 1, t.lane);
+      const int j = f / kDecWaves;  // wave f % 8 reduces fragments f % 8 + 8j
+      if (j < kHeld) {
+#pragma unroll
+        for (int i = 0; i < kHeld; i++)
+          if (i == j) t.held[i] = c;
+      } else {
+        store_c(*t.a, t.f_begin + f, c, t.g, t.r);  // past the held ones: correct, with stricter waits
+      }
+    }
   }
 
   static __device__ __forceinline__ void run(const DecArgs& a) {
@@ -256,44 +296,54 @@ struct Decode {
     const int tid = threadIdx.x;
     t.lane = tid & 63;
     t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    t.wsm = smem + t.wave * SZ_WAVE;
     t.g = t.lane >> 4;
     t.r = t.lane & 15;
     // balanced contiguous split of the fragments over the workgroups (each
     // has at least one: the grid is at most the fragment count)
     t.f_begin = (int)((int64_t)a.nfrags * blockIdx.x / gridDim.x);
     t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
-    t.S = t.nf * NQ;
     t.rb = BF4 ? (uint32_t)(a.K >> 1) : (uint32_t)a.K;
     t.nb = (uint32_t)(a.K >> 5);
-    constexpr int SL = SROW / 4;  // scale lanes per row
-    t.vo0 = (uint32_t)((t.lane ^ ((2 * t.wave) & 15)) * 16);
-    t.vo1 = (uint32_t)((t.lane ^ ((2 * t.wave + 1) & 15)) * 16);
-    const int sl = t.lane < 2 * SL ? t.lane : 2 * SL - 1;  // lanes past the two rows repeat the last one
-    t.srow_l = 2 * t.wave + sl / SL;
-    t.sbyte_l = (uint32_t)((sl % SL) * 4);
-
-    prologue(t, std::make_integer_sequence<int, (kDecStages - 1 > NQ ? kDecStages - 1 : NQ)>{});
+    // copy lane l: row l >> 3 (+8), physical chunk l & 7 holding logical chunk
+    // (l & 7) ^ ((row >> 1) & 7)
+    t.brow = t.lane >> 3;
 #pragma unroll
-    for (int u = 0; u < MPW; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; h++) t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * 16);
+    // scale copy i, lane l: entry e = 64 i + l is row e / LPR, dword e % LPR
+    // (entries past row 15 repeat row 15 into the slot's unused tail)
+#pragma unroll
+    for (int i = 0; i < NSI; i++) {
+      const int e = 64 * i + t.lane;
+      t.srow[i] = min(e / LPR, 15);
+      t.scol[i] = (uint32_t)(4 * (e % LPR));
+    }
+
+    prologue(t, std::make_integer_sequence<int, (D - 1 > NQ ? D - 1 : NQ)>{});
+#pragma unroll
+    for (int u = 0; u < MPS; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // the first fragment (exact wait counts while A is arriving), then the rest
     fragment<true>(t, 0, std::make_integer_sequence<int, NQ>{});
     for (int f = 1; f < t.nf; f++) fragment<false>(t, f, std::make_integer_sequence<int, NQ>{});
-    stage_barrier();
-    if (t.wave == (t.nf - 1) % kDecWaves) reduce_store(a, smem, t.f_begin + t.nf - 1, (t.nf - 1) & 1, t.lane, t.g, t.r);
+#pragma unroll
+    for (int i = 0; i < kHeld; i++) {
+      const int f = t.wave + kDecWaves * i;
+      if (f < t.nf) store_c(a, t.f_begin + f, t.held[i], t.g, t.r);
+    }
     wait_vm<0>();  // no copy into LDS may still be in flight when the workgroup ends
   }
 };
 
-template <bool BF4, int KA>
+template <bool BF4, int KW>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void decode_kernel(DecArgs a) {
-  Decode<BF4, KA>::run(a);
+  Decode<BF4, KW>::run(a);
 }
 
-template <bool BF4, int KA>
+template <bool BF4, int KW>
 hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   const int grid = a.nfrags < cus ? a.nfrags : cus;
-  hipLaunchKernelGGL((decode_kernel<BF4, KA>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<BF4, KW>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -307,7 +357,6 @@ hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream) {
 }
 
 }  // namespace
-
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB) {
   return M <= 16 && (fmt == 0 || fmt == 1) && (K == 2048 || K == 4096 || K == 8192) &&
          (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;

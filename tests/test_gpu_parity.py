@@ -163,12 +163,14 @@ def test_mx_blockpow2_recipe_full():
     assert r["ok"], r
 
 
-# The decode kernel (M <= 16, K in {2048, 4096, 8192}) streams 16-row weight
-# fragments through LDS in stages of 1 KiB per row: N not a multiple of 16 (or
-# of 4) exercises the clamped last weight rows and the scalar output tail; few
-# fragments per workgroup (N = 64, 300) and many (N = 4165 and the full
-# decode workload) cover the stage ring's prologue, tail and the partial-sum
-# slots; K = 4608 and 1536 take the split-K skinny kernel instead.
+# The decode kernel (M <= 16, K in {2048, 4096, 8192}) gives each of its 8
+# waves one eighth of K and streams that band of 16-row weight fragments
+# through a per-wave LDS ring: N not a multiple of 16 (or of 4) exercises the
+# clamped last weight rows and the scalar output tail; one fragment per
+# workgroup (N = 16, 64, 250, 300: the ring's prologue runs past the last
+# stage) and several (N = 1001, 4165, 5000 and the full decode workload) cover
+# the ring, the scale slots and the partial-sum slots; K = 4608 and 1536 take
+# the split-K skinny kernel instead.
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (7, 1000, 1536), (16, 1001, 4608), (13, 250, 8192),
                                    (16, 4165, 4096), (3, 64, 8192), (16, 16, 2048), (9, 5000, 8192)])
@@ -202,7 +204,7 @@ def test_accumulator_width_on_gpu():
 def test_nan_propagation():
     say("nan propagation")
     rng = np.random.default_rng(5)
-    for M, K in ((8, 256), (8, 1024), (200, 256)):   # skinny, decode and tiled kernels
+    for M, K in ((8, 256), (8, 2048), (200, 256)):   # skinny, decode and tiled kernels
         N = 40
         a32 = rng.standard_normal((M, K)).astype(np.float32)
         b32 = rng.standard_normal((N, K)).astype(np.float32)
