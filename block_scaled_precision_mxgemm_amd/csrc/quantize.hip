@@ -48,64 +48,43 @@ __device__ __forceinline__ Mag split_abs(uint32_t bits) {
 
 __device__ __forceinline__ int floor_log2_u(uint32_t s) { return 31 - __clz((int)s); }
 
-// round(s / 2^sh) with ties to even; s < 2^24.
-__device__ __forceinline__ uint32_t rne_shift(uint32_t s, int sh) {
-  if (sh <= 0) return s << (-sh);
-  if (sh >= 26) return 0u;
-  const uint32_t q = s >> sh;
-  const uint32_t rem = s & ((1u << sh) - 1u);
-  const uint32_t half = 1u << (sh - 1);
-  return q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+// Code of x * 2^-e in a format with MBITS mantissa bits whose smallest normal
+// exponent is KMIN, saturated at MAXCODE (sign not included), branch-free:
+//   |x| = m * 2^(k - 23) with m in [2^23, 2^24) (subnormal x normalized first)
+//   so k = floor(log2 |x * 2^-e|);
+//   normal results (k >= KMIN): q = m / 2^(23 - MBITS) rounded to nearest, ties
+//   to even, lies in [2^MBITS, 2^(MBITS+1)], and the code is
+//   ((k - KMIN) << MBITS) + q, the carry of q = 2^(MBITS+1) running into the
+//   exponent field by itself;
+//   subnormal results (k < KMIN): the spacing is fixed at 2^(KMIN - MBITS), so
+//   q = m / 2^(23 - MBITS + KMIN - k) rounded the same way is the code, and
+//   q = 2^MBITS is the smallest normal;
+//   zero (m = 0) gives q = 0, shifts past 31 bits give 0, and every code
+//   above MAXCODE (the largest finite value) saturates to it.
+template <int MBITS, int KMIN, uint32_t MAXCODE>
+__device__ __forceinline__ uint32_t encode_mag(uint32_t bits, int e) {
+  const uint32_t ex = (bits >> 23) & 0xffu;
+  const uint32_t mant = bits & 0x7fffffu;
+  const uint32_t lz = (uint32_t)__clz((int)mant) - 8u;  // 24 for mant = 0
+  const bool sub = ex == 0u;
+  const uint32_t m = sub ? (mant << lz) : (mant | 0x800000u);
+  const int k = (sub ? 1 - (int)lz : (int)ex) - 127 - e;
+  const int t = k - KMIN;
+  const uint32_t sh = (uint32_t)min(23 - MBITS + max(-t, 0), 31);
+  const uint32_t lsb = (m >> sh) & 1u;
+  const uint32_t q = (m + ((1u << (sh - 1u)) - 1u) + lsb) >> sh;
+  const uint32_t code = q + ((uint32_t)max(t, 0) << MBITS);
+  return min(code, MAXCODE);
 }
 
-// E4M3 code of x * 2^-e (sign from x).
+// E4M3 (bias 7, 3 mantissa bits, no infinity, largest finite 448 = 0x7E) and
+// E2M1 (bias 1, 1 mantissa bit, largest 6 = 0x7) codes of x * 2^-e.
 __device__ __forceinline__ uint32_t encode_e4m3(uint32_t bits, int e) {
-  const uint32_t sign = (bits >> 31) << 7;
-  const Mag m = split_abs(bits);
-  if (m.s == 0) return sign;
-  const int base = m.ex - 23 - e;              // |v| = s * 2^base
-  const int fl = floor_log2_u(m.s) + base;     // floor(log2 |v|)
-  const int qe = max(fl, -6) - 3;              // grid spacing 2^qe
-  uint32_t q = rne_shift(m.s, qe - base);      // |v| / 2^qe, rounded
-  uint32_t code;
-  if (qe == -9) {
-    code = q;                                  // subnormal step 2^-9; q = 8 is 2^-6
-  } else {
-    int ef = qe + 10;                          // biased exponent field (bias 7)
-    if (q == 16u) {
-      ++ef;
-      q = 8u;
-    }
-    const uint32_t mant = q - 8u;
-    if (ef > 15 || (ef == 15 && mant == 7u))
-      code = 0x7eu;                            // saturate at 448
-    else
-      code = ((uint32_t)ef << 3) | mant;
-  }
-  return code | sign;
+  return encode_mag<3, -6, 0x7Eu>(bits, e) | ((bits >> 31) << 7);
 }
 
-// E2M1 nibble of x * 2^-e (sign from x).
 __device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
-  const uint32_t sign = (bits >> 31) << 3;
-  const Mag m = split_abs(bits);
-  if (m.s == 0) return sign;
-  const int base = m.ex - 23 - e;
-  const int fl = floor_log2_u(m.s) + base;
-  const int qe = max(fl, 0) - 1;
-  uint32_t q = rne_shift(m.s, qe - base);
-  uint32_t code;
-  if (qe == -1) {
-    code = q;                                  // 0, 0.5 or (q = 2) 1.0
-  } else {
-    int ef = qe + 2;                           // biased exponent field (bias 1)
-    if (q == 4u) {
-      ++ef;
-      q = 2u;
-    }
-    code = (ef > 3) ? 7u : (((uint32_t)ef << 1) | (q - 2u));  // saturate at 6
-  }
-  return code | sign;
+  return encode_mag<1, 0, 0x7u>(bits, e) | ((bits >> 31) << 3);
 }
 
 // One block of 32: lanes sub = 0..7 of the block hold its elements 4*sub ..

@@ -102,6 +102,32 @@ def test_quantize_all_e4m3_ties():
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
+@pytest.mark.parametrize("elem", [oracle.E4M3, oracle.E2M1])
+def test_quantize_every_mantissa_at_boundary_exponents(elem):
+    """All 2^23 fp32 mantissas, both signs, at the exponents where the
+    rounding changes regime, with the block maximum fixed so the scale is
+    2^0: for E4M3 the round-to-zero edge (2^-10), the last subnormal and first
+    normal binades (2^-7, 2^-6) and the saturating top binade (2^8); for E2M1
+    2^-2 (round to zero or 0.5), 2^-1 (subnormal), 2^0 and 2^2 (saturation)."""
+    say("quantize every mantissa", elem)
+    if elem == oracle.E4M3:
+        amax, ks = np.float32(256.0), (-10, -7, -6, 8)
+    else:
+        amax, ks = np.float32(4.0), (-2, -1, 0, 2)
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    for k in ks:
+        for sign in (0, 1):
+            v = ((np.uint32(sign) << np.uint32(31)) | (np.uint32(k + 127) << np.uint32(23)) | mant).view(np.float32)
+            v = np.concatenate([v, v[:(-len(v)) % 31]]).reshape(-1, 31)
+            x = np.empty((v.shape[0], 32), dtype=np.float32)
+            x[:, 0] = amax
+            x[:, 1:] = np.clip(v, -amax * np.float32(1.99), amax * np.float32(1.99))
+            q, s = gpu_quantize(x, elem)
+            qo, so = oracle.quantize(x, elem)
+            assert np.array_equal(s.cpu().numpy(), so), (k, sign)
+            assert np.array_equal(q.cpu().numpy(), qo), (k, sign)
+
+
 # ------------------------------------------------------------ MX GEMM, small
 
 SMALL_SHAPES = [
