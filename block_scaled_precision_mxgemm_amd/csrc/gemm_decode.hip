@@ -162,15 +162,18 @@ struct Decode {
   }
   static __device__ __forceinline__ void order_fence() { asm volatile("" ::: "memory"); }
 
-  // Copies of stage q of fragment fs (fs may run past the workgroup's last
-  // fragment: then the last stage's source is read again into a buffer no
-  // live stage uses, which keeps the number of copies per stage fixed, as the
-  // wait counts require).  Rows past N read row N-1 again.  Every copy is
-  // issued by all lanes, unconditionally.
+  // Copies of stage q of fragment fs.  fs may run past the workgroup's last
+  // fragment.  In the prologue and the first fragment (fixed == true) the
+  // last stage's source is then read again into a buffer no live stage uses:
+  // the number of copies per stage stays fixed, so the compiler's own wait
+  // counts for the A loads interleaved there stay exact.  Later such copies
+  // are skipped (the stage waits then account for it).  Rows past N read row
+  // N-1 again.  Every copy that is issued is issued by all lanes.
   // (q is a constant at every call site once inlined)
-  static __device__ __forceinline__ void issue(State& t, int fs, int q) {
+  static __device__ __forceinline__ void issue(State& t, int fs, int q, bool fixed) {
     constexpr int kRsrcWord3 = 0x00020000;
     const DecArgs& a = *t.a;
+    if (!fixed && fs >= t.nf) return;
     const bool past = fs >= t.nf;
     const int fv = past ? t.nf - 1 : fs;
     const int qv = past ? NQ - 1 : q;
@@ -231,7 +234,7 @@ struct Decode {
   static __device__ __forceinline__ void prologue(State& t, std::integer_sequence<int, P...>) {
     (
         [&] {
-          if constexpr (P <= D - 2) issue(t, P / NQ, P % NQ);
+          if constexpr (P <= D - 2) issue(t, P / NQ, P % NQ, true);
           order_fence();
           if constexpr (P < NQ) load_a<P>(t);
           order_fence();
@@ -245,10 +248,15 @@ struct Decode {
     // this wave's copies of the stage are complete once at most the younger
     // vector-memory instructions are outstanding (the counter completes in
     // issue order; stores of C issued since are younger still and only make
-    // the wait stricter)
-    wait_stage<younger(Q, FIRST)>();
+    // the wait stricter).  Past the first fragment, when a younger stage lies
+    // beyond the last one its copies were skipped, and the stage waits for
+    // everything instead.
+    if (FIRST || (f * NQ + Q) + D - 2 < t.nf * NQ)
+      wait_stage<younger(Q, FIRST)>();
+    else
+      wait_stage<0>();
     // stage s + D - 1, into the buffer read at stage s - 1
-    issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ);
+    issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ, FIRST);
     const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * kStageBytes;
     const uint8_t* sc = t.wsm + D * kStageBytes + (f % NSL) * SZ_SC;
     const int g = t.g, r = t.r;
