@@ -15,8 +15,8 @@ import torch
 
 import oracle
 from block_scaled_precision_mxgemm_amd import inputs as mxin
-from gpu_util import (DEV, FMT_ELEMS, binding, gpu_mx, gpu_quantize, mx_case, mx_sources, nan_canary, say,
-                      to_dev)
+from gpu_util import (DEV, FMT_ELEMS, MFMA_ALIGNMENT_TERMS, binding, gpu_mx, gpu_quantize, mx_case, mx_sources,
+                      nan_canary, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,6 +205,45 @@ def test_mx_gemm_decode_kernel_full(fmt, M, N, K):
     a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=7 * M + N + K + fmt)
     r, _ = mx_case(a32, b32, fmt)
     assert r["ok"], r
+
+
+# Scale planes at an odd byte address: the ABI takes any alignment for them;
+# the ping-pong and decode kernels need 4-byte aligned scale rows, so these
+# shapes must fall back (256-wide tiled, skinny and 128-wide tiled kernels
+# with byte-wise scale loads) and still match the oracle.
+@pytest.mark.parametrize("M,N,K,fmt,npts", [(4096, 4096, 256, 0, 20000), (16, 1000, 2048, 1, None),
+                                            (8, 520, 384, 2, None), (300, 257, 512, 0, None)])
+def test_mx_gemm_unaligned_scale_planes(M, N, K, fmt, npts):
+    say("mx unaligned scales", M, N, K, fmt)
+    b = binding()
+    ea, eb = FMT_ELEMS[fmt]
+    a32, b32 = mx_sources("mxfp8_2048", M, N, K, seed=M + N + K + fmt)
+    qa, sa = gpu_quantize(a32, ea)
+    qb, sb = gpu_quantize(b32, eb)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 4, dtype=torch.uint8, device=DEV)
+        v = buf[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 4 == 1
+        return v
+
+    sa1, sb1 = shifted(sa), shifted(sb)
+    out = nan_canary(M, N)
+    b.mxgemm_run(qa, sa1, qb, sb1, fmt, out=out)
+    torch.cuda.synchronize()
+    c = out.cpu().numpy()
+    qa_n, sa_n, qb_n, sb_n = (t.cpu().numpy() for t in (qa, sa, qb, sb))
+    if npts is None:
+        ref, ab = oracle.mx_gemm(qa_n, sa_n, ea, qb_n, sb_n, eb, M, N, K)
+        got = c
+    else:
+        pts = mxin.sample_points(M, N, npts)
+        ref, ab = oracle.mx_gemm(qa_n, sa_n, ea, qb_n, sb_n, eb, M, N, K, points=pts)
+        got = c[pts[0], pts[1]]
+    r = oracle.gate(got, ref, ab, K, extra_terms=MFMA_ALIGNMENT_TERMS)
+    assert r["ok"], r
+    assert not np.isnan(c).any()
 
 
 def test_accumulator_width_on_gpu():
