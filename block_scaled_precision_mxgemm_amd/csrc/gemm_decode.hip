@@ -1,5 +1,6 @@
-// gemm_decode.hip - MX GEMM for decode shapes with at most 16 activation rows
-// (M <= 16) against a large weight matrix B (N x K, MXFP8 or MXFP4).  The
+// gemm_decode.hip - MX GEMM for decode shapes with few activation rows (M <= 64;
+// one launch per 32 rows at K = 8192) against a large weight matrix B (N x K,
+// MXFP8 or MXFP4).  The
 // product is bound by the bytes of B, which must stream from HBM exactly
 // once; the weight plane is what quantization shrinks ("Metal tensors で
 // カスタム機械学習オペレーションを最適化する", section "主要内容": inference
@@ -10,7 +11,9 @@
 //   * one persistent workgroup of 8 waves per CU owns a contiguous range of
 //     16-row blocks of B ("fragments");
 //   * wave w owns the k range [w K/8, (w+1) K/8) of every fragment and holds
-//     the matching A operands (16 rows) in registers for the whole kernel;
+//     the matching A operands (1 to 4 blocks of 16 rows) in registers for the
+//     whole kernel; each weight operand it reads from LDS feeds one MFMA per
+//     row block;
 //   * each wave streams its own k band of the fragment rows through a private
 //     LDS ring of kDecStages stages (16 rows x 128 bytes) with direct
 //     global->LDS copies of 8 rows x 128 bytes per instruction (whole cache
@@ -64,8 +67,10 @@ struct DecArgs {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// KW: MFMAs (128 k each) per wave per fragment, K / 1024.
-template <bool BF4, int KW>
+// KW: MFMAs (128 k each) per wave per fragment, K / 1024.  MB: blocks of 16
+// activation rows (M <= 16 MB); each weight operand read from LDS feeds one
+// MFMA per block, so the weight stream is the same for every MB.
+template <bool BF4, int KW, int MB>
 struct Decode {
   static constexpr int D = kDecStages;
   static constexpr int MPS = BF4 ? 2 : 1;                // MFMAs per stage (128 bytes of a row)
@@ -79,11 +84,14 @@ struct Decode {
   static constexpr int SZ_SC = NSI * 256;
   static constexpr int SZ_WAVE = D * kStageBytes + NSL * SZ_SC;
   static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
-  static constexpr int LDS = OFF_PART + 2 * kDecWaves * 64 * 16;
-  static constexpr int NSA = KW > 4 ? 2 : 1;             // loads of this wave's A scale dwords
+  static constexpr int SZ_PSLOT = MB * kDecWaves * 64 * 16;  // one fragment's partials
+  static constexpr int LDS = OFF_PART + 2 * SZ_PSLOT;
+  static constexpr int NSA = KW > 4 ? 2 : 1;             // loads of this wave's A scale dwords (per block)
+  static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
   static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
+  static_assert(MB >= 1 && MB * KW <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
 
   // fp8 operand of the MFMA covering k0 .. k0+127 of row `p` (p at k0):
   // lane group g holds k0 + 16g .. +15 and k0 + 64 + 16g .. +15
@@ -93,18 +101,18 @@ struct Decode {
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 
-  // Sum of the 8 per-wave partials of a fragment, in wave order.  Lane (g, r)
-  // holds C[r][16 frag + 4g .. 4g+3].
-  static __device__ __forceinline__ v4f reduce(const uint8_t* smem, int slot, int lane) {
-    const v4f* part = reinterpret_cast<const v4f*>(smem + OFF_PART) + (size_t)slot * kDecWaves * 64;
+  // Sum of the 8 per-wave partials of a fragment's row block mb, in wave
+  // order.  Lane (g, r) holds C[16 mb + r][16 frag + 4g .. 4g+3].
+  static __device__ __forceinline__ v4f reduce(const uint8_t* smem, int slot, int mb, int lane) {
+    const v4f* part = reinterpret_cast<const v4f*>(smem + OFF_PART + slot * SZ_PSLOT) + mb * kDecWaves * 64;
     v4f s = part[lane];
 #pragma unroll
     for (int w = 1; w < kDecWaves; w++) s += part[w * 64 + lane];
     return s;
   }
 
-  static __device__ __forceinline__ void store_c(const DecArgs& a, int frag, v4f s, int g, int r) {
-    const int m = r;
+  static __device__ __forceinline__ void store_c(const DecArgs& a, int frag, int mb, v4f s, int g, int r) {
+    const int m = 16 * mb + r;
     const int n = frag * 16 + 4 * g;
     if (m < a.M) {
       float* crow = a.C + (int64_t)m * a.N;
@@ -130,15 +138,15 @@ struct Decode {
     uint32_t bch[2];      // lane's swizzled chunk offset, rows 0-7 / 8-15
     int srow[NSI];        // lane's row in each scale copy
     uint32_t scol[NSI];   // and its byte in that row's band
-    v8i av[KW];           // A operands of this wave's MFMAs
-    uint32_t sa[KW];      // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
-    v4f acc[MPS];
-    v4f held[kHeld];      // reduced fragments w, w + 8, ..., stored at the end
+    v8i av[MB][KW];       // A operands of this wave's MFMAs, per row block
+    uint32_t sa[MB][KW];  // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
+    v4f acc[MB][MPS];
+    v4f held[HELD][MB];   // reduced fragments w, w + 8, ..., stored at the end
   };
 
   // Vector-memory instructions of the A loads that stage q of the first
   // fragment needs: lo and hi halves per MFMA, and the scale dwords with q = 0.
-  static constexpr int la(int q) { return 2 * MPS + (q == 0 ? NSA : 0); }
+  static constexpr int la(int q) { return MB * (2 * MPS + (q == 0 ? NSA : 0)); }
   static constexpr int la_from(int q) { return q >= NQ ? 0 : la(q) + la_from(q + 1); }
   // Copies issued after stage s's copies and before its wait: the copies of
   // stages s+1 .. s+D-2 (2 weight copies each, plus the scale copies at every
@@ -205,24 +213,27 @@ struct Decode {
   template <int Q>
   static __device__ __forceinline__ void load_a(State& t) {
     const DecArgs& a = *t.a;
-    const int m = min(t.r, a.M - 1);
-    const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.wave * KW * 128;
 #pragma unroll
-    for (int u = 0; u < MPS; u++) t.av[Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
-    if constexpr (Q == 0) {
-      // the scale dwords stay raw until the MFMA: extracting a byte here would
-      // wait for this load in the middle of the prologue
-      const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
-      if constexpr (KW == 2) {
-        const v2i d = *reinterpret_cast<const v2i*>(srow);
-        t.sa[0] = (uint32_t)d[0];
-        t.sa[1] = (uint32_t)d[1];
-      } else {
+    for (int mb = 0; mb < MB; mb++) {
+      const int m = min(16 * mb + t.r, a.M - 1);
+      const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.wave * KW * 128;
 #pragma unroll
-        for (int i = 0; i < NSA; i++) {
-          const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
+      for (int u = 0; u < MPS; u++) t.av[mb][Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
+      if constexpr (Q == 0) {
+        // the scale dwords stay raw until the MFMA: extracting a byte here
+        // would wait for this load in the middle of the prologue
+        const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
+        if constexpr (KW == 2) {
+          const v2i d = *reinterpret_cast<const v2i*>(srow);
+          t.sa[mb][0] = (uint32_t)d[0];
+          t.sa[mb][1] = (uint32_t)d[1];
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; e++) t.sa[4 * i + e] = (uint32_t)d[e];
+          for (int i = 0; i < NSA; i++) {
+            const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
+#pragma unroll
+            for (int e = 0; e < 4; e++) t.sa[mb][4 * i + e] = (uint32_t)d[e];
+          }
         }
       }
     }
@@ -274,34 +285,42 @@ struct Decode {
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       const int sb = sc[r * SBW + 4 * j + g];
-      t.acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, t.av[j], t.acc[u], BF4 ? kFmtFp4 : kFmtFp8,
-                                                                  kFmtFp8, 0, sb, 0,
-                                                                  (int)__builtin_amdgcn_ubfe(t.sa[j], 8 * g, 8));
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++)
+        t.acc[mb][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bv, t.av[mb][j], t.acc[mb][u], BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8, 0, sb, 0,
+            (int)__builtin_amdgcn_ubfe(t.sa[mb][j], 8 * g, 8));
     }
   }
 
   template <bool FIRST, int... Q>
   static __device__ __forceinline__ void fragment(State& t, int f, std::integer_sequence<int, Q...>) {
     (stage<Q, FIRST>(t, f), ...);
-    v4f p = t.acc[0];
 #pragma unroll
-    for (int u = 1; u < MPS; u++) p += t.acc[u];
-    reinterpret_cast<v4f*>(t.smem + OFF_PART)[((f & 1) * kDecWaves + t.wave) * 64 + t.lane] = p;
+    for (int mb = 0; mb < MB; mb++) {
+      v4f p = t.acc[mb][0];
 #pragma unroll
-    for (int u = 0; u < MPS; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int u = 1; u < MPS; u++) p += t.acc[mb][u];
+      reinterpret_cast<v4f*>(t.smem + OFF_PART + (f & 1) * SZ_PSLOT)[(mb * kDecWaves + t.wave) * 64 + t.lane] = p;
+#pragma unroll
+      for (int u = 0; u < MPS; u++) t.acc[mb][u] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
     // every wave's partial of fragment f is in LDS after the barrier; the
     // slot is written again two fragments later, after the next barrier,
     // which the reducing wave reaches only once it has read it
     wg_barrier();
     if (t.wave == f % kDecWaves) {
-      const v4f c = reduce(t.smem, f & 1, t.lane);
       const int j = f / kDecWaves;  // wave f % 8 reduces fragments f % 8 + 8j
-      if (j < kHeld) {
 #pragma unroll
-        for (int i = 0; i < kHeld; i++)
-          if (i == j) t.held[i] = c;
-      } else {
-        store_c(*t.a, t.f_begin + f, c, t.g, t.r);  // past the held ones: correct, with stricter waits
+      for (int mb = 0; mb < MB; mb++) {
+        const v4f c = reduce(t.smem, f & 1, mb, t.lane);
+        if (j < HELD) {
+#pragma unroll
+          for (int i = 0; i < HELD; i++)
+            if (i == j) t.held[i][mb] = c;
+        } else {
+          store_c(*t.a, t.f_begin + f, mb, c, t.g, t.r);  // past the held ones: correct, with stricter waits
+        }
       }
     }
   }
@@ -339,65 +358,89 @@ struct Decode {
 
     prologue(t, std::make_integer_sequence<int, (D - 1 > NQ ? D - 1 : NQ)>{});
 #pragma unroll
-    for (int u = 0; u < MPS; u++) t.acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int u = 0; u < MPS; u++) t.acc[mb][u] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // the first fragment (exact wait counts while A is arriving), then the rest
     fragment<true>(t, 0, std::make_integer_sequence<int, NQ>{});
     for (int f = 1; f < t.nf; f++) fragment<false>(t, f, std::make_integer_sequence<int, NQ>{});
 #pragma unroll
-    for (int i = 0; i < kHeld; i++) {
+    for (int i = 0; i < HELD; i++) {
       const int f = t.wave + kDecWaves * i;
-      if (f < t.nf) store_c(a, t.f_begin + f, t.held[i], t.g, t.r);
+      if (f < t.nf) {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) store_c(a, t.f_begin + f, mb, t.held[i][mb], t.g, t.r);
+      }
     }
     wait_vm<0>();  // no copy into LDS may still be in flight when the workgroup ends
   }
 };
 
-template <bool BF4, int KW>
+template <bool BF4, int KW, int MB>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void decode_kernel(DecArgs a) {
-  Decode<BF4, KW>::run(a);
+  Decode<BF4, KW, MB>::run(a);
 }
 
-template <bool BF4, int KW>
+template <bool BF4, int KW, int MB>
 hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   const int grid = a.nfrags < cus ? a.nfrags : cus;
-  hipLaunchKernelGGL((decode_kernel<BF4, KW>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<BF4, KW, MB>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+// row blocks of 16 activations: 1 or 2 for every K, 4 for K <= 4096 (the A
+// operands of all blocks must fit 128 registers per lane)
+template <bool BF4, int KW>
+hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
+  if (a.M <= 16) return launch_dec<BF4, KW, 1>(a, cus, stream);
+  if (a.M <= 32 || KW > 4) return launch_dec<BF4, KW, 2>(a, cus, stream);
+  return launch_dec<BF4, KW, (KW > 4 ? 2 : 4)>(a, cus, stream);
 }
 
 template <bool BF4>
 hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream) {
   switch (a.K) {
-    case 2048: return launch_dec<BF4, 2>(a, cus, stream);
-    case 4096: return launch_dec<BF4, 4>(a, cus, stream);
-    default: return launch_dec<BF4, 8>(a, cus, stream);
+    case 2048: return launch_dec_m<BF4, 2>(a, cus, stream);
+    case 4096: return launch_dec_m<BF4, 4>(a, cus, stream);
+    default: return launch_dec_m<BF4, 8>(a, cus, stream);
   }
 }
 
+// Rows of A one launch covers.  At K = 8192 the A operands of 2 row blocks
+// fill the registers, so 33 .. 64 rows take two launches, each streaming B
+// once (16 x 28672 x 8192 fp8 x fp4: 2 x 26-29 us, against 110-128 us for the
+// split-K kernel).
+int64_t rows_per_launch(int64_t K) { return K == 8192 ? 32 : 64; }
+
 }  // namespace
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB) {
-  return M <= 16 && (fmt == 0 || fmt == 1) && (K == 2048 || K == 4096 || K == 8192) &&
+  return M <= 64 && (fmt == 0 || fmt == 1) && (K == 2048 || K == 4096 || K == 8192) &&
          (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
 }
 
 hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
                             int64_t N, int64_t K, int fmt, hipStream_t stream) {
-  DecArgs a{};
-  a.A = (const uint8_t*)A;
-  a.SA = SA;
-  a.B = (const uint8_t*)B;
-  a.SB = SB;
-  a.C = C;
-  a.M = (int)M;
-  a.N = (int)N;
-  a.K = (int)K;
-  a.nfrags = (int)((N + 15) / 16);
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (cus <= 0) cus = 1;
-  return fmt == 1 ? launch_dec_k<true>(a, cus, stream) : launch_dec_k<false>(a, cus, stream);
+  const int64_t step = rows_per_launch(K);
+  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += step) {
+    DecArgs a{};
+    a.A = (const uint8_t*)A + m0 * K;  // E4M3 activations: one byte per element
+    a.SA = SA + m0 * (K / 32);
+    a.B = (const uint8_t*)B;
+    a.SB = SB;
+    a.C = C + m0 * N;
+    a.M = (int)(M - m0 < step ? M - m0 : step);
+    a.N = (int)N;
+    a.K = (int)K;
+    a.nfrags = (int)((N + 15) / 16);
+    e = fmt == 1 ? launch_dec_k<true>(a, cus, stream) : launch_dec_k<false>(a, cus, stream);
+  }
+  return e;
 }
 
 }  // namespace mxg

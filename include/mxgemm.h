@@ -101,7 +101,9 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  *   fmt        MXG_FMT_FP8_FP8, MXG_FMT_FP8_FP4 or MXG_FMT_FP4_FP4
  * Each 32-element block product is formed by CDNA4's scaled fp8/fp4 MFMA,
  * which applies the E8M0 scales itself; partial sums accumulate in fp32.
- * Small M (M <= 64) takes a split-K streaming kernel for decode shapes.
+ * Decode shapes take weight-streaming kernels: K = 2048, 4096 or 8192
+ * with M <= 64 one that reads B once per launch (two launches for
+ * M > 32 at K = 8192), other small M (M <= 64) a split-K kernel.
  * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the
  * workloads this library is tested on (the MFMA's internal alignment of
  * wide-range products is the dominant error term; see the design notes).

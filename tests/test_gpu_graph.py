@@ -61,6 +61,7 @@ def _mx_operands(name, M, N, K, fmt, seed):
 @pytest.mark.parametrize("name,M,N,K,fmt", [("mxfp8_8192", 4096, 4096, 256, 0),
                                             ("mxfp8_2048", 512, 384, 512, 0),
                                             ("decode_16x28672x8192", 16, 1000, 2048, 1),
+                                            ("decode_16x28672x8192", 48, 1000, 4096, 0),
                                             ("decode_16x28672x8192", 40, 512, 1536, 0)])
 def test_mx_gemm_graph_replay(name, M, N, K, fmt):
     say("graph replay mx", name, M, N, K, fmt)
