@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MXFP8 GEMM TFLOP/s (% of fp8 peak) at 8192³; fp8/fp16 ratio; decode GB/s"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 MFMA
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # Sources each committed counter entry depends on (dispatch + kernel): the
@@ -102,7 +103,9 @@ def time_graph(fn, launches: int, replays: int, warmup: int):
     return e0.elapsed_time(e1) / (replays * launches)
 
 
-def mx_operands(name, dev, elem_b=None):
+def mx_operands(name, dev):
+    """The workload's fp32 sources on the device and their MX codes and
+    scales, in the workload's element formats."""
     import torch
 
     from block_scaled_precision_mxgemm_amd import inputs as mxin
@@ -113,8 +116,9 @@ def mx_operands(name, dev, elem_b=None):
     ta = torch.from_numpy(a32).to(dev)
     tb = torch.from_numpy(b32).to(dev)
     del a32, b32
-    qa, sa = mx.mxgemm_quantize(ta, mx.E4M3)
-    qb, sb = mx.mxgemm_quantize(tb, mx.E2M1 if elem_b == "e2m1" else mx.E4M3)
+    elem = {"e4m3": mx.E4M3, "e2m1": mx.E2M1}
+    qa, sa = mx.mxgemm_quantize(ta, elem[w.elem_a])
+    qb, sb = mx.mxgemm_quantize(tb, elem[w.elem_b])
     torch.cuda.synchronize()
     return w, ta, tb, qa, sa, qb, sb
 
@@ -296,7 +300,15 @@ def main():
         ms4 = time_launches(lambda i=0: mx.mxgemm_run(qa4, sa4, qb4, sb4, 0, out=c4), 20, 5)
         extra["prefill_8192x14336x4096"] = {"ms": ms4, "TFLOP/s": f4 / (ms4 * 1e-3) / 1e12,
                                             "fp8_peak_frac": f4 / (ms4 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
-        del qa4, sa4, qb4, sb4, c4
+        del qa4, sa4, qb4, sb4
+
+        # the same prefill GEMM with both operands MXFP4 (E2M1), against the fp4 roof
+        w5, ta, tb, qa5, sa5, qb5, sb5 = mx_operands("prefill_mxfp4_8192x14336x4096", dev)
+        del ta, tb
+        ms5 = time_launches(lambda i=0: mx.mxgemm_run(qa5, sa5, qb5, sb5, mx.FMT_FP4_FP4, out=c4), 20, 5)
+        extra["prefill_mxfp4_8192x14336x4096"] = {"ms": ms5, "TFLOP/s": f4 / (ms5 * 1e-3) / 1e12,
+                                                  "fp4_peak_frac": f4 / (ms5 * 1e-3) / 1e12 / PEAK_FP4_TFLOPS}
+        del qa5, sa5, qb5, sb5, c4
         torch.cuda.empty_cache()
 
     if args.only in ("all", "decode"):

@@ -14,7 +14,8 @@ operands).  Recipes per workload:
   mxfp8_2048    2048^3, A, B ~ N(0, 1) * 2^u with one u ~ U{-6..6} per
                 (row, 32-element K block), drawn independently for A and B
   prefill       M=8192 x N=14336 x K=4096; A ~ N(0, 1) with each element
-                multiplied by 50 with probability 0.001; B ~ N(0, 0.02) (std)
+                multiplied by 50 with probability 0.001; B ~ N(0, 0.02) (std);
+                the MXFP4 x MXFP4 prefill takes the same sources
   decode        M=16 x N=28672 x K=8192; A ~ N(0, 1) (MXFP8), B ~ N(0, 0.02)
                 (MXFP4, E2M1 codes)
   mxfp8_8192    8192^3, A, B ~ N(0, 1)
@@ -50,6 +51,8 @@ WORKLOADS = {
                  "MXFP8 GEMM 2048^3, N(0,1) x 2^U{-6..6} per 32-K block"),
         Workload("prefill_8192x14336x4096", 8192, 14336, 4096, 4, "e4m3", "e4m3", "prefill",
                  "LLM-prefill MXFP8 GEMM, 8192 tokens x 4096 -> 14336"),
+        Workload("prefill_mxfp4_8192x14336x4096", 8192, 14336, 4096, 4, "e2m1", "e2m1", "prefill",
+                 "LLM-prefill MXFP4 x MXFP4 GEMM (both operands E2M1), same sources"),
         Workload("decode_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "e2m1", "decode",
                  "decode MXFP8 x MXFP4 GEMM, 16 tokens x 8192 -> 28672"),
         Workload("mxfp8_8192", 8192, 8192, 8192, 6, "e4m3", "e4m3", "normal",

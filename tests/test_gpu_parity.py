@@ -168,7 +168,7 @@ def test_mx_gemm_large_tiles_full():
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_mx_gemm_persistent_two_tiles_full(fmt):
     """More 256 x 256 tiles (16 x 17 = 272) than the grid's one workgroup per
     CU, so some workgroups run a second tile after the tile transition (next
