@@ -80,6 +80,14 @@ def _load():
     lib.mxref_fp16_gemm.restype = ci
     lib.mxref_fp16_gemm_points.argtypes = [p, p, i64, i64, i64, ci, p, p, i64, p, p]
     lib.mxref_fp16_gemm_points.restype = ci
+    lib.mxref_gelu.argtypes = [ctypes.c_double]
+    lib.mxref_gelu.restype = ctypes.c_double
+    lib.mxref_round_bf16.argtypes = [ctypes.c_double]
+    lib.mxref_round_bf16.restype = ctypes.c_double
+    lib.mxref_round_f16.argtypes = [ctypes.c_double]
+    lib.mxref_round_f16.restype = ctypes.c_double
+    lib.mxref_epilogue.argtypes = [p, p, i64, p, ci, p]
+    lib.mxref_epilogue.restype = ci
     lib.mxref_num_threads.argtypes = []
     lib.mxref_num_threads.restype = ci
     _lib = lib
@@ -253,3 +261,97 @@ def gate(c_test, c_ref, abs_ref, K, extra_terms=0):
         "inf_mismatch": inf_mismatch,
         "n_exact": n_exact,
     }
+
+
+# --------------------------------------------------------------- epilogue
+# The output step of the fused GEMM: y = act(c + bias[col]) in float64, then
+# the output type.  "Resumo Técnico: RIGEL", section "4. Oportunidades de
+# Otimização" (GEMM fused with bias and GELU).  Reading: GELU(y) = y Phi(y).
+
+OUT_F32, OUT_BF16, OUT_F16 = 0, 1, 2
+ACT_NONE, ACT_GELU = 0, 1
+
+# Largest slope of GELU: d/dy [y Phi(y)] = Phi(y) + y phi(y), maximal at
+# y = sqrt(2): Phi(sqrt 2) + sqrt(2) phi(sqrt 2) = 1.12897...
+GELU_LIPSCHITZ = 1.129
+# Error of the GPU's GELU in units of |y| / 2 (absolute error of its erf):
+# Abramowitz & Stegun 7.1.26 (1.5e-7) plus its fp32 evaluation (reciprocal,
+# five fma / mul, exp, the final 2 - E: at most 8 roundings of values <= 2).
+GELU_ERF_ERR = 1.5e-7 + 8 * 2.0 ** -23
+
+
+def gelu(y):
+    lib = _load()
+    return np.array([lib.mxref_gelu(float(v)) for v in np.ravel(y)], dtype=np.float64).reshape(np.shape(y))
+
+
+def round_out(v, out_type):
+    """float64 values rounded (RNE, overflow to inf) to the output type."""
+    if out_type == OUT_F32:
+        return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+    lib = _load()
+    f = lib.mxref_round_bf16 if out_type == OUT_BF16 else lib.mxref_round_f16
+    return np.array([f(float(x)) for x in np.ravel(v)], dtype=np.float64).reshape(np.shape(v))
+
+
+def epilogue(c, cols, bias, act):
+    """act(c + bias[cols]) in float64 (bias None: no bias)."""
+    c = np.ascontiguousarray(c, dtype=np.float64).ravel()
+    cols = np.ascontiguousarray(cols, dtype=np.int64).ravel()
+    y = np.empty_like(c)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    rc = _load().mxref_epilogue(_ptr(c), _ptr(cols), c.shape[0], None if b is None else _ptr(b), int(act), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle epilogue: bad arguments")
+    return y
+
+
+def _half_ulp(a, out_type):
+    """Half the spacing of the output format at magnitude a (a >= 0)."""
+    P, EMIN = {OUT_F32: (24, -126), OUT_BF16: (8, -126), OUT_F16: (11, -14)}[out_type]
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, EMIN)
+    # one binade up as well, so a value that rounds up across a power of two
+    # is covered
+    return np.ldexp(1.0, (e + 1 - P).astype(np.int64)) * 0.5 * 2.0
+
+
+def epilogue_gate(out_vals, c_ref, abs_ref, K, cols, bias, act, out_type, extra_terms=0):
+    """Gate for the fused output: |out - act(c_ref + bias)| within
+
+      d_c   = (K + extra_terms) 2^-24 sum|a b|   (accumulation, as in gate())
+      d_y   = d_c + 2^-24 |y|                     (the fp32 bias add)
+      d_g   = L d_y + |y|/2 (GELU_ERF_ERR + 2^-22) + 2^-23 |g|   (with GELU;
+              L the largest slope of GELU)
+      + half an ulp of the output type at the value (its final rounding),
+    with |y| and |g| taken as the larger of the reference and the output.
+    NaN positions must match; infinities must match in position and sign.
+    """
+    t = np.asarray(out_vals, dtype=np.float64).ravel()
+    c = np.asarray(c_ref, dtype=np.float64).ravel()
+    ab = np.asarray(abs_ref, dtype=np.float64).ravel()
+    ref = epilogue(c, cols, bias, act)
+    y_ref = c if bias is None else c + np.asarray(bias, dtype=np.float64)[np.asarray(cols).ravel()]
+    nan_t, nan_r = np.isnan(t), np.isnan(ref)
+    nan_mismatch = int(np.count_nonzero(nan_t != nan_r))
+    inf_t, inf_r = np.isinf(t), np.isinf(ref)
+    inf_mismatch = int(np.count_nonzero((inf_t != inf_r) | (inf_t & inf_r & (np.sign(t) != np.sign(ref)))))
+    fin = ~(nan_t | nan_r | inf_t | inf_r)
+    t, ref, c, ab, y_ref = t[fin], ref[fin], c[fin], ab[fin], y_ref[fin]
+    d = (K + extra_terms) * U * ab
+    ymag = np.maximum(np.abs(y_ref), np.abs(t))
+    if bias is not None:
+        d = d + U * ymag
+    if act == ACT_GELU:
+        gmag = np.maximum(np.abs(ref), np.abs(t))
+        d = GELU_LIPSCHITZ * d + 0.5 * ymag * (GELU_ERF_ERR + 2.0 ** -22) + 2.0 ** -23 * gmag
+    tol = d + _half_ulp(np.maximum(np.abs(ref), np.abs(t)), out_type)
+    err = np.abs(t - ref)
+    bad = err > tol
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+    n_bad = int(np.count_nonzero(bad)) + nan_mismatch + inf_mismatch
+    return {"ok": n_bad == 0, "n_bad": n_bad, "n": int(np.size(out_vals)),
+            "max_ratio": float(ratio.max()) if ratio.size else 0.0,
+            "nan_mismatch": nan_mismatch, "inf_mismatch": inf_mismatch}

@@ -373,3 +373,57 @@ int mxref_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------- epilogue */
+
+/* The output step of the fused GEMM (bias, GELU, output type), as the plain
+ * definitions.  Source of the operation: "Resumo Técnico: RIGEL", section
+ * "4. Oportunidades de Otimização" (a GEMM fused with bias and GELU).
+ * Reading: GELU is the Gaussian error linear unit y * Phi(y), Phi the
+ * standard normal distribution function; bias is one value per output
+ * column.  Phi(y) = erfc(-y / sqrt 2) / 2 (the same as (1 + erf(y / sqrt 2))
+ * / 2, without its cancellation for negative y), with the C library's erfc. */
+double mxref_gelu(double y)
+{
+    return 0.5 * y * erfc(-y / sqrt(2.0));
+}
+
+/* Round a double to the nearest value of a binary format with P significant
+ * bits, smallest normal exponent EMIN and largest finite value
+ * (2 - 2^(1-P)) * 2^EMAX, ties to even; beyond the largest finite value
+ * (after rounding) the result is +-infinity, NaN stays NaN. */
+static double round_binary(double v, int P, int EMIN, int EMAX)
+{
+    double a, q, r, fl;
+    int e;
+    if (isnan(v) || isinf(v) || v == 0.0) return v;
+    a = fabs(v);
+    e = ilogb(a);                      /* floor(log2 a), exact */
+    if (e < EMIN) e = EMIN;            /* subnormal range: fixed quantum */
+    q = ldexp(1.0, e - (P - 1));       /* spacing of the format around a */
+    r = a / q;                         /* exact: power-of-two scaling */
+    fl = floor(r);
+    if (r - fl > 0.5 || (r - fl == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    a = fl * q;
+    if (a > ldexp(2.0 - ldexp(1.0, 1 - P), EMAX)) a = INFINITY;
+    return v < 0 ? -a : a;
+}
+
+/* bfloat16: 8 significant bits, exponent range of binary32. */
+double mxref_round_bf16(double v) { return round_binary(v, 8, -126, 127); }
+/* IEEE binary16: 11 significant bits, exponents -14 .. 15. */
+double mxref_round_f16(double v) { return round_binary(v, 11, -14, 15); }
+
+/* y[p] = act(c[p] + bias[col[p]]) for n points (bias may be NULL; act 0 =
+ * none, 1 = GELU), in float64. */
+int mxref_epilogue(const double *c, const int64_t *col, int64_t n, const float *bias, int act, double *y)
+{
+    int64_t p;
+    if (!c || !y || n < 0 || (bias && !col) || (act != 0 && act != 1)) return 1;
+    for (p = 0; p < n; p++) {
+        double v = c[p];
+        if (bias) v += (double)bias[col[p]];
+        y[p] = act ? mxref_gelu(v) : v;
+    }
+    return 0;
+}
