@@ -288,7 +288,8 @@ def gelu(y):
 def round_out(v, out_type):
     """float64 values rounded (RNE, overflow to inf) to the output type."""
     if out_type == OUT_F32:
-        return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+        with np.errstate(over="ignore", invalid="ignore"):
+            return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
     lib = _load()
     f = lib.mxref_round_bf16 if out_type == OUT_BF16 else lib.mxref_round_f16
     return np.array([f(float(x)) for x in np.ravel(v)], dtype=np.float64).reshape(np.shape(v))
@@ -326,17 +327,20 @@ def epilogue_gate(out_vals, c_ref, abs_ref, K, cols, bias, act, out_type, extra_
               L the largest slope of GELU)
       + half an ulp of the output type at the value (its final rounding),
     with |y| and |g| taken as the larger of the reference and the output.
-    NaN positions must match; infinities must match in position and sign.
+    NaN positions must match; infinities must match in position and sign,
+    where the reference's infinities are those of the exact value rounded to
+    the output type (beyond its range it is +-inf).
     """
     t = np.asarray(out_vals, dtype=np.float64).ravel()
     c = np.asarray(c_ref, dtype=np.float64).ravel()
     ab = np.asarray(abs_ref, dtype=np.float64).ravel()
     ref = epilogue(c, cols, bias, act)
     y_ref = c if bias is None else c + np.asarray(bias, dtype=np.float64)[np.asarray(cols).ravel()]
+    ref_r = round_out(ref, out_type)
     nan_t, nan_r = np.isnan(t), np.isnan(ref)
     nan_mismatch = int(np.count_nonzero(nan_t != nan_r))
-    inf_t, inf_r = np.isinf(t), np.isinf(ref)
-    inf_mismatch = int(np.count_nonzero((inf_t != inf_r) | (inf_t & inf_r & (np.sign(t) != np.sign(ref)))))
+    inf_t, inf_r = np.isinf(t), np.isinf(ref_r)
+    inf_mismatch = int(np.count_nonzero((inf_t != inf_r) | (inf_t & inf_r & (np.sign(t) != np.sign(ref_r)))))
     fin = ~(nan_t | nan_r | inf_t | inf_r)
     t, ref, c, ab, y_ref = t[fin], ref[fin], c[fin], ab[fin], y_ref[fin]
     d = (K + extra_terms) * U * ab

@@ -130,3 +130,17 @@ def test_epilogue_gate_controls():
     # a dropped bias is caught
     nob = oracle.round_out(oracle.epilogue(c, cols, None, oracle.ACT_GELU), oracle.OUT_BF16)
     assert not oracle.epilogue_gate(nob, c, ab, 256, cols, bias, oracle.ACT_GELU, oracle.OUT_BF16)["ok"]
+
+
+def test_epilogue_gate_overflow_to_infinity():
+    # 1e30 exceeds fp16: the exact value rounds to +inf, which the output must be
+    c = np.array([1e30, -1e30, 1.0])
+    cols = np.zeros(3, dtype=np.int64)
+    ok = np.array([np.inf, -np.inf, 1.0])
+    assert oracle.epilogue_gate(ok, c, np.zeros(3), 0, cols, None, oracle.ACT_NONE, oracle.OUT_F16)["ok"]
+    bad = np.array([65504.0, -np.inf, 1.0])
+    assert oracle.epilogue_gate(bad, c, np.zeros(3), 0, cols, None, oracle.ACT_NONE, oracle.OUT_F16)["inf_mismatch"] == 1
+    # in bf16 the same values are finite
+    fin = oracle.round_out(c, oracle.OUT_BF16)
+    assert np.isfinite(fin).all()
+    assert oracle.epilogue_gate(fin, c, np.zeros(3), 0, cols, None, oracle.ACT_NONE, oracle.OUT_BF16)["ok"]
