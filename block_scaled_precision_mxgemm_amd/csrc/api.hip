@@ -32,7 +32,7 @@ bool dim_ok(int64_t d) { return d >= 1 && d <= MXG_MAX_DIM; }
 
 int to_status(hipError_t e) { return e == hipSuccess ? MXG_OK : MXG_EHIP; }
 
-int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const float* C, int64_t M,
+int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const void* C, int64_t M,
                 int64_t N, int64_t K, int fmt) {
   if (!A || !SA || !B || !SB || !C) return MXG_EINVAL;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
@@ -40,6 +40,27 @@ int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* 
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXG_EALIGN;
   return MXG_OK;
 }
+
+int validate_epi(const float* bias, int act, int out_type) {
+  if (act != MXG_ACT_NONE && act != MXG_ACT_GELU) return MXG_EINVAL;
+  if (out_type != MXG_OUT_F32 && out_type != MXG_OUT_BF16 && out_type != MXG_OUT_F16) return MXG_EINVAL;
+  if (bias != nullptr && !aligned16(bias)) return MXG_EALIGN;
+  return MXG_OK;
+}
+
+// Kernel choice for an MX product (arguments validated): the weight-streaming
+// decode kernel, the split-K skinny kernel, or the tiled / ping-pong kernels.
+int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
+           int64_t N, int64_t K, int fmt, hipStream_t st) {
+  if (mxg::decode_ok(M, K, fmt, SA, SB)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
+  if (M <= mxg::kSkinnyMaxM && fmt != MXG_FMT_FP4_FP4)
+    return to_status(mxg::launch_mx_skinny(A, SA, B, SB, e, M, N, K, fmt, st));
+  return to_status(mxg::launch_mx_tiled(A, SA, B, SB, e, M, N, K, fmt, st));
+}
+
+static_assert(MXG_OUT_F32 == mxg::kOutF32 && MXG_OUT_BF16 == mxg::kOutBF16 && MXG_OUT_F16 == mxg::kOutF16,
+              "output type ids");
+static_assert(MXG_ACT_NONE == mxg::kActNone && MXG_ACT_GELU == mxg::kActGelu, "activation ids");
 
 }  // namespace
 
@@ -85,12 +106,32 @@ int mxgemm_run(const void* A, const uint8_t* scaleA, const void* B, const uint8_
   if (s != MXG_OK) return s;
   s = check_device();
   if (s != MXG_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  if (mxg::decode_ok(M, K, fmt, scaleA, scaleB))
-    return to_status(mxg::launch_mx_decode(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
-  if (M <= mxg::kSkinnyMaxM && fmt != MXG_FMT_FP4_FP4)
-    return to_status(mxg::launch_mx_skinny(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
-  return to_status(mxg::launch_mx_tiled(A, scaleA, B, scaleB, C, M, N, K, fmt, st));
+  return run_mx(A, scaleA, B, scaleB, mxg::Epi{C, nullptr, mxg::kOutF32, mxg::kActNone}, M, N, K, fmt,
+                (hipStream_t)stream);
+}
+
+int mxgemm_run_fused(const void* A, const uint8_t* scaleA, const void* B, const uint8_t* scaleB, void* C,
+                     int64_t M, int64_t N, int64_t K, int fmt, const float* bias, int act, int out_type,
+                     void* stream) {
+  int s = validate_mx(A, scaleA, B, scaleB, C, M, N, K, fmt);
+  if (s != MXG_OK) return s;
+  s = validate_epi(bias, act, out_type);
+  if (s != MXG_OK) return s;
+  s = check_device();
+  if (s != MXG_OK) return s;
+  return run_mx(A, scaleA, B, scaleB, mxg::Epi{C, bias, out_type, act}, M, N, K, fmt, (hipStream_t)stream);
+}
+
+int mxgemm_epilogue(const float* X, int64_t M, int64_t N, const float* bias, int act, int out_type, void* Y,
+                    void* stream) {
+  if (!X || !Y) return MXG_EINVAL;
+  if (!dim_ok(M) || !dim_ok(N)) return MXG_EINVAL;
+  if (!aligned16(X) || !aligned16(Y)) return MXG_EALIGN;
+  int s = validate_epi(bias, act, out_type);
+  if (s != MXG_OK) return s;
+  s = check_device();
+  if (s != MXG_OK) return s;
+  return to_status(mxg::launch_epilogue(X, M, N, mxg::Epi{Y, bias, out_type, act}, (hipStream_t)stream));
 }
 
 int fp16gemm_run(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K, int b_is_nk,

@@ -60,7 +60,7 @@ struct DecArgs {
   const uint8_t* SA;
   const uint8_t* B;
   const uint8_t* SB;
-  float* C;
+  Epi e;       // output: C (this launch's first row), bias, activation, element type
   int M, N, K;
   int nfrags;  // ceil(N / 16)
 };
@@ -114,16 +114,7 @@ struct Decode {
   static __device__ __forceinline__ void store_c(const DecArgs& a, int frag, int mb, v4f s, int g, int r) {
     const int m = 16 * mb + r;
     const int n = frag * 16 + 4 * g;
-    if (m < a.M) {
-      float* crow = a.C + (int64_t)m * a.N;
-      if ((a.N & 3) == 0 && n + 3 < a.N) {
-        *reinterpret_cast<v4f*>(crow + n) = s;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          if (n + i < a.N) crow[n + i] = s[i];
-      }
-    }
+    if (m < a.M) epi_store4<false>(a.e, a.N, m, n, s, (a.N & 3) == 0 && n + 3 < a.N);
   }
 
   // Per-wave state (all in registers once inlined).
@@ -419,28 +410,29 @@ bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* 
          (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
 }
 
-hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                            int64_t N, int64_t K, int fmt, hipStream_t stream) {
+hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
   if (cus <= 0) cus = 1;
   const int64_t step = rows_per_launch(K);
-  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += step) {
+  for (int64_t m0 = 0; m0 < M && err == hipSuccess; m0 += step) {
     DecArgs a{};
     a.A = (const uint8_t*)A + m0 * K;  // E4M3 activations: one byte per element
     a.SA = SA + m0 * (K / 32);
     a.B = (const uint8_t*)B;
     a.SB = SB;
-    a.C = C + m0 * N;
+    a.e = e;
+    a.e.C = (uint8_t*)e.C + m0 * N * epi_elem_bytes(e.out);
     a.M = (int)(M - m0 < step ? M - m0 : step);
     a.N = (int)N;
     a.K = (int)K;
     a.nfrags = (int)((N + 15) / 16);
-    e = fmt == 1 ? launch_dec_k<true>(a, cus, stream) : launch_dec_k<false>(a, cus, stream);
+    err = fmt == 1 ? launch_dec_k<true>(a, cus, stream) : launch_dec_k<false>(a, cus, stream);
   }
-  return e;
+  return err;
 }
 
 }  // namespace mxg

@@ -28,7 +28,7 @@ struct SkArgs {
   const uint8_t* SA;
   const uint8_t* B;
   const uint8_t* SB;
-  float* C;
+  Epi e;             // output: C, bias, activation, element type
   int M, N, K;
   int64_t lda, ldb;  // row strides in bytes
   int nslices;       // ceil(K / 128)
@@ -148,14 +148,7 @@ struct Skinny {
         for (int w = 0; w < 3; w++) v += red[w][t][j][lane];
         if (m >= a.M) continue;
         const int n = n0 + j * 16 + 4 * g;
-        float* crow = a.C + (int64_t)m * a.N;
-        if ((a.N & 3) == 0 && n + 3 < a.N) {
-          *reinterpret_cast<v4f*>(crow + n) = v;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; i++)
-            if (n + i < a.N) crow[n + i] = v[i];
-        }
+        epi_store4<false>(a.e, a.N, m, n, v, (a.N & 3) == 0 && n + 3 < a.N);
       }
     }
   }
@@ -182,14 +175,14 @@ hipError_t launch_by_m(const SkArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                            int64_t N, int64_t K, int fmt, hipStream_t stream) {
+hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
   SkArgs a{};
   a.A = (const uint8_t*)A;
   a.SA = SA;
   a.B = (const uint8_t*)B;
   a.SB = SB;
-  a.C = C;
+  a.e = e;
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;

@@ -48,6 +48,10 @@ struct Cfg {
   static constexpr int LDS = 2 * STAGE;
   static constexpr int NQA = SZA / 1024, NQB = SZB / 1024;  // 1 KiB wave copies per slice
   static constexpr int NW = WM * WN, NTHR = NW * 64;         // waves, threads per workgroup
+  // bias / activation / 16-bit output in the epilogue: with 64 accumulator
+  // fragments per lane (256 x 256 tiles) that code would not fit beside
+  // them, so the launcher sends such epilogues to the 128 x 128 tiles
+  static constexpr bool EPI_GENERAL = FM * FN <= 16;
   static_assert(NQA % NW == 0 && NQB % NW == 0, "tile copies split evenly over the waves");
   static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
@@ -58,7 +62,7 @@ struct Args {
   const uint8_t* SA;
   const uint8_t* B;
   const uint8_t* SB;
-  float* C;
+  Epi e;                // output: C, bias, activation, element type
   int M, N, K;
   int tiles_m, tiles_n;
   int64_t lda, ldb;     // row strides in bytes of A and B (B: of its K x N rows when BKN)
@@ -368,21 +372,15 @@ struct Kernel {
 
     // ---- epilogue: lane (g, r) holds C[m][n .. n+3] -------------------------
     const bool vec_ok = (a.N & 3) == 0;
+    const Epi e = T::EPI_GENERAL ? a.e : Epi{a.e.C, nullptr, kOutF32, kActNone};
 #pragma unroll
     for (int i = 0; i < T::FM; i++) {
       const int m = m0 + wi * T::TM + i * 16 + r;
       if (m >= a.M) continue;
-      float* crow = a.C + (int64_t)m * a.N;
 #pragma unroll
       for (int j = 0; j < T::FN; j++) {
         const int n = n0 + wj * T::TN + j * 16 + 4 * g;
-        if (vec_ok && n + 3 < a.N) {
-          *reinterpret_cast<v4f*>(crow + n) = acc[i][j];
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; t++)
-            if (n + t < a.N) crow[n + t] = acc[i][j][t];
-        }
+        epi_store4<false>(e, a.N, m, n, acc[i][j], vec_ok && n + 3 < a.N);
       }
     }
   }
@@ -410,14 +408,14 @@ hipError_t launch(const Args& a0, hipStream_t stream) {
   return hipGetLastError();
 }
 
-Args make_args(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M, int64_t N,
-               int64_t K) {
+Args make_args(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e, int64_t M,
+               int64_t N, int64_t K) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = SA;
   a.B = (const uint8_t*)B;
   a.SB = SB;
-  a.C = C;
+  a.e = e;
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
@@ -444,15 +442,19 @@ bool use_big_tiles(int64_t M, int64_t N) {
 
 }  // namespace
 
-hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                           int64_t N, int64_t K, int fmt, hipStream_t stream) {
-  Args a = make_args(A, SA, B, SB, C, M, N, K);
+hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                           int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
+  Args a = make_args(A, SA, B, SB, e, M, N, K);
   const bool af4 = (fmt == 2), bf4 = (fmt != 0);
   a.lda = af4 ? K / 2 : K;
   a.ldb = bf4 ? K / 2 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
-  const bool big = use_big_tiles(M, N);
-  if (big && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, C, M, N, K, fmt, stream);
+  // the 256 x 256 tiled kernels store plain fp32 only (MxBig*::EPI_GENERAL)
+  const bool big_pp = use_big_tiles(M, N);
+  if (big_pp && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, e, M, N, K, fmt, stream);
+  const bool big = big_pp && e.bias == nullptr && e.act == kActNone && e.out == kOutF32;
+  static_assert(!MxBig88::EPI_GENERAL && MxMid88::EPI_GENERAL && MxMid84::EPI_GENERAL && MxMid44::EPI_GENERAL,
+                "general epilogues run on the 128 x 128 tiles");
   if (fmt == 0) return big ? launch<MxBig88, 1>(a, stream) : launch<MxMid88, 2>(a, stream);
   if (fmt == 1) return big ? launch<MxBig84, 1>(a, stream) : launch<MxMid84, 2>(a, stream);
   return big ? launch<MxBig44, 1>(a, stream) : launch<MxMid44, 2>(a, stream);
@@ -460,7 +462,7 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
 
 hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                             int b_is_nk, hipStream_t stream) {
-  Args a = make_args(A, nullptr, B, nullptr, C, M, N, K);
+  Args a = make_args(A, nullptr, B, nullptr, Epi{C, nullptr, kOutF32, kActNone}, M, N, K);
   a.lda = K * 2;
   if (!b_is_nk) {
     a.ldb = N * 2;
@@ -473,7 +475,7 @@ hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int6
 
 hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
                             int64_t N, int64_t K, hipStream_t stream) {
-  Args a = make_args(A, SA, B, SB, C, M, N, K);
+  Args a = make_args(A, SA, B, SB, Epi{C, nullptr, kOutF32, kActNone}, M, N, K);
   a.lda = K;
   a.ldb = K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;

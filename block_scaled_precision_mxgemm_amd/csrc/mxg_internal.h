@@ -5,16 +5,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mxg_epilogue.h"
+
 namespace mxg {
 
 hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S,
                            hipStream_t stream);
 
-// fmt: 0 = fp8 x fp8, 1 = fp8 x fp4, 2 = fp4 x fp4
-hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                           int64_t N, int64_t K, int fmt, hipStream_t stream);
-hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                            int64_t N, int64_t K, int fmt, hipStream_t stream);
+// fmt: 0 = fp8 x fp8, 1 = fp8 x fp4, 2 = fp4 x fp4.  The MX launchers write
+// C through the epilogue `e` (output pointer, bias, activation, output type).
+hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                           int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
 hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                             int b_is_nk, hipStream_t stream);
 hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
@@ -24,17 +27,21 @@ hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, con
 // MX: K % 128 == 0 and 4-byte aligned scale planes; fp16: K % 64 == 0 and an
 // N x K right operand).
 bool pingpong_mx_ok(const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N, int64_t K);
-hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                              int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                              int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
 hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream);
 
-// Decode kernel for M <= 16 (MX fp8 x fp8 or fp8 x fp4): K one of 2048,
+// Decode kernel for M <= 64 (MX fp8 x fp8 or fp8 x fp4): K one of 2048,
 // 4096, 8192 (A's k range per wave is held in registers), 4-byte aligned
 // scale planes.
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB);
-hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
-                            int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
+
+// Stand-alone epilogue: Y = out(act(X + bias)) for an M x N fp32 matrix X,
+// written through `e` (the decomposed form of the fused GEMM epilogue).
+hipError_t launch_epilogue(const float* X, int64_t M, int64_t N, const Epi& e, hipStream_t stream);
 
 // Largest M served by the split-K streaming kernel.
 constexpr int64_t kSkinnyMaxM = 64;

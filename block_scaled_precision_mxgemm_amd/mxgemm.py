@@ -21,6 +21,14 @@ FMT_FP4_FP4 = 2
 
 _FMT_ELEMS = {FMT_FP8_FP8: (E4M3, E4M3), FMT_FP8_FP4: (E4M3, E2M1), FMT_FP4_FP4: (E2M1, E2M1)}
 
+# output types and activations of the fused epilogue (MXG_OUT_*, MXG_ACT_*)
+OUT_F32 = 0
+OUT_BF16 = 1
+OUT_F16 = 2
+ACT_NONE = 0
+ACT_GELU = 1
+_OUT_DTYPES = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_F16: torch.float16}
+
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxgemm.so")
 
 
@@ -48,6 +56,10 @@ def _load():
     lib.mxgemm_run.restype = ci
     lib.mxgemm_run_dequant_fp16.argtypes = [p, p, p, p, p, i64, i64, i64, ci, p]
     lib.mxgemm_run_dequant_fp16.restype = ci
+    lib.mxgemm_run_fused.argtypes = [p, p, p, p, p, i64, i64, i64, ci, p, ci, ci, p]
+    lib.mxgemm_run_fused.restype = ci
+    lib.mxgemm_epilogue.argtypes = [p, i64, i64, p, ci, ci, p, p]
+    lib.mxgemm_epilogue.restype = ci
     lib.fp16gemm_run.argtypes = [p, p, p, i64, i64, i64, ci, p]
     lib.fp16gemm_run.restype = ci
     lib.mxgemm_device_supported.argtypes = []
@@ -112,7 +124,7 @@ def mxgemm_quantize(x: torch.Tensor, elem: int = E4M3, q: torch.Tensor | None = 
     return q, s
 
 
-def _mx_args(a_q, a_s, b_q, b_s, fmt, out):
+def _mx_args(a_q, a_s, b_q, b_s, fmt, out, out_dtype=torch.float32):
     if fmt not in _FMT_ELEMS:
         raise ValueError("unknown fmt %r" % (fmt,))
     ea, eb = _FMT_ELEMS[fmt]
@@ -127,10 +139,18 @@ def _mx_args(a_q, a_s, b_q, b_s, fmt, out):
         raise ValueError("operand shapes disagree: A %s/%s, B %s/%s" %
                          (tuple(a_q.shape), tuple(a_s.shape), tuple(b_q.shape), tuple(b_s.shape)))
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a_q.device)
-    if out.dtype != torch.float32 or out.shape != (M, N) or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous M x N float32 GPU tensor")
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    if out.dtype != out_dtype or out.shape != (M, N) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous M x N %s GPU tensor" % (out_dtype,))
     return a_q, a_s, b_q, b_s, out, M, N, K
+
+
+def _bias_arg(bias, N):
+    if bias is None:
+        return None
+    if bias.dtype != torch.float32 or not bias.is_cuda or bias.shape != (N,) or not bias.is_contiguous():
+        raise ValueError("bias must be a contiguous float32 GPU tensor of N values")
+    return bias
 
 
 def mxgemm_run(a_q, a_s, b_q, b_s, fmt: int = FMT_FP8_FP8, out: torch.Tensor | None = None, stream=None):
@@ -139,6 +159,41 @@ def mxgemm_run(a_q, a_s, b_q, b_s, fmt: int = FMT_FP8_FP8, out: torch.Tensor | N
     rc = _load().mxgemm_run(a_q.data_ptr(), a_s.data_ptr(), b_q.data_ptr(), b_s.data_ptr(), out.data_ptr(),
                             M, N, K, fmt, _stream(stream))
     _check(rc, "mxgemm_run")
+    return out
+
+
+def mxgemm_run_fused(a_q, a_s, b_q, b_s, fmt: int = FMT_FP8_FP8, bias: torch.Tensor | None = None,
+                     act: int = ACT_NONE, out_type: int = OUT_F32, out: torch.Tensor | None = None, stream=None):
+    """mxgemm_run with the output step fused into the GEMM: C = out_type(act(A B^T + bias)).
+    bias: N float32 values or None; act: ACT_NONE / ACT_GELU; out_type: OUT_F32 /
+    OUT_BF16 / OUT_F16 (the output tensor's dtype float32 / bfloat16 / float16)."""
+    if out_type not in _OUT_DTYPES:
+        raise ValueError("unknown out_type %r" % (out_type,))
+    a_q, a_s, b_q, b_s, out, M, N, K = _mx_args(a_q, a_s, b_q, b_s, fmt, out, _OUT_DTYPES[out_type])
+    bias = _bias_arg(bias, N)
+    rc = _load().mxgemm_run_fused(a_q.data_ptr(), a_s.data_ptr(), b_q.data_ptr(), b_s.data_ptr(), out.data_ptr(),
+                                  M, N, K, fmt, None if bias is None else bias.data_ptr(), act, out_type,
+                                  _stream(stream))
+    _check(rc, "mxgemm_run_fused")
+    return out
+
+
+def mxgemm_epilogue(x: torch.Tensor, bias: torch.Tensor | None = None, act: int = ACT_NONE,
+                    out_type: int = OUT_F32, out: torch.Tensor | None = None, stream=None):
+    """The same output step as a separate pass over an fp32 M x N matrix x."""
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D float32 GPU tensor")
+    if out_type not in _OUT_DTYPES:
+        raise ValueError("unknown out_type %r" % (out_type,))
+    M, N = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=_OUT_DTYPES[out_type], device=x.device)
+    if out.dtype != _OUT_DTYPES[out_type] or out.shape != (M, N) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous M x N %s GPU tensor" % (_OUT_DTYPES[out_type],))
+    bias = _bias_arg(bias, N)
+    rc = _load().mxgemm_epilogue(x.data_ptr(), M, N, None if bias is None else bias.data_ptr(), act, out_type,
+                                 out.data_ptr(), _stream(stream))
+    _check(rc, "mxgemm_epilogue")
     return out
 
 

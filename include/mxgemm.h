@@ -64,6 +64,13 @@ extern "C" {
 /* Largest accepted M, N (rows) and K. */
 #define MXG_MAX_DIM (1 << 20)
 
+/* Output element types and activations of mxgemm_run_fused / mxgemm_epilogue. */
+#define MXG_OUT_F32 0    /* fp32 */
+#define MXG_OUT_BF16 1   /* bfloat16 bits, uint16 per element */
+#define MXG_OUT_F16 2    /* IEEE binary16 bits, uint16 per element */
+#define MXG_ACT_NONE 0
+#define MXG_ACT_GELU 1   /* GELU(y) = y * Phi(y), Phi the standard normal CDF */
+
 /*
  * mxgemm_quantize - fp32 rows -> block-scaled codes plus UE8M0 scales.
  *
@@ -112,6 +119,52 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
 int mxgemm_run(const void *A, const uint8_t *scaleA,
                const void *B, const uint8_t *scaleB,
                float *C, int64_t M, int64_t N, int64_t K, int fmt, void *stream);
+
+/*
+ * mxgemm_run_fused - mxgemm_run with the output step fused into the GEMM's
+ * epilogue: for every element, in fp32 with round-to-nearest-even,
+ *   y = acc[i][j] + bias[j]        (when bias != NULL)
+ *   y = GELU(y)                    (when act == MXG_ACT_GELU)
+ *   C[i][j] = y in the type out_type (RNE; overflow -> +-inf; NaN stays NaN)
+ * where acc is exactly what mxgemm_run writes for the same operands.  C then
+ * makes a single trip to memory, at 2 bytes per element for bf16 / fp16:
+ * the fused GEMM + bias + GELU kernel of "Resumo Técnico: RIGEL", section
+ * "4. Oportunidades de Otimização".  GELU is evaluated as y/2 * (1 + erf(y /
+ * sqrt 2)) with erf from Abramowitz & Stegun formula 7.1.26 (absolute error
+ * <= 1.5e-7); GELU(-inf) is NaN.
+ *
+ *   A, scaleA, B, scaleB, M, N, K, fmt  as for mxgemm_run
+ *   C         device, M x N row-major elements of out_type, 16-byte aligned;
+ *             overwritten
+ *   bias      device, N fp32 values, 16-byte aligned (read only), or NULL
+ *   act       MXG_ACT_NONE or MXG_ACT_GELU
+ *   out_type  MXG_OUT_F32, MXG_OUT_BF16 or MXG_OUT_F16
+ * With bias == NULL, act == MXG_ACT_NONE and out_type == MXG_OUT_F32 the
+ * result is bit-identical to mxgemm_run.  The result equals, bit for bit,
+ * mxgemm_run followed by mxgemm_epilogue with the same bias / act / out_type.
+ * Returns MXG_OK or an error status (MXG_EINVAL for an unknown act or
+ * out_type, MXG_EALIGN for a misaligned C or bias).  Deterministic.
+ */
+int mxgemm_run_fused(const void *A, const uint8_t *scaleA,
+                     const void *B, const uint8_t *scaleB,
+                     void *C, int64_t M, int64_t N, int64_t K, int fmt,
+                     const float *bias, int act, int out_type, void *stream);
+
+/*
+ * mxgemm_epilogue - the same output step as a separate pass over an fp32
+ * matrix: Y[i][j] = out_type(act(X[i][j] + bias[j])), with the arithmetic
+ * of mxgemm_run_fused.  The decomposed path the fused kernel is compared
+ * with; also usable on any fp32 GEMM result.
+ *
+ *   X         device, M x N fp32 row-major, 16-byte aligned (read only)
+ *   M, N      >= 1
+ *   bias, act, out_type  as for mxgemm_run_fused
+ *   Y         device, M x N elements of out_type, 16-byte aligned; may not
+ *             overlap X unless Y == X and out_type == MXG_OUT_F32
+ * Returns MXG_OK or an error status.  Deterministic.
+ */
+int mxgemm_epilogue(const float *X, int64_t M, int64_t N, const float *bias,
+                    int act, int out_type, void *Y, void *stream);
 
 /*
  * fp16gemm_run - dense fp16 comparison GEMM, fp32 accumulate and output.

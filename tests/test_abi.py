@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["mxgemm_quantize", "mxgemm_run", "fp16gemm_run", "mxgemm_run_dequant_fp16",
-                                  "mxgemm_device_supported", "mxgemm_status_string"])
+                                  "mxgemm_run_fused", "mxgemm_epilogue", "mxgemm_device_supported",
+                                  "mxgemm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -73,6 +74,25 @@ def test_validation_codes(lib):
     d.restype = ctypes.c_int
     d.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p]
     assert d(*ok, 16, 16, 64, 1, None) == 1                                 # ablation is fp8 x fp8 only
+    fu = lib.mxgemm_run_fused
+    fu.restype = ctypes.c_int
+    fu.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_void_p]
+    assert fu(*ok, 16, 16, 64, 0, None, 2, 0, None) == 1                    # unknown activation
+    assert fu(*ok, 16, 16, 64, 0, None, 0, 3, None) == 1                    # unknown output type
+    assert fu(*ok, 16, 16, 64, 0, 0x1004, 1, 1, None) == 2                  # misaligned bias
+    assert fu(A, A, A, A, 0x1008, 16, 16, 64, 0, None, 0, 1, None) == 2     # misaligned C
+    assert fu(*ok, 16, 16, 48, 0, None, 0, 1, None) == 1                    # K % 32 != 0
+    ep = lib.mxgemm_epilogue
+    ep.restype = ctypes.c_int
+    ep.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    assert ep(None, 4, 4, None, 0, 0, A, None) == 1                         # null X
+    assert ep(A, 0, 4, None, 0, 0, A, None) == 1                            # M = 0
+    assert ep(A, 4, 4, None, 5, 0, A, None) == 1                            # unknown activation
+    assert ep(A, 4, 4, None, 0, 9, A, None) == 1                            # unknown output type
+    assert ep(A, 4, 4, 0x1002, 1, 1, A, None) == 2                          # misaligned bias
+    assert ep(A, 4, 4, None, 0, 1, 0x1002, None) == 2                       # misaligned Y
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
