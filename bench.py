@@ -236,6 +236,14 @@ def main():
         del ta16, tb16
 
     if args.only == "all":
+        # the same product with a bf16 C (the fused epilogue's 16-bit output):
+        # what the fp32 C write costs at this size
+        c16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        bms = time_launches(lambda i=0: mx.mxgemm_run_fused(qa, sa, qb, sb, mx.FMT_FP8_FP8, out_type=mx.OUT_BF16,
+                                                            out=c16), 20, 5)
+        extra["mxfp8_8192_bf16_out"] = {"ms": bms, "TFLOP/s": flops / (bms * 1e-3) / 1e12,
+                                        "fp8_peak_frac": flops / (bms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        del c16
         # dequantize-to-fp16 ablation on the headline operands
         dms = time_launches(lambda i=0: mx.mxgemm_run_dequant_fp16(qa, sa, qb, sb, mx.FMT_FP8_FP8, out=c), 5, 2)
         extra["ablation_dequant_fp16_8192"] = {"ms": dms, "TFLOP/s": flops / (dms * 1e-3) / 1e12,
@@ -300,7 +308,24 @@ def main():
         ms4 = time_launches(lambda i=0: mx.mxgemm_run(qa4, sa4, qb4, sb4, 0, out=c4), 20, 5)
         extra["prefill_8192x14336x4096"] = {"ms": ms4, "TFLOP/s": f4 / (ms4 * 1e-3) / 1e12,
                                             "fp8_peak_frac": f4 / (ms4 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
-        del qa4, sa4, qb4, sb4
+        # fused epilogue (bias + GELU, bf16 C written once) against the
+        # decomposed path (fp32 C, then a separate bias + GELU + bf16 pass)
+        bias4 = torch.from_numpy(np.random.default_rng(44).standard_normal(w4.N).astype(np.float32)).to(dev)
+        c16 = torch.empty((w4.M, w4.N), dtype=torch.bfloat16, device=dev)
+        fz = lambda i=0: mx.mxgemm_run_fused(qa4, sa4, qb4, sb4, 0, bias=bias4, act=mx.ACT_GELU,
+                                             out_type=mx.OUT_BF16, out=c16)
+        fz_ms = time_launches(fz, 20, 5)
+        ep = lambda i=0: mx.mxgemm_epilogue(c4, bias4, mx.ACT_GELU, mx.OUT_BF16, out=c16)
+        ep_ms = time_launches(ep, 20, 5)
+        dz = lambda i=0: (mx.mxgemm_run(qa4, sa4, qb4, sb4, 0, out=c4), ep())
+        dz_ms = time_launches(dz, 20, 5)
+        ep_bytes = w4.M * w4.N * (4 + 2) + w4.N * 4
+        extra["prefill_fused_bias_gelu_bf16"] = {
+            "ms": fz_ms, "TFLOP/s": f4 / (fz_ms * 1e-3) / 1e12,
+            "decomposed_ms": dz_ms, "fused_speedup": dz_ms / fz_ms,
+            "epilogue_pass_ms": ep_ms, "epilogue_pass_GB/s": ep_bytes / (ep_ms * 1e-3) / 1e9,
+            "note": "C = bf16(GELU(A B^T + bias)); decomposed = fp32 GEMM + separate epilogue pass"}
+        del qa4, sa4, qb4, sb4, c16
 
         # the same prefill GEMM with both operands MXFP4 (E2M1), against the fp4 roof
         w5, ta, tb, qa5, sa5, qb5, sb5 = mx_operands("prefill_mxfp4_8192x14336x4096", dev)
