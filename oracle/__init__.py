@@ -32,6 +32,7 @@ import subprocess
 import numpy as np
 
 E4M3 = 0
+E5M2 = 1
 E2M1 = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +65,8 @@ def _load():
     ci = ctypes.c_int
     lib.mxref_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.mxref_e4m3_value.restype = ctypes.c_double
+    lib.mxref_e5m2_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_e5m2_value.restype = ctypes.c_double
     lib.mxref_e2m1_value.argtypes = [ctypes.c_uint8]
     lib.mxref_e2m1_value.restype = ctypes.c_double
     lib.mxref_ue8m0_value.argtypes = [ctypes.c_uint8]
@@ -111,6 +114,13 @@ def e4m3_table() -> np.ndarray:
     return np.array([lib.mxref_e4m3_value(c) for c in range(256)], dtype=np.float64)
 
 
+def e5m2_table() -> np.ndarray:
+    """float64[256]: value of every E5M2 code (+-inf for 0x7C / 0xFC, NaN for
+    exponent field 31 with a nonzero mantissa)."""
+    lib = _load()
+    return np.array([lib.mxref_e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+
 def e2m1_table() -> np.ndarray:
     """float64[16]: value of every E2M1 nibble."""
     lib = _load()
@@ -128,8 +138,8 @@ def fp16_value(bits: int) -> float:
 
 
 def row_bytes(K: int, elem: int) -> int:
-    """Bytes per operand row: K for E4M3, K/2 for packed E2M1."""
-    return K if elem == E4M3 else K // 2
+    """Bytes per operand row: K for E4M3 and E5M2, K/2 for packed E2M1."""
+    return K // 2 if elem == E2M1 else K
 
 
 # --------------------------------------------------------------- quantize
@@ -137,7 +147,7 @@ def row_bytes(K: int, elem: int) -> int:
 def quantize(x: np.ndarray, elem: int):
     """Quantize fp32 rows (K contiguous) to (codes uint8, scales uint8).
 
-    codes: rows x K (E4M3) or rows x K/2 (E2M1, even k in the low nibble);
+    codes: rows x K (E4M3, E5M2) or rows x K/2 (E2M1, even k in the low nibble);
     scales: rows x K/32 UE8M0 bytes.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -146,7 +156,7 @@ def quantize(x: np.ndarray, elem: int):
     s = np.zeros((rows, K // 32), dtype=np.uint8)
     rc = _load().mxref_quantize(_ptr(x), rows, K, elem, _ptr(q), _ptr(s))
     if rc != 0:
-        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E2M1)")
+        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E5M2/E2M1)")
     return q, s
 
 

@@ -15,12 +15,15 @@ import oracle
 from conftest import read_golden_kv, read_golden_rows
 
 E4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+E5 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
 E2 = np.array([float(v) for _, v in read_golden_rows("e2m1_values.txt")])
 
 
 def _decode(q, elem, K):
     if elem == oracle.E4M3:
         return E4[q]
+    if elem == oracle.E5M2:
+        return E5[q]
     return E2[np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[0], K)]
 
 
@@ -29,6 +32,10 @@ def _rand_operand(rng, rows, K, elem, lo=110, hi=140, finite=True):
         q = rng.integers(0, 256, size=(rows, K), dtype=np.uint8)
         if finite:
             q[(q & 0x7F) == 0x7F] = 0x7E
+    elif elem == oracle.E5M2:
+        q = rng.integers(0, 256, size=(rows, K), dtype=np.uint8)
+        if finite:
+            q[(q & 0x7C) == 0x7C] &= 0xFB   # exponent field 31 (inf / NaN) -> 30
     else:
         q = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
     s = rng.integers(lo, hi, size=(rows, K // 32), dtype=np.uint8)
@@ -60,6 +67,9 @@ def _exact(aq, as_, ea, bq, bs, eb, M, N, K):
     (oracle.E4M3, oracle.E4M3, 3, 5, 96, 2),
     (oracle.E4M3, oracle.E2M1, 4, 4, 64, 3),
     (oracle.E2M1, oracle.E2M1, 2, 3, 64, 4),
+    (oracle.E5M2, oracle.E5M2, 3, 4, 64, 5),
+    (oracle.E4M3, oracle.E5M2, 4, 3, 32, 6),
+    (oracle.E5M2, oracle.E4M3, 2, 4, 96, 7),
 ])
 def test_bruteforce_exact_rationals(ea, eb, M, N, K, seed):
     rng = np.random.default_rng(seed)
