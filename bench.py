@@ -116,7 +116,7 @@ def mx_operands(name, dev):
     ta = torch.from_numpy(a32).to(dev)
     tb = torch.from_numpy(b32).to(dev)
     del a32, b32
-    elem = {"e4m3": mx.E4M3, "e2m1": mx.E2M1}
+    elem = {"e4m3": mx.E4M3, "e5m2": mx.E5M2, "e2m1": mx.E2M1}
     qa, sa = mx.mxgemm_quantize(ta, elem[w.elem_a])
     qb, sb = mx.mxgemm_quantize(tb, elem[w.elem_b])
     torch.cuda.synchronize()
@@ -217,6 +217,14 @@ def main():
         qbytes = M * K * (4 + 1 + 1 / 32)
         extra["quantize_8192x8192_e4m3"] = {"ms": qms, "GB/s": qbytes / (qms * 1e-3) / 1e9,
                                             "hbm_frac": qbytes / (qms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    if args.only == "all":
+        # E4M3 activations x E5M2 weights on the same sources (the E5M2 operand
+        # format of the scaled MFMA)
+        qb5, sb5 = mx.mxgemm_quantize(tb, mx.E5M2)
+        ms45 = time_launches(lambda i=0: mx.mxgemm_run(qa, sa, qb5, sb5, mx.FMT_FP8_BF8, out=c), 20, 5)
+        extra["mxfp8xbf8_8192"] = {"ms": ms45, "TFLOP/s": flops / (ms45 * 1e-3) / 1e12,
+                                   "fp8_peak_frac": flops / (ms45 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        del qb5, sb5
     del ta, tb
 
     if args.only in ("all", "fp16"):

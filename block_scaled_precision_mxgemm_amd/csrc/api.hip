@@ -36,7 +36,7 @@ int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* 
                 int64_t N, int64_t K, int fmt) {
   if (!A || !SA || !B || !SB || !C) return MXG_EINVAL;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
-  if (fmt != MXG_FMT_FP8_FP8 && fmt != MXG_FMT_FP8_FP4 && fmt != MXG_FMT_FP4_FP4) return MXG_EINVAL;
+  if (fmt < MXG_FMT_FP8_FP8 || fmt > MXG_FMT_BF8_FP8) return MXG_EINVAL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXG_EALIGN;
   return MXG_OK;
 }
@@ -49,11 +49,12 @@ int validate_epi(const float* bias, int act, int out_type) {
 }
 
 // Kernel choice for an MX product (arguments validated): the weight-streaming
-// decode kernel, the split-K skinny kernel, or the tiled / ping-pong kernels.
+// decode kernel, the split-K skinny kernel (both for E4M3 activations against
+// E4M3 or E2M1 weights), or the tiled / ping-pong kernels (every format pair).
 int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
            int64_t N, int64_t K, int fmt, hipStream_t st) {
   if (mxg::decode_ok(M, K, fmt, SA, SB)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
-  if (M <= mxg::kSkinnyMaxM && fmt != MXG_FMT_FP4_FP4)
+  if (M <= mxg::kSkinnyMaxM && (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4))
     return to_status(mxg::launch_mx_skinny(A, SA, B, SB, e, M, N, K, fmt, st));
   return to_status(mxg::launch_mx_tiled(A, SA, B, SB, e, M, N, K, fmt, st));
 }
@@ -61,6 +62,8 @@ int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, c
 static_assert(MXG_OUT_F32 == mxg::kOutF32 && MXG_OUT_BF16 == mxg::kOutBF16 && MXG_OUT_F16 == mxg::kOutF16,
               "output type ids");
 static_assert(MXG_ACT_NONE == mxg::kActNone && MXG_ACT_GELU == mxg::kActGelu, "activation ids");
+static_assert(MXG_ELEM_E4M3 == mxg::kFmtFp8 && MXG_ELEM_E5M2 == mxg::kFmtBf8 && MXG_ELEM_E2M1 == mxg::kFmtFp4,
+              "element ids are the MFMA format ids");
 
 }  // namespace
 
@@ -93,7 +96,7 @@ int mxgemm_device_supported(void) {
 int mxgemm_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S, void* stream) {
   if (!X || !Q || !S) return MXG_EINVAL;
   if (!dim_ok(rows) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
-  if (elem != MXG_ELEM_E4M3 && elem != MXG_ELEM_E2M1) return MXG_EINVAL;
+  if (elem != MXG_ELEM_E4M3 && elem != MXG_ELEM_E5M2 && elem != MXG_ELEM_E2M1) return MXG_EINVAL;
   if (!aligned16(X) || !aligned16(Q)) return MXG_EALIGN;
   const int d = check_device();
   if (d != MXG_OK) return d;

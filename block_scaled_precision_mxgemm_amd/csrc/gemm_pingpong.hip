@@ -49,8 +49,11 @@ namespace {
 
 enum PPKind { kPPMX = 0, kPPF16 = 1 };
 
-template <int KIND, bool AF4, bool BF4>
+// FA_, FB_: MFMA format ids of A and B (kFmtFp8 E4M3, kFmtBf8 E5M2, kFmtFp4 E2M1)
+template <int KIND, int FA_, int FB_>
 struct PPCfg {
+  static constexpr int FA = FA_, FB = FB_;
+  static constexpr bool AF4 = FA == kFmtFp4, BF4 = FB == kFmtFp4;
   static constexpr bool SCALED = (KIND == kPPMX);
   static constexpr bool A_FP4 = AF4, B_FP4 = BF4;
   static constexpr int RA = AF4 ? 64 : 128;   // bytes per A row per slice
@@ -163,7 +166,7 @@ struct PPKernel {
   template <int... I>
   static __device__ __forceinline__ void compute_scaled(v4f (&acc)[8][4], const v8i (&af)[8], const v8i (&bf)[4],
                                                         const int (&sa)[2], int sb, std::integer_sequence<int, I...>) {
-    constexpr int FB = T::B_FP4 ? kFmtFp4 : kFmtFp8, FA = T::A_FP4 ? kFmtFp4 : kFmtFp8;
+    constexpr int FB = T::FB, FA = T::FA;
     (mfma_scaled_acc_pk<FB, FA, I / 8, (I % 8) & 3>(acc[I % 8][I / 8], bf[I / 8], af[I % 8], sb, sa[(I % 8) >> 2]),
      ...);
   }
@@ -425,10 +428,15 @@ hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, c
   a.N = (int)N;
   a.K = (int)K;
   a.lda = (fmt == 2) ? K / 2 : K;
-  a.ldb = (fmt == 0) ? K : K / 2;
-  if (fmt == 0) return launch_pp<PPCfg<kPPMX, false, false>>(a, 128, stream);
-  if (fmt == 1) return launch_pp<PPCfg<kPPMX, false, true>>(a, 128, stream);
-  return launch_pp<PPCfg<kPPMX, true, true>>(a, 128, stream);
+  a.ldb = (fmt == 1 || fmt == 2) ? K / 2 : K;
+  switch (fmt) {
+    case 0: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtFp8>>(a, 128, stream);
+    case 1: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtFp4>>(a, 128, stream);
+    case 2: return launch_pp<PPCfg<kPPMX, kFmtFp4, kFmtFp4>>(a, 128, stream);
+    case 3: return launch_pp<PPCfg<kPPMX, kFmtBf8, kFmtBf8>>(a, 128, stream);
+    case 4: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtBf8>>(a, 128, stream);
+    default: return launch_pp<PPCfg<kPPMX, kFmtBf8, kFmtFp8>>(a, 128, stream);
+  }
 }
 
 hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
@@ -442,7 +450,7 @@ hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, i
   a.K = (int)K;
   a.lda = K * 2;
   a.ldb = K * 2;
-  return launch_pp<PPCfg<kPPF16, false, false>>(a, 64, stream);
+  return launch_pp<PPCfg<kPPF16, kFmtFp8, kFmtFp8>>(a, 64, stream);
 }
 
 }  // namespace mxg

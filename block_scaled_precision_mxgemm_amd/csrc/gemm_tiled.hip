@@ -31,11 +31,14 @@ namespace {
 
 enum Kind { kMX = 0, kF16 = 1, kDEQ = 2 };
 
-template <int KIND, int BM_, int BN_, int WM_, int WN_, bool AF4_, bool BF4_, bool BKN_>
+// FA_, FB_: MFMA format ids of the MX operands (kFmtFp8 E4M3, kFmtBf8 E5M2,
+// kFmtFp4 E2M1); unused by the fp16 kinds
+template <int KIND, int BM_, int BN_, int WM_, int WN_, int FA_, int FB_, bool BKN_>
 struct Cfg {
   static constexpr int KIND_ = KIND;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr bool AF4 = AF4_, BF4 = BF4_, BKN = BKN_;
+  static constexpr int FA = FA_, FB = FB_;
+  static constexpr bool AF4 = FA == kFmtFp4, BF4 = FB == kFmtFp4, BKN = BKN_;
   static constexpr bool SCALED = (KIND != kF16);
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
   static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
@@ -326,7 +329,7 @@ struct Kernel {
           }
 #pragma unroll
           for (int i = 0; i < T::FM; i++)
-            mfma_scaled_acc<T::BF4 ? kFmtFp4 : kFmtFp8, T::AF4 ? kFmtFp4 : kFmtFp8>(acc[i][j], bcur, af[i], sbcur,
+            mfma_scaled_acc<T::FB, T::FA>(acc[i][j], bcur, af[i], sbcur,
                                                                                     sa[i]);
           bcur = bnext;
           sbcur = sbnext;
@@ -424,16 +427,23 @@ Args make_args(const void* A, const uint8_t* SA, const void* B, const uint8_t* S
 
 // Configurations: 256 x 256 tiles (one workgroup per CU, 128 x 128 per wave)
 // for large outputs, 128 x 128 (two workgroups per CU) otherwise.
-using MxBig88 = Cfg<kMX, 256, 256, 2, 2, false, false, false>;
-using MxBig84 = Cfg<kMX, 256, 256, 2, 2, false, true, false>;
-using MxBig44 = Cfg<kMX, 256, 256, 2, 2, true, true, false>;
-using MxMid88 = Cfg<kMX, 128, 128, 2, 2, false, false, false>;
-using MxMid84 = Cfg<kMX, 128, 128, 2, 2, false, true, false>;
-using MxMid44 = Cfg<kMX, 128, 128, 2, 2, true, true, false>;
-using F16Big = Cfg<kF16, 256, 256, 2, 2, false, false, false>;
-using F16Mid = Cfg<kF16, 128, 128, 2, 2, false, false, false>;
-using F16MidKN = Cfg<kF16, 128, 128, 2, 2, false, false, true>;
-using DeqMid = Cfg<kDEQ, 128, 128, 2, 2, false, false, false>;
+template <int FA, int FB>
+using MxBig = Cfg<kMX, 256, 256, 2, 2, FA, FB, false>;
+template <int FA, int FB>
+using MxMid = Cfg<kMX, 128, 128, 2, 2, FA, FB, false>;
+using MxBig88 = MxBig<kFmtFp8, kFmtFp8>;
+using MxMid88 = MxMid<kFmtFp8, kFmtFp8>;
+using MxMid84 = MxMid<kFmtFp8, kFmtFp4>;
+using MxMid44 = MxMid<kFmtFp4, kFmtFp4>;
+using F16Big = Cfg<kF16, 256, 256, 2, 2, kFmtFp8, kFmtFp8, false>;
+using F16Mid = Cfg<kF16, 128, 128, 2, 2, kFmtFp8, kFmtFp8, false>;
+using F16MidKN = Cfg<kF16, 128, 128, 2, 2, kFmtFp8, kFmtFp8, true>;
+using DeqMid = Cfg<kDEQ, 128, 128, 2, 2, kFmtFp8, kFmtFp8, false>;
+
+template <int FA, int FB>
+hipError_t launch_mx_fmt(const Args& a, bool big, hipStream_t stream) {
+  return big ? launch<MxBig<FA, FB>, 1>(a, stream) : launch<MxMid<FA, FB>, 2>(a, stream);
+}
 
 bool use_big_tiles(int64_t M, int64_t N) {
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -445,7 +455,7 @@ bool use_big_tiles(int64_t M, int64_t N) {
 hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
   Args a = make_args(A, SA, B, SB, e, M, N, K);
-  const bool af4 = (fmt == 2), bf4 = (fmt != 0);
+  const bool af4 = (fmt == 2), bf4 = (fmt == 1 || fmt == 2);
   a.lda = af4 ? K / 2 : K;
   a.ldb = bf4 ? K / 2 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
@@ -455,9 +465,14 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
   const bool big = big_pp && e.bias == nullptr && e.act == kActNone && e.out == kOutF32;
   static_assert(!MxBig88::EPI_GENERAL && MxMid88::EPI_GENERAL && MxMid84::EPI_GENERAL && MxMid44::EPI_GENERAL,
                 "general epilogues run on the 128 x 128 tiles");
-  if (fmt == 0) return big ? launch<MxBig88, 1>(a, stream) : launch<MxMid88, 2>(a, stream);
-  if (fmt == 1) return big ? launch<MxBig84, 1>(a, stream) : launch<MxMid84, 2>(a, stream);
-  return big ? launch<MxBig44, 1>(a, stream) : launch<MxMid44, 2>(a, stream);
+  switch (fmt) {
+    case 0: return launch_mx_fmt<kFmtFp8, kFmtFp8>(a, big, stream);
+    case 1: return launch_mx_fmt<kFmtFp8, kFmtFp4>(a, big, stream);
+    case 2: return launch_mx_fmt<kFmtFp4, kFmtFp4>(a, big, stream);
+    case 3: return launch_mx_fmt<kFmtBf8, kFmtBf8>(a, big, stream);
+    case 4: return launch_mx_fmt<kFmtFp8, kFmtBf8>(a, big, stream);
+    default: return launch_mx_fmt<kFmtBf8, kFmtFp8>(a, big, stream);
+  }
 }
 
 hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,

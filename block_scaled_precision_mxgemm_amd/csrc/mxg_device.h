@@ -29,8 +29,9 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// MFMA operand-format ids (cbsz / blgp fields).
+// MFMA operand-format ids (cbsz / blgp fields): E4M3, E5M2, E2M1.
 constexpr int kFmtFp8 = 0;
+constexpr int kFmtBf8 = 1;
 constexpr int kFmtFp4 = 4;
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row.  Fragment reads
@@ -91,6 +92,10 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& c, const v8i& a, const v8i&
   if constexpr (FA == kFmtFp8 && FB == kFmtFp8) {
     asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
         : "+a"(c) : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+  } else if constexpr (FA != kFmtFp4 && FB != kFmtFp4) {
+    // 8-register operands with an E5M2 side: the format ids go in cbsz / blgp
+    asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:%5 blgp:%6"
+        : "+a"(c) : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b), "i"(FA), "i"(FB));
   } else if constexpr (FA == kFmtFp4 && FB == kFmtFp8) {
     const v4i a4 = {a[0], a[1], a[2], a[3]};
     asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4"
@@ -100,6 +105,7 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& c, const v8i& a, const v8i&
     asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] blgp:4"
         : "+a"(c) : "v"(a), "v"(b4), "v"(scale_a), "v"(scale_b));
   } else {
+    static_assert(FA == kFmtFp4 && FB == kFmtFp4, "fp4 pairs only with E4M3 or E2M1");
     const v4i a4 = {a[0], a[1], a[2], a[3]};
     const v4i b4 = {b[0], b[1], b[2], b[3]};
     asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
@@ -119,6 +125,13 @@ __device__ __forceinline__ void mfma_scaled_acc_pk(v4f& c, const v8i& a, const v
     asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
                  : "+a"(c)
                  : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1));
+  } else if constexpr (FA != kFmtFp4 && FB != kFmtFp4) {
+    asm volatile(
+        "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] cbsz:%9 "
+        "blgp:%10"
+        : "+a"(c)
+        : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1), "i"(FA),
+          "i"(FB));
   } else if constexpr (FA == kFmtFp4 && FB == kFmtFp8) {
     const v4i a4 = {a[0], a[1], a[2], a[3]};
     asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] cbsz:4"
@@ -130,6 +143,7 @@ __device__ __forceinline__ void mfma_scaled_acc_pk(v4f& c, const v8i& a, const v
                  : "+a"(c)
                  : "v"(a), "v"(b4), "v"(scale_a), "v"(scale_b), "i"(BA & 1), "i"(BB & 1), "i"(BA >> 1), "i"(BB >> 1));
   } else {
+    static_assert(FA == kFmtFp4 && FB == kFmtFp4, "fp4 pairs only with E4M3 or E2M1");
     const v4i a4 = {a[0], a[1], a[2], a[3]};
     const v4i b4 = {b[0], b[1], b[2], b[3]};
     asm volatile(

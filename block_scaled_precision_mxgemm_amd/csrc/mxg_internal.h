@@ -12,7 +12,8 @@ namespace mxg {
 hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S,
                            hipStream_t stream);
 
-// fmt: 0 = fp8 x fp8, 1 = fp8 x fp4, 2 = fp4 x fp4.  The MX launchers write
+// fmt: 0 = E4M3 x E4M3, 1 = E4M3 x E2M1, 2 = E2M1 x E2M1, 3 = E5M2 x E5M2,
+// 4 = E4M3 x E5M2, 5 = E5M2 x E4M3 (A x B).  The MX launchers write
 // C through the epilogue `e` (output pointer, bias, activation, output type).
 hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);

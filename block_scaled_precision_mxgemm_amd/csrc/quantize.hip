@@ -2,11 +2,13 @@
 // consecutive K elements.
 //
 // Rule (one block of 32): amax = max |x|; e = floor(log2 amax) - emax with
-// emax = 8 (E4M3, largest finite 448 = 1.75 * 2^8) or 2 (E2M1, 6 = 1.5 * 2^2),
+// emax = 8 (E4M3, largest finite 448 = 1.75 * 2^8), 15 (E5M2, 57344 =
+// 1.75 * 2^15) or 2 (E2M1, 6 = 1.5 * 2^2),
 // clamped to [-127, 127], e = -127 for an all-zero block; scale byte e + 127;
 // every element x * 2^-e is rounded to nearest, ties to even, and saturated to
 // the largest finite magnitude (E4M3 has no infinity and clamps at +-448:
-// "Resumo Técnico: RIGEL", section 3, saturation).  A block holding a NaN or
+// "Resumo Técnico: RIGEL", section 3, saturation; E5M2 is saturated the same
+// way inside a block, although a plain E5M2 cast overflows to infinity).  A block holding a NaN or
 // an infinity gets scale byte 255 (NaN) and zero codes.  One E8M0 scale per 32
 // elements along the reduction axis: WWDC26 session 330 summary, section
 // "Scale Factor 付き量子化 tensor を作成する".
@@ -83,6 +85,11 @@ __device__ __forceinline__ uint32_t encode_e4m3(uint32_t bits, int e) {
   return encode_mag<3, -6, 0x7Eu>(bits, e) | ((bits >> 31) << 7);
 }
 
+// E5M2 (bias 15, 2 mantissa bits, largest finite 57344 = 0x7B).
+__device__ __forceinline__ uint32_t encode_e5m2(uint32_t bits, int e) {
+  return encode_mag<2, -14, 0x7Bu>(bits, e) | ((bits >> 31) << 7);
+}
+
 __device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
   return encode_mag<1, 0, 0x7u>(bits, e) | ((bits >> 31) << 3);
 }
@@ -92,7 +99,8 @@ __device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
 template <int ELEM>
 __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int sub, uint8_t* __restrict__ Q,
                                                uint8_t* __restrict__ S) {
-  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : 2;
+  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : (ELEM == kFmtBf8) ? 15 : 2;
+  constexpr bool kByte = ELEM != kFmtFp4;  // one code per byte
   uint32_t amax = 0u;
 #pragma unroll
   for (int i = 0; i < 4; i++) amax = max(amax, (uint32_t)x[i] & 0x7fffffffu);
@@ -110,10 +118,13 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
   uint32_t c[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    c[i] = bad ? 0u : ((ELEM == kFmtFp8) ? encode_e4m3((uint32_t)x[i], e) : encode_e2m1((uint32_t)x[i], e));
+    c[i] = bad ? 0u
+               : (ELEM == kFmtFp8)   ? encode_e4m3((uint32_t)x[i], e)
+               : (ELEM == kFmtBf8)   ? encode_e5m2((uint32_t)x[i], e)
+                                     : encode_e2m1((uint32_t)x[i], e);
   }
   const int64_t off = blk * 32 + sub * 4;  // element index
-  if (ELEM == kFmtFp8) {
+  if (kByte) {
     *reinterpret_cast<uint32_t*>(Q + off) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
   } else {
     *reinterpret_cast<uint16_t*>(Q + (off >> 1)) = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
@@ -158,6 +169,9 @@ hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, vo
   if (grid > 256 * 32) grid = 256 * 32;
   if (elem == kFmtFp8)
     hipLaunchKernelGGL(quantize_kernel<kFmtFp8>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
+                       total);
+  else if (elem == kFmtBf8)
+    hipLaunchKernelGGL(quantize_kernel<kFmtBf8>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
                        total);
   else
     hipLaunchKernelGGL(quantize_kernel<kFmtFp4>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,

@@ -18,7 +18,8 @@ operands).  Recipes per workload:
                 the MXFP4 x MXFP4 prefill takes the same sources
   decode        M=16 x N=28672 x K=8192; A ~ N(0, 1) (MXFP8), B ~ N(0, 0.02)
                 (MXFP4, E2M1 codes)
-  mxfp8_8192    8192^3, A, B ~ N(0, 1)
+  mxfp8_8192    8192^3, A, B ~ N(0, 1); the E4M3 x E5M2 8192^3 product takes
+                the same sources
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ WORKLOADS = {
                  "decode MXFP8 x MXFP4 GEMM, 16 tokens x 8192 -> 28672"),
         Workload("mxfp8_8192", 8192, 8192, 8192, 6, "e4m3", "e4m3", "normal",
                  "MXFP8 GEMM 8192^3, N(0,1) operands"),
+        Workload("mxfp8xbf8_8192", 8192, 8192, 8192, 6, "e4m3", "e5m2", "normal",
+                 "MX GEMM 8192^3, E4M3 A x E5M2 B, the same N(0,1) sources"),
     ]
 }
 

@@ -14,12 +14,17 @@ import os
 import torch
 
 E4M3 = 0
+E5M2 = 1
 E2M1 = 4
 FMT_FP8_FP8 = 0
 FMT_FP8_FP4 = 1
 FMT_FP4_FP4 = 2
+FMT_BF8_BF8 = 3
+FMT_FP8_BF8 = 4
+FMT_BF8_FP8 = 5
 
-_FMT_ELEMS = {FMT_FP8_FP8: (E4M3, E4M3), FMT_FP8_FP4: (E4M3, E2M1), FMT_FP4_FP4: (E2M1, E2M1)}
+_FMT_ELEMS = {FMT_FP8_FP8: (E4M3, E4M3), FMT_FP8_FP4: (E4M3, E2M1), FMT_FP4_FP4: (E2M1, E2M1),
+              FMT_BF8_BF8: (E5M2, E5M2), FMT_FP8_BF8: (E4M3, E5M2), FMT_BF8_FP8: (E5M2, E4M3)}
 
 # output types and activations of the fused epilogue (MXG_OUT_*, MXG_ACT_*)
 OUT_F32 = 0
@@ -85,7 +90,7 @@ def _stream(stream):
 def _dev_u8(t: torch.Tensor, name: str) -> torch.Tensor:
     if not t.is_cuda:
         raise ValueError(name + " must be a GPU tensor")
-    if t.dtype in (torch.float8_e4m3fn, torch.float8_e8m0fnu):
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2, torch.float8_e8m0fnu):
         t = t.view(torch.uint8)
     if t.dtype != torch.uint8:
         raise TypeError(name + " must hold uint8 codes")
@@ -95,7 +100,7 @@ def _dev_u8(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def _row_bytes(K: int, elem: int) -> int:
-    return K if elem == E4M3 else K // 2
+    return K // 2 if elem == E2M1 else K
 
 
 def mxgemm_device_supported() -> bool:

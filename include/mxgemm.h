@@ -28,8 +28,10 @@
  *     planes are M x K/32 and N x K/32 bytes, row-major, and use the same row
  *     order as their data planes.
  *   - E4M3 is the OCP "FN" variant (bias 7, max 448, NaN = S.1111.111, no
- *     infinity).  E2M1 codes are packed with the even K index in the low
- *     nibble.  UE8M0 byte e means 2^(e-127); e = 255 is NaN and propagates.
+ *     infinity).  E5M2 is the OCP variant with IEEE-style specials (bias 15,
+ *     max 57344, S.11111.00 = +-inf, S.11111.xx (xx != 0) = NaN).  E2M1 codes
+ *     are packed with the even K index in the low nibble.  UE8M0 byte e means
+ *     2^(e-127); e = 255 is NaN and propagates.
  *   - Data pointers (codes, fp16, fp32) must be 16-byte aligned (the kernels
  *     move operands with 16-byte loads); scale pointers need no alignment.
  *     The 128-byte row alignment the RIGEL summary reports for Metal inline
@@ -54,12 +56,16 @@ extern "C" {
 
 /* Element formats (values equal the MFMA operand-format ids). */
 #define MXG_ELEM_E4M3 0
+#define MXG_ELEM_E5M2 1
 #define MXG_ELEM_E2M1 4
 
 /* Operand-format pairs for mxgemm_run: (A element, B element). */
-#define MXG_FMT_FP8_FP8 0
-#define MXG_FMT_FP8_FP4 1
-#define MXG_FMT_FP4_FP4 2
+#define MXG_FMT_FP8_FP8 0   /* E4M3 x E4M3 */
+#define MXG_FMT_FP8_FP4 1   /* E4M3 x E2M1 */
+#define MXG_FMT_FP4_FP4 2   /* E2M1 x E2M1 */
+#define MXG_FMT_BF8_BF8 3   /* E5M2 x E5M2 */
+#define MXG_FMT_FP8_BF8 4   /* E4M3 x E5M2 */
+#define MXG_FMT_BF8_FP8 5   /* E5M2 x E4M3 */
 
 /* Largest accepted M, N (rows) and K. */
 #define MXG_MAX_DIM (1 << 20)
@@ -76,11 +82,13 @@ extern "C" {
  *
  * For every row r and every block b of 32 consecutive elements along K:
  *   amax = max |X[r][32b .. 32b+31]|;
- *   e    = floor(log2(amax)) - emax  (emax = 8 for E4M3, 2 for E2M1),
+ *   e    = floor(log2(amax)) - emax  (emax = 8 for E4M3, 15 for E5M2, 2 for
+ *          E2M1),
  *          clamped to [-127, 127]; e = -127 when amax = 0;
  *   S[r][b] = e + 127;
  *   Q[r][k] = round-to-nearest-even(X[r][k] * 2^-e), saturated to +-448
- *             (E4M3) or +-6 (E2M1), sign kept (-0 -> 0x80 / 0x8).
+ *             (E4M3), +-57344 (E5M2) or +-6 (E2M1), sign kept (-0 -> 0x80 /
+ *             0x8).
  * A block holding a NaN or an infinity gets S = 255 (NaN) and zero codes.
  * E4M3 saturating rather than overflowing follows "Resumo Técnico: RIGEL",
  * section 3 (saturation); one E8M0 scale per 32 elements follows the WWDC26
@@ -89,8 +97,9 @@ extern "C" {
  *
  *   X     device, rows x K fp32, row-major, 16-byte aligned (read only)
  *   rows  >= 1;  K >= 32, K % 32 == 0
- *   elem  MXG_ELEM_E4M3 (Q: rows x K bytes) or MXG_ELEM_E2M1 (Q: rows x K/2
- *         bytes, even k in the low nibble); Q 16-byte aligned (written)
+ *   elem  MXG_ELEM_E4M3 or MXG_ELEM_E5M2 (Q: rows x K bytes) or MXG_ELEM_E2M1
+ *         (Q: rows x K/2 bytes, even k in the low nibble); Q 16-byte aligned
+ *         (written)
  *   S     device, rows x K/32 bytes (written)
  * Returns MXG_OK or an error status.  The output is bit-for-bit deterministic.
  */
@@ -100,20 +109,21 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
 /*
  * mxgemm_run - C = (A * 2^sA)(B * 2^sB)^T in fp32 on the scaled MFMA path.
  *
- *   A, scaleA  device; A is M x K codes (E4M3: M*K bytes; E2M1: M*K/2 bytes),
- *              scaleA is M x K/32 UE8M0 bytes
+ *   A, scaleA  device; A is M x K codes (E4M3 / E5M2: M*K bytes; E2M1: M*K/2
+ *              bytes), scaleA is M x K/32 UE8M0 bytes
  *   B, scaleB  device; B is N x K codes, scaleB is N x K/32 bytes
  *   C          device, M x N fp32 row-major, 16-byte aligned; overwritten
  *   M, N       >= 1 (any value; edges are masked); K >= 32, K % 32 == 0
- *   fmt        MXG_FMT_FP8_FP8, MXG_FMT_FP8_FP4 or MXG_FMT_FP4_FP4
+ *   fmt        one of the MXG_FMT_* pairs (A element, B element)
  * Each 32-element block product is formed by CDNA4's scaled fp8/fp4 MFMA,
  * which applies the E8M0 scales itself; partial sums accumulate in fp32.
- * Decode shapes take weight-streaming kernels: K = 2048, 4096 or 8192
- * with M <= 64 one that reads B once per launch (two launches for
- * M > 32 at K = 8192), other small M (M <= 64) a split-K kernel.
+ * Decode shapes with E4M3 activations and E4M3 or E2M1 weights take
+ * weight-streaming kernels: K = 2048, 4096 or 8192 with M <= 64 one that
+ * reads B once per launch (two launches for M > 32 at K = 8192), other
+ * small M (M <= 64) a split-K kernel.
  * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the
- * workloads this library is tested on (the MFMA's internal alignment of
- * wide-range products is the dominant error term; see the design notes).
+ * workloads this library is tested on; the MFMA's internal alignment of
+ * wide-range products within one instruction is the dominant error term.
  * Returns MXG_OK or an error status.  The result is deterministic.
  */
 int mxgemm_run(const void *A, const uint8_t *scaleA,

@@ -10,7 +10,8 @@ from block_scaled_precision_mxgemm_amd import inputs as mxin
 
 DEV = "cuda:0"
 
-FMT_ELEMS = {0: (oracle.E4M3, oracle.E4M3), 1: (oracle.E4M3, oracle.E2M1), 2: (oracle.E2M1, oracle.E2M1)}
+FMT_ELEMS = {0: (oracle.E4M3, oracle.E4M3), 1: (oracle.E4M3, oracle.E2M1), 2: (oracle.E2M1, oracle.E2M1),
+             3: (oracle.E5M2, oracle.E5M2), 4: (oracle.E4M3, oracle.E5M2), 5: (oracle.E5M2, oracle.E4M3)}
 
 # Per-dtype allowance of the scaled fp8/fp4 MFMA path, in units of
 # 2^-24 * sum|a b|.  CDNA4's v_mfma_scale_f32_16x16x128_f8f6f4 does not add the

@@ -102,16 +102,20 @@ def test_quantize_all_e4m3_ties():
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
-@pytest.mark.parametrize("elem", [oracle.E4M3, oracle.E2M1])
+@pytest.mark.parametrize("elem", [oracle.E4M3, oracle.E5M2, oracle.E2M1])
 def test_quantize_every_mantissa_at_boundary_exponents(elem):
     """All 2^23 fp32 mantissas, both signs, at the exponents where the
     rounding changes regime, with the block maximum fixed so the scale is
     2^0: for E4M3 the round-to-zero edge (2^-10), the last subnormal and first
-    normal binades (2^-7, 2^-6) and the saturating top binade (2^8); for E2M1
+    normal binades (2^-7, 2^-6) and the saturating top binade (2^8); for E5M2
+    2^-18 (round to zero or 2^-16), the subnormal binades 2^-16 and 2^-15, the
+    first normal binade 2^-14 and the saturating top binade 2^15; for E2M1
     2^-2 (round to zero or 0.5), 2^-1 (subnormal), 2^0 and 2^2 (saturation)."""
     say("quantize every mantissa", elem)
     if elem == oracle.E4M3:
         amax, ks = np.float32(256.0), (-10, -7, -6, 8)
+    elif elem == oracle.E5M2:
+        amax, ks = np.float32(32768.0), (-18, -16, -15, -14, 15)
     else:
         amax, ks = np.float32(4.0), (-2, -1, 0, 2)
     mant = np.arange(1 << 23, dtype=np.uint32)
@@ -140,7 +144,7 @@ SMALL_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
 def test_mx_gemm_small_full(fmt, M, N, K):
     say("mx small", fmt, M, N, K)
@@ -168,7 +172,7 @@ def test_mx_gemm_large_tiles_full():
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5])
 def test_mx_gemm_persistent_two_tiles_full(fmt):
     """More 256 x 256 tiles (16 x 17 = 272) than the grid's one workgroup per
     CU, so some workgroups run a second tile after the tile transition (next
