@@ -1,6 +1,6 @@
-// gemm_decode.hip - MX GEMM for decode shapes with few activation rows (M <= 64;
-// one launch per 32 rows at K = 8192) against a large weight matrix B (N x K,
-// MXFP8 or MXFP4).  The
+// gemm_decode.hip - MX GEMM for decode shapes with few activation rows (M <= 64)
+// against a large weight matrix B (N x K, MXFP8 or MXFP4; K a multiple of 2048
+// up to 16384).  The
 // product is bound by the bytes of B, which must stream from HBM exactly
 // once; the weight plane is what quantization shrinks ("Metal tensors で
 // カスタム機械学習オペレーションを最適化する", section "主要内容": inference
@@ -86,12 +86,16 @@ struct Decode {
   static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
   static constexpr int SZ_PSLOT = MB * kDecWaves * 64 * 16;  // one fragment's partials
   static constexpr int LDS = OFF_PART + 2 * SZ_PSLOT;
-  static constexpr int NSA = KW > 4 ? 2 : 1;             // loads of this wave's A scale dwords (per block)
+  // loads of this wave's SBW A scale bytes per block: 16-byte loads when
+  // SBW is a multiple of 16, else 8-byte ones (SBW = 4 KW, KW even)
+  static constexpr bool SA16 = (KW % 4) == 0;
+  static constexpr int NSA = SA16 ? KW / 4 : KW / 2;
   static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
   static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
   static_assert(MB >= 1 && MB * KW <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
+  static_assert(KW % 2 == 0, "K a multiple of 2048");
 
   // fp8 operand of the MFMA covering k0 .. k0+127 of row `p` (p at k0):
   // lane group g holds k0 + 16g .. +15 and k0 + 64 + 16g .. +15
@@ -214,10 +218,13 @@ struct Decode {
         // the scale dwords stay raw until the MFMA: extracting a byte here
         // would wait for this load in the middle of the prologue
         const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
-        if constexpr (KW == 2) {
-          const v2i d = *reinterpret_cast<const v2i*>(srow);
-          t.sa[mb][0] = (uint32_t)d[0];
-          t.sa[mb][1] = (uint32_t)d[1];
+        if constexpr (!SA16) {
+#pragma unroll
+          for (int i = 0; i < NSA; i++) {
+            const v2i d = *reinterpret_cast<const v2i*>(srow + 8 * i);
+            t.sa[mb][2 * i] = (uint32_t)d[0];
+            t.sa[mb][2 * i + 1] = (uint32_t)d[1];
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < NSA; i++) {
@@ -380,33 +387,48 @@ hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// row blocks of 16 activations: 1 or 2 for every K, 4 for K <= 4096 (the A
-// operands of all blocks must fit 128 registers per lane)
+// Row blocks of 16 activations per launch: the A operands of all blocks must
+// fit 128 registers per lane (MB KW <= 16).
+constexpr int max_blocks(int kw) { return kw <= 4 ? 4 : kw <= 8 ? 2 : 1; }
+
 template <bool BF4, int KW>
 hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
-  if (a.M <= 16) return launch_dec<BF4, KW, 1>(a, cus, stream);
-  if (a.M <= 32 || KW > 4) return launch_dec<BF4, KW, 2>(a, cus, stream);
-  return launch_dec<BF4, KW, (KW > 4 ? 2 : 4)>(a, cus, stream);
+  if (a.M <= 16 || max_blocks(KW) == 1) return launch_dec<BF4, KW, 1>(a, cus, stream);
+  if (a.M <= 32 || max_blocks(KW) == 2) return launch_dec<BF4, KW, (max_blocks(KW) >= 2 ? 2 : 1)>(a, cus, stream);
+  return launch_dec<BF4, KW, max_blocks(KW)>(a, cus, stream);
 }
+
+// Largest K / 1024: with fp8 weights (one MFMA per stage) the per-stage
+// state of 14 or 16 MFMAs per wave no longer fits beside the A operands.
+constexpr int max_kw(bool bf4) { return bf4 ? 16 : 12; }
 
 template <bool BF4>
 hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream) {
-  switch (a.K) {
-    case 2048: return launch_dec_m<BF4, 2>(a, cus, stream);
-    case 4096: return launch_dec_m<BF4, 4>(a, cus, stream);
-    default: return launch_dec_m<BF4, 8>(a, cus, stream);
+  switch (a.K / 1024) {
+    case 2: return launch_dec_m<BF4, 2>(a, cus, stream);
+    case 4: return launch_dec_m<BF4, 4>(a, cus, stream);
+    case 6: return launch_dec_m<BF4, 6>(a, cus, stream);
+    case 8: return launch_dec_m<BF4, 8>(a, cus, stream);
+    case 10: return launch_dec_m<BF4, 10>(a, cus, stream);
+    case 12: return launch_dec_m<BF4, 12>(a, cus, stream);
+    default:
+      if constexpr (max_kw(BF4) >= 16) {
+        return a.K == 14336 ? launch_dec_m<BF4, 14>(a, cus, stream) : launch_dec_m<BF4, 16>(a, cus, stream);
+      } else {
+        return hipErrorInvalidValue;  // excluded by decode_ok
+      }
   }
 }
 
-// Rows of A one launch covers.  At K = 8192 the A operands of 2 row blocks
-// fill the registers, so 33 .. 64 rows take two launches, each streaming B
-// once (16 x 28672 x 8192 fp8 x fp4: 2 x 26-29 us, against 110-128 us for the
-// split-K kernel).
-int64_t rows_per_launch(int64_t K) { return K == 8192 ? 32 : 64; }
+// Rows of A one launch covers: 64 for K <= 4096, 32 for K <= 8192, 16
+// above (the A operands of all row blocks fill the registers).  More rows
+// take more launches, each streaming B once (16 x 28672 x 8192 fp8 x fp4,
+// 33 .. 64 rows: 2 x 26-29 us, against 110-128 us for the split-K kernel).
+int64_t rows_per_launch(int64_t K) { return 16 * max_blocks((int)(K / 1024)); }
 
 }  // namespace
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB) {
-  return M <= 64 && (fmt == 0 || fmt == 1) && (K == 2048 || K == 4096 || K == 8192) &&
+  return M <= 64 && (fmt == 0 || fmt == 1) && (K % 2048) == 0 && K >= 2048 && K <= 1024 * max_kw(fmt == 1) &&
          (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
 }
 

