@@ -41,6 +41,13 @@ constexpr int kDecWaves = 8;
 // brings each wave's first stage back sooner (16 x 28672 x 8192: 24.3 us at
 // depth 4 against 25.7 us at depth 8; fp8 weights 39.7 against 39.4 us).
 constexpr int kDecStages = 4;
+// Ring depth when every workgroup owns at most one fragment (N <= 16 x CUs):
+// a wave's whole stream is then a few stages, all of which can be in flight
+// at once (16 x 4096 x 4096 fp8 x fp4: 9.8 against 11.0 us; 8 x 2048 x 8192:
+// 9.6-9.8 against 10.7 us; allowing 2 or 4 fragments per workgroup made
+// 16 x 8192 x 8192 slower, 13.6-13.8 against 12.2 us).
+constexpr int kDecStagesDeep = 8;
+constexpr int kDeepMaxFrags = 1;
 constexpr int kBand = 128;                    // bytes of each weight row per stage and wave
 constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
 // Reduced output fragments a wave keeps in registers until its copies are
@@ -70,9 +77,9 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0
 // KW: MFMAs (128 k each) per wave per fragment, K / 1024.  MB: blocks of 16
 // activation rows (M <= 16 MB); each weight operand read from LDS feeds one
 // MFMA per block, so the weight stream is the same for every MB.
-template <bool BF4, int KW, int MB>
+template <bool BF4, int KW, int MB, int D_>
 struct Decode {
-  static constexpr int D = kDecStages;
+  static constexpr int D = D_;
   static constexpr int MPS = BF4 ? 2 : 1;                // MFMAs per stage (128 bytes of a row)
   static constexpr int NQ = KW / MPS;                    // stages per fragment
   static constexpr int WB = BF4 ? KW * 64 : KW * 128;    // bytes of a weight row per wave
@@ -91,7 +98,7 @@ struct Decode {
   static constexpr bool SA16 = (KW % 4) == 0;
   static constexpr int NSA = SA16 ? KW / 4 : KW / 2;
   static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
-  static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
+  static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
   static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
   static_assert(MB >= 1 && MB * KW <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
@@ -375,15 +382,16 @@ struct Decode {
   }
 };
 
-template <bool BF4, int KW, int MB>
+template <bool BF4, int KW, int MB, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void decode_kernel(DecArgs a) {
-  Decode<BF4, KW, MB>::run(a);
+  static_assert(Decode<BF4, KW, MB, D>::FITS, "fits the 160 KiB LDS of a gfx950 CU");
+  Decode<BF4, KW, MB, D>::run(a);
 }
 
-template <bool BF4, int KW, int MB>
+template <bool BF4, int KW, int MB, int D = kDecStages>
 hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   const int grid = a.nfrags < cus ? a.nfrags : cus;
-  hipLaunchKernelGGL((decode_kernel<BF4, KW, MB>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<BF4, KW, MB, D>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -393,7 +401,13 @@ constexpr int max_blocks(int kw) { return kw <= 4 ? 4 : kw <= 8 ? 2 : 1; }
 
 template <bool BF4, int KW>
 hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
-  if (a.M <= 16 || max_blocks(KW) == 1) return launch_dec<BF4, KW, 1>(a, cus, stream);
+  if (a.M <= 16 || max_blocks(KW) == 1) {
+    // few weight fragments per CU: the ring covers a whole fragment
+    if constexpr (Decode<BF4, KW, 1, kDecStagesDeep>::FITS) {
+      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<BF4, KW, 1, kDecStagesDeep>(a, cus, stream);
+    }
+    return launch_dec<BF4, KW, 1>(a, cus, stream);
+  }
   if (a.M <= 32 || max_blocks(KW) == 2) return launch_dec<BF4, KW, (max_blocks(KW) >= 2 ? 2 : 1)>(a, cus, stream);
   return launch_dec<BF4, KW, max_blocks(KW)>(a, cus, stream);
 }
