@@ -39,10 +39,12 @@ KERNEL_SOURCES = {
     "mx_gemm_8192": ["block_scaled_precision_mxgemm_amd/csrc/api.hip",
                      "block_scaled_precision_mxgemm_amd/csrc/gemm_tiled.hip",
                      "block_scaled_precision_mxgemm_amd/csrc/gemm_pingpong.hip",
-                     "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"],
+                     "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h",
+                     "block_scaled_precision_mxgemm_amd/csrc/mxg_epilogue.h"],
     "decode_16x28672x8192": ["block_scaled_precision_mxgemm_amd/csrc/api.hip",
                              "block_scaled_precision_mxgemm_amd/csrc/gemm_decode.hip",
-                             "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h"],
+                             "block_scaled_precision_mxgemm_amd/csrc/mxg_device.h",
+                             "block_scaled_precision_mxgemm_amd/csrc/mxg_epilogue.h"],
 }
 
 
