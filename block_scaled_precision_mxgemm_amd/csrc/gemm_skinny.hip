@@ -9,10 +9,13 @@
 //   * no LDS staging of B: every lane loads its MFMA operand bytes straight
 //     from global memory (16-byte loads) in the scaled-MFMA register layout,
 //     so each B byte is read once and used once;
-//   * a workgroup owns NF * 16 columns of C (rows of B); its 4 waves split
-//     the K range four ways (split-K) and the partial sums are added in LDS
+//   * a workgroup owns NF * 16 columns of C (rows of B); its W waves split
+//     the K range W ways (split-K) and the partial sums are added in LDS
 //     in a fixed order, so the result is deterministic and needs no atomics
-//     and no zero-initialised output;
+//     and no zero-initialised output.  For M <= 16, NF is the largest of 4,
+//     2, 1 that still gives every CU a workgroup, and W = 8 when NF < 4
+//     (16 x 8192 x 28672 fp8 x fp4: 55 against 88 us; 16 x 1024 x 11008:
+//     13 against 30 us; 16 x 28672 x 5120 keeps NF = 4, W = 4);
 //   * each wave keeps two groups of U slices in flight (registers), loading
 //     group j+1 while the MFMAs of group j run;
 //   * the activation rows (<= 64, a few hundred KiB) are re-read from L2 by
@@ -34,7 +37,7 @@ struct SkArgs {
   int nslices;       // ceil(K / 128)
 };
 
-template <int MT, int NF, bool BF4, int U>
+template <int MT, int NF, bool BF4, int U, int W>
 struct Skinny {
   struct Group {
     v8i a[U][MT];
@@ -107,12 +110,12 @@ struct Skinny {
   }
 
   static __device__ __forceinline__ void run(const SkArgs& a) {
-    __shared__ v4f red[3][MT][NF][64];
+    __shared__ v4f red[W - 1][MT][NF][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int n0 = blockIdx.x * NF * 16;
     // K split: wave w takes slices [s_begin, s_end)
-    const int per = (a.nslices + 3) / 4;
+    const int per = (a.nslices + W - 1) / W;
     const int s_begin = min(wave * per, a.nslices);
     const int s_end = min(s_begin + per, a.nslices);
 
@@ -145,7 +148,7 @@ struct Skinny {
       for (int j = 0; j < NF; j++) {
         v4f v = acc[t][j];
 #pragma unroll
-        for (int w = 0; w < 3; w++) v += red[w][t][j][lane];
+        for (int w = 0; w < W - 1; w++) v += red[w][t][j][lane];
         if (m >= a.M) continue;
         const int n = n0 + j * 16 + 4 * g;
         epi_store4<false>(a.e, a.N, m, n, v, (a.N & 3) == 0 && n + 3 < a.N);
@@ -154,21 +157,30 @@ struct Skinny {
   }
 };
 
-template <int MT, int NF, bool BF4, int U>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void skinny_kernel(SkArgs a) {
-  Skinny<MT, NF, BF4, U>::run(a);
+template <int MT, int NF, bool BF4, int U, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(W * 64, W * 64))) void skinny_kernel(SkArgs a) {
+  Skinny<MT, NF, BF4, U, W>::run(a);
 }
 
-template <int MT, int NF, bool BF4, int U>
+template <int MT, int NF, bool BF4, int U, int W = 4>
 hipError_t launch_sk(const SkArgs& a, hipStream_t stream) {
   const int grid = (a.N + NF * 16 - 1) / (NF * 16);
-  hipLaunchKernelGGL((skinny_kernel<MT, NF, BF4, U>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((skinny_kernel<MT, NF, BF4, U, W>), dim3(grid), dim3(W * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool BF4>
 hipError_t launch_by_m(const SkArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_sk<1, 4, BF4, 2>(a, stream);
+  if (a.M <= 16) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                  hipSuccess || cus <= 0)
+      cus = 256;
+    const int64_t frags = (a.N + 15) / 16;
+    if (frags >= 4 * (int64_t)cus) return launch_sk<1, 4, BF4, 2, 4>(a, stream);
+    if (frags >= 2 * (int64_t)cus) return launch_sk<1, 2, BF4, 2, 8>(a, stream);
+    return launch_sk<1, 1, BF4, 2, 8>(a, stream);
+  }
   if (a.M <= 32) return launch_sk<2, 4, BF4, 2>(a, stream);
   return launch_sk<4, 2, BF4, 2>(a, stream);
 }
