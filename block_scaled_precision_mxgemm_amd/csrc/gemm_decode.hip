@@ -93,10 +93,13 @@ struct Decode {
   static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
   static constexpr int SZ_PSLOT = MB * kDecWaves * 64 * 16;  // one fragment's partials
   static constexpr int LDS = OFF_PART + 2 * SZ_PSLOT;
-  // loads of this wave's SBW A scale bytes per block: 16-byte loads when
-  // SBW is a multiple of 16, else 8-byte ones (SBW = 4 KW, KW even)
-  static constexpr bool SA16 = (KW % 4) == 0;
-  static constexpr int NSA = SA16 ? KW / 4 : KW / 2;
+  // loads of this wave's SBW = 4 KW A scale bytes per block: 16-byte loads
+  // and, when KW % 4 == 2, one 8-byte load for the last 8 bytes.  The wait
+  // counts below count these instructions, so they are written as the
+  // widest loads the compiler could merge them into (separate 8-byte loads
+  // of adjacent bytes were merged, which made the counts one too high).
+  static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8;
+  static constexpr int NSA = NS16 + NS8;
   static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
   static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
@@ -225,20 +228,16 @@ struct Decode {
         // the scale dwords stay raw until the MFMA: extracting a byte here
         // would wait for this load in the middle of the prologue
         const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
-        if constexpr (!SA16) {
 #pragma unroll
-          for (int i = 0; i < NSA; i++) {
-            const v2i d = *reinterpret_cast<const v2i*>(srow + 8 * i);
-            t.sa[mb][2 * i] = (uint32_t)d[0];
-            t.sa[mb][2 * i + 1] = (uint32_t)d[1];
-          }
-        } else {
+        for (int i = 0; i < NS16; i++) {
+          const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
 #pragma unroll
-          for (int i = 0; i < NSA; i++) {
-            const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
-#pragma unroll
-            for (int e = 0; e < 4; e++) t.sa[mb][4 * i + e] = (uint32_t)d[e];
-          }
+          for (int e = 0; e < 4; e++) t.sa[mb][4 * i + e] = (uint32_t)d[e];
+        }
+        if constexpr (NS8 == 1) {
+          const v2i d = *reinterpret_cast<const v2i*>(srow + 16 * NS16);
+          t.sa[mb][4 * NS16] = (uint32_t)d[0];
+          t.sa[mb][4 * NS16 + 1] = (uint32_t)d[1];
         }
       }
     }

@@ -102,3 +102,30 @@ def test_kernel_source_is_hazard_free(src):
     for f in funcs:
         problems += H.check_function(f)
     assert not problems, "\n".join(problems[:20])
+
+
+@pytest.mark.skipif(shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")) is None, reason="hipcc not found")
+def test_decode_kernel_first_wait_counts_the_issued_loads():
+    """The decode kernel's stage waits count the vector-memory instructions
+    issued after a stage's copies; in the first fragment these include the
+    A operand and A scale loads of the prologue, counted as 2 KW + NSA per
+    row block (NSA = the 16-byte scale loads plus one 8-byte load when 4 KW is
+    not a multiple of 16).  The compiler must issue exactly that many global
+    loads before the first wait, or the wait lets a stage's copies still be
+    in flight."""
+    import re
+    from block_scaled_precision_mxgemm_amd import build as B
+    asm = H.compile_to_asm(os.path.join(ROOT, "block_scaled_precision_mxgemm_amd", "csrc", "gemm_decode.hip"),
+                           B.FLAGS, B.HIPCC)
+    seen = 0
+    for m in re.finditer(r"^(_ZN3mxg12_GLOBAL__N_113decode_kernelILb([01])ELi(\d+)ELi(\d+)ELi(\d+)EEEv\S*):", asm,
+                         re.M):
+        kw, mb = int(m.group(3)), int(m.group(4))
+        body = asm[m.end():asm.index(".Lfunc_end", m.end())]
+        first_wait = re.search(r"s_waitcnt vmcnt\(", body)
+        assert first_wait, m.group(1)
+        loads = re.findall(r"^\s*global_load_\w+", body[:first_wait.start()], re.M)
+        nsa = (4 * kw) // 16 + ((4 * kw) % 16) // 8
+        assert len(loads) == mb * (2 * kw + nsa), (m.group(1), len(loads), mb * (2 * kw + nsa))
+        seen += 1
+    assert seen >= 20
