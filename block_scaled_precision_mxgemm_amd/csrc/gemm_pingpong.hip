@@ -394,6 +394,188 @@ void pingpong_kernel(PPArgs a) {
   PPKernel<T>::run(a);
 }
 
+// ---- 128 x 128 tiles, K split between the groups --------------------------
+//
+// Outputs with too few 256 x 256 tiles for the chip (2048^3 has 64) take one
+// workgroup per 128 x 128 tile with the same 8-wave ping-pong, but both groups
+// compute the whole tile: group 0 the even K slices, group 1 the odd ones,
+// each wave a 64 x 64 sub-tile (4 x 4 fragments, 64 accumulator registers).
+// Each group double-buffers its own slices (A, B and scale rows of one slice
+// per stage), so while one group reads fragments and issues its next copies
+// the other runs its 16 MFMAs, as in the 256 x 256 kernel; a single-group
+// 128 x 128 kernel instead spends its copy issue, fragment reads and MFMAs in
+// series.  At the end group 1 passes its partial sums to group 0 through LDS
+// and group 0 adds them (its own first, a fixed order) and stores the tile
+// through the epilogue.
+template <class T>
+struct PP128Kernel {
+  using P = PPKernel<T>;
+  static constexpr int SZ_A = 128 * T::RA, SZ_B = 128 * T::RB;
+  static constexpr int SZ_S = T::SCALED ? 128 * 4 : 0;  // scale rows of one operand, one slice
+  static constexpr int SZ_STAGE = SZ_A + SZ_B + 2 * SZ_S;
+  static constexpr int SZ_GROUP = 2 * SZ_STAGE;
+  static constexpr int SZ_RED = 4 * 16 * 64 * 16;  // group 1's partials: 4 waves x 16 fragments x 64 lanes
+  static constexpr int LDS = 2 * SZ_GROUP > SZ_RED ? 2 * SZ_GROUP : SZ_RED;
+  static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
+
+  template <int... I>
+  static __device__ __forceinline__ void compute_scaled(v4f (&acc)[4][4], const v8i (&af)[4], const v8i (&bf)[4],
+                                                        int sa, int sb, std::integer_sequence<int, I...>) {
+    (mfma_scaled_acc_pk<T::FB, T::FA, I / 4, I % 4>(acc[I % 4][I / 4], bf[I / 4], af[I % 4], sb, sa), ...);
+  }
+
+  static __device__ __forceinline__ void run(const PPArgs& a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, sw = wave & 3;
+    const int lg = lane >> 4, r = lane & 15;
+    const int S = a.nslices;
+    const int S0 = (S + 1) / 2;              // group 0 takes slices 0, 2, ...
+    const int Sg = grp == 0 ? S0 : S / 2;    // group 1 takes slices 1, 3, ...
+    const int nb = a.K >> 5;
+    int tm, tn;
+    tile_of_block(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * 128, n0 = tn * 128;
+
+    constexpr int kRsrcWord3 = 0x00020000;
+    const uint32_t lda = (uint32_t)a.lda, ldb = (uint32_t)a.ldb;
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)(a.A + (int64_t)m0 * lda), 0, 128 * lda, kRsrcWord3);
+    const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)n0 * ldb), 0, 128 * ldb, kRsrcWord3);
+    __amdgpu_buffer_rsrc_t rs_sa = rs_a, rs_sb = rs_b;
+    if (T::SCALED) {
+      rs_sa = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SA + (int64_t)m0 * nb), 0, 128 * nb, kRsrcWord3);
+      rs_sb = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)n0 * nb), 0, 128 * nb, kRsrcWord3);
+    }
+    const uint32_t oa = P::template lane_offset<T::RA>(a.lda, lane, sw);
+    // equal row sizes come with equal strides in every launch
+    const uint32_t ob = (T::RA == T::RB) ? oa : P::template lane_offset<T::RB>(a.ldb, lane, sw);
+    const uint32_t os = (uint32_t)(lane * nb);
+    uint8_t* gbase = smem + grp * SZ_GROUP;
+
+    // copies of this group's iteration i (slice 2i + grp) into its stage i & 1
+    auto copy_iter = [&](int i) {
+      const int k = 2 * i + grp;
+      uint8_t* st = gbase + (i & 1) * SZ_STAGE;
+      P::template copy_rows<T::RA, 128>(rs_a, lda, 0, k, st, sw, oa);
+      P::template copy_rows<T::RB, 128>(rs_b, ldb, 0, k, st + SZ_A, sw, ob);
+      if (T::SCALED) {
+        P::template copy_scales<128>(rs_sa, nb, 0, k, st + SZ_A + SZ_B, sw, os);
+        P::template copy_scales<128>(rs_sb, nb, 0, k, st + SZ_A + SZ_B + SZ_S, sw, os);
+      }
+    };
+    if (Sg > 0) copy_iter(0);
+    vm_wait_all();
+    phase_barrier();
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    mfma_fence_init(acc);
+
+    // Barrier pairing: group 0's load phase of iteration i meets group 1's
+    // compute phase of iteration i - 1 and the other way round; group 1
+    // starts one phase late and skips the barrier after its last compute,
+    // then both groups pad to the 2 S0 barriers of group 0's loop.
+    int nbar = 0;
+    if (grp == 1) {
+      phase_barrier();
+      nbar = 1;
+    }
+    const int wr = (sw >> 1) * 64, wc = (sw & 1) * 64;  // this wave's sub-tile
+    for (int i = 0; i < Sg; i++) {
+      const uint8_t* st = gbase + (i & 1) * SZ_STAGE;
+      v8i af[4], bf[4];
+      int sa = 0, sb = 0;
+#pragma unroll
+      for (int f = 0; f < 4; f++) af[f] = P::template read_frag<T::RA>(st, wr + 16 * f + r, lg);
+#pragma unroll
+      for (int f = 0; f < 4; f++) bf[f] = P::template read_frag<T::RB>(st + SZ_A, wc + 16 * f + r, lg);
+      if (T::SCALED) {
+        const uint8_t* lsa = st + SZ_A + SZ_B;
+        const uint8_t* lsb = lsa + SZ_S;
+        uint32_t x[4], y[4];
+#pragma unroll
+        for (int f = 0; f < 4; f++) x[f] = lsa[(wr + 16 * f + r) * 4 + lg];
+#pragma unroll
+        for (int f = 0; f < 4; f++) y[f] = lsb[(wc + 16 * f + r) * 4 + lg];
+        sa = (int)(x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24));
+        sb = (int)(y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24));
+      }
+      if (i + 1 < Sg) copy_iter(i + 1);
+      if constexpr (T::SCALED) {
+        // as in the 256 x 256 kernel: the packed scales are operands of the
+        // barrier, and s_nop covers the VALU-write -> MFMA-read wait states
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_nop 4" : "+v"(sa), "+v"(sb)::"memory");
+      } else {
+        phase_barrier();
+      }
+      nbar++;
+      if constexpr (T::SCALED) {
+        compute_scaled(acc, af, bf, sa, sb, std::make_integer_sequence<int, 16>{});
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int f = 0; f < 4; f++) {
+              const v4i bq = h ? v4i{bf[j][4], bf[j][5], bf[j][6], bf[j][7]} : v4i{bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
+              const v4i aq = h ? v4i{af[f][4], af[f][5], af[f][6], af[f][7]} : v4i{af[f][0], af[f][1], af[f][2], af[f][3]};
+              mfma_f16_acc_v(acc[f][j], bq, aq);
+            }
+      }
+      vm_wait_all();  // this group's copies for iteration i + 1
+      if (grp == 0 || i + 1 < Sg) {
+        phase_barrier();
+        nbar++;
+      }
+    }
+    for (; nbar < 2 * S0; nbar++) phase_barrier();
+    mfma_drain(acc);
+
+    // every load phase and copy has completed: the stages are free
+    v4f* red = reinterpret_cast<v4f*>(smem) + sw * 16 * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) red[(i * 4 + j) * 64] = acc[i][j];
+    }
+    phase_barrier();
+    if (grp == 1) return;
+    // Lane (lg, r) of fragment (i, j) holds C[m][n .. n+3] with m = 16 i + r
+    // of the sub-tile's rows and n = 16 j + 4 lg of its columns.
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t m = m0 + wr + 16 * i + r;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const v4f v = acc[i][j] + red[(i * 4 + j) * 64];
+        epi_store4<true>(a.e, a.N, m, n0 + wc + 16 * j + 4 * lg, v, true);
+      }
+    }
+  }
+};
+
+template <class T>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void pp128_kernel(PPArgs a) {
+  PP128Kernel<T>::run(a);
+}
+
+template <class T>
+hipError_t launch_pp128(PPArgs a, int kslice, hipStream_t stream) {
+  a.tiles_m = a.M / 128;
+  a.tiles_n = a.N / 128;
+  a.nslices = a.K / kslice;
+  const int tiles = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((pp128_kernel<T>), dim3((unsigned)tiles), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <class T>
 hipError_t launch_pp(PPArgs a, int kslice, hipStream_t stream) {
   a.tiles_m = (a.M + 255) / 256;
@@ -414,6 +596,10 @@ hipError_t launch_pp(PPArgs a, int kslice, hipStream_t stream) {
 
 bool pingpong_mx_ok(const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N, int64_t K) {
   return (M % 256) == 0 && (N % 256) == 0 && (K % 128) == 0 && (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
+}
+
+bool pp128_mx_ok(const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N, int64_t K) {
+  return (M % 128) == 0 && (N % 128) == 0 && (K % 128) == 0 && (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
 }
 
 hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
@@ -437,6 +623,43 @@ hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, c
     case 4: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtBf8>>(a, 128, stream);
     default: return launch_pp<PPCfg<kPPMX, kFmtBf8, kFmtFp8>>(a, 128, stream);
   }
+}
+
+hipError_t launch_mx_pp128(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                           int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
+  PPArgs a{};
+  a.A = (const uint8_t*)A;
+  a.SA = SA;
+  a.B = (const uint8_t*)B;
+  a.SB = SB;
+  a.e = e;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.lda = (fmt == 2) ? K / 2 : K;
+  a.ldb = (fmt == 1 || fmt == 2) ? K / 2 : K;
+  switch (fmt) {
+    case 0: return launch_pp128<PPCfg<kPPMX, kFmtFp8, kFmtFp8>>(a, 128, stream);
+    case 1: return launch_pp128<PPCfg<kPPMX, kFmtFp8, kFmtFp4>>(a, 128, stream);
+    case 2: return launch_pp128<PPCfg<kPPMX, kFmtFp4, kFmtFp4>>(a, 128, stream);
+    case 3: return launch_pp128<PPCfg<kPPMX, kFmtBf8, kFmtBf8>>(a, 128, stream);
+    case 4: return launch_pp128<PPCfg<kPPMX, kFmtFp8, kFmtBf8>>(a, 128, stream);
+    default: return launch_pp128<PPCfg<kPPMX, kFmtBf8, kFmtFp8>>(a, 128, stream);
+  }
+}
+
+hipError_t launch_f16_pp128(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
+                            hipStream_t stream) {
+  PPArgs a{};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.e = Epi{C, nullptr, kOutF32, kActNone};
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.lda = K * 2;
+  a.ldb = K * 2;
+  return launch_pp128<PPCfg<kPPF16, kFmtFp8, kFmtFp8>>(a, 64, stream);
 }
 
 hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,

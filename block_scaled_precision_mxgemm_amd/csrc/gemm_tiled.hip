@@ -462,6 +462,7 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
   // the 256 x 256 tiled kernels store plain fp32 only (MxBig*::EPI_GENERAL)
   const bool big_pp = use_big_tiles(M, N);
   if (big_pp && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, e, M, N, K, fmt, stream);
+  if (pp128_mx_ok(SA, SB, M, N, K)) return launch_mx_pp128(A, SA, B, SB, e, M, N, K, fmt, stream);
   const bool big = big_pp && e.bias == nullptr && e.act == kActNone && e.out == kOutF32;
   static_assert(!MxBig88::EPI_GENERAL && MxMid88::EPI_GENERAL && MxMid84::EPI_GENERAL && MxMid44::EPI_GENERAL,
                 "general epilogues run on the 128 x 128 tiles");
@@ -485,6 +486,7 @@ hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int6
   }
   a.ldb = K * 2;
   if (use_big_tiles(M, N) && M % 256 == 0 && N % 256 == 0 && K % 64 == 0) return launch_f16_pingpong(A, B, C, M, N, K, stream);
+  if (M % 128 == 0 && N % 128 == 0 && K % 64 == 0) return launch_f16_pp128(A, B, C, M, N, K, stream);
   return use_big_tiles(M, N) ? launch<F16Big, 1>(a, stream) : launch<F16Mid, 2>(a, stream);
 }
 

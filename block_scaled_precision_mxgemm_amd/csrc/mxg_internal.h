@@ -32,6 +32,14 @@ hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, c
                               int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
 hipError_t launch_f16_pingpong(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream);
+// The same ping-pong on 128 x 128 tiles with K split between the two wave
+// groups (M, N multiples of 128; MX: K % 128 == 0 and 4-byte aligned scale
+// planes; fp16: K % 64 == 0 and an N x K right operand).
+bool pp128_mx_ok(const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N, int64_t K);
+hipError_t launch_mx_pp128(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
+                           int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
+hipError_t launch_f16_pp128(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
+                            hipStream_t stream);
 
 // Decode kernel for M <= 64 (MX fp8 x fp8 or fp8 x fp4): K one of 2048,
 // 4096, 8192 (A's k range per wave is held in registers), 4-byte aligned

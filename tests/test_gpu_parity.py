@@ -369,6 +369,35 @@ def test_fp16_gemm_persistent_two_tiles():
     assert r["ok"], r
 
 
+# ----------------------------------------- 128 x 128 split-K ping-pong
+
+# Full 128-tiles with fewer than 256 tiles of 256 x 256: the two wave groups
+# of one workgroup take the even and odd K slices of a 128 x 128 tile.  One
+# slice (group 1 idle), an odd slice count (group 0 one slice more, barrier
+# padding), an even one, and more tiles than CUs.
+PP128_SHAPES = [(128, 128, 128), (256, 384, 384), (384, 128, 640), (1024, 1152, 256), (2304, 2176, 512)]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("M,N,K", PP128_SHAPES)
+def test_mx_gemm_pp128_full(fmt, M, N, K):
+    say("mx pp128", fmt, M, N, K)
+    a32, b32 = mx_sources("mxfp8_2048", M, N, K, seed=3 * M + N + K + fmt)
+    pts = None if M * N <= 1 << 20 else mxin.sample_points(M, N, 40000, tile=128)
+    r, _ = mx_case(a32, b32, fmt, points=pts)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (256, 384, 192), (384, 256, 320), (2304, 2176, 256)])
+def test_fp16_gemm_pp128(M, N, K):
+    say("fp16 pp128", M, N, K)
+    w = mxin.WORKLOADS["mxfp8_2048"]
+    a16, b16 = mxin.fp16_sources(w, True, M, N, K, seed=M + N + K)
+    pts = None if M * N <= 1 << 20 else mxin.sample_points(M, N, 40000, tile=128)
+    r = _fp16_case(a16, b16, True, points=pts)
+    assert r["ok"], r
+
+
 # ---------------------------------------------------- dequant ablation
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (129, 200, 160), (300, 257, 384)])
