@@ -12,10 +12,11 @@
 //   * a workgroup owns NF * 16 columns of C (rows of B); its W waves split
 //     the K range W ways (split-K) and the partial sums are added in LDS
 //     in a fixed order, so the result is deterministic and needs no atomics
-//     and no zero-initialised output.  For M <= 16, NF is the largest of 4,
-//     2, 1 that still gives every CU a workgroup, and W = 8 when NF < 4
-//     (16 x 8192 x 28672 fp8 x fp4: 55 against 88 us; 16 x 1024 x 11008:
-//     13 against 30 us; 16 x 28672 x 5120 keeps NF = 4, W = 4);
+//     and no zero-initialised output.  NF is the largest of 4 (2 for M > 32),
+//     2, 1 that still gives every CU a workgroup, and W = 8 when NF is
+//     below that maximum (16 x 8192 x 28672 fp8 x fp4: 55 against 88 us;
+//     16 x 1024 x 11008: 13 against 30 us; 16 x 28672 x 5120 keeps NF = 4,
+//     W = 4);
 //   * each wave keeps two groups of U slices in flight (registers), loading
 //     group j+1 while the MFMAs of group j run;
 //   * the activation rows (<= 64, a few hundred KiB) are re-read from L2 by
@@ -169,20 +170,26 @@ hipError_t launch_sk(const SkArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Column width (fragments per workgroup) and K split: the widest of NFMAX,
+// 2, 1 fragments that still gives every CU a workgroup, with 8 waves
+// splitting K when narrower than NFMAX.
+template <int MT, int NFMAX, bool BF4>
+hipError_t launch_by_n(const SkArgs& a, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t frags = (a.N + 15) / 16;
+  if (frags >= NFMAX * (int64_t)cus) return launch_sk<MT, NFMAX, BF4, 2, 4>(a, stream);
+  if (NFMAX > 2 && frags >= 2 * (int64_t)cus) return launch_sk<MT, (NFMAX > 2 ? 2 : 1), BF4, 2, 8>(a, stream);
+  return launch_sk<MT, 1, BF4, 2, 8>(a, stream);
+}
+
 template <bool BF4>
 hipError_t launch_by_m(const SkArgs& a, hipStream_t stream) {
-  if (a.M <= 16) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                  hipSuccess || cus <= 0)
-      cus = 256;
-    const int64_t frags = (a.N + 15) / 16;
-    if (frags >= 4 * (int64_t)cus) return launch_sk<1, 4, BF4, 2, 4>(a, stream);
-    if (frags >= 2 * (int64_t)cus) return launch_sk<1, 2, BF4, 2, 8>(a, stream);
-    return launch_sk<1, 1, BF4, 2, 8>(a, stream);
-  }
-  if (a.M <= 32) return launch_sk<2, 4, BF4, 2>(a, stream);
-  return launch_sk<4, 2, BF4, 2>(a, stream);
+  if (a.M <= 16) return launch_by_n<1, 4, BF4>(a, stream);
+  if (a.M <= 32) return launch_by_n<2, 4, BF4>(a, stream);
+  return launch_by_n<4, 2, BF4>(a, stream);
 }
 
 }  // namespace

@@ -155,11 +155,12 @@ def test_mx_gemm_small_full(fmt, M, N, K):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 512), (16, 1000, 1024), (17, 64, 96), (33, 500, 4096),
-                                   (64, 129, 256), (5, 28, 32), (16, 8200, 1536), (10, 16400, 4608)])
+                                   (64, 129, 256), (5, 28, 32), (16, 8200, 1536), (10, 16400, 4608),
+                                   (32, 8200, 1536), (24, 16400, 1536), (48, 8200, 1536)])
 def test_mx_gemm_skinny_full(fmt, M, N, K):
-    """The split-K kernel: for M <= 16 its column width and wave count follow
-    N (1, 2 or 4 fragments per workgroup; 8200 and 16400 columns take the
-    wider ones, with a ragged last workgroup)."""
+    """The split-K kernel: its column width and wave count follow N (1, 2 or
+    4 fragments per workgroup, at most 2 above 32 rows; 8200 and 16400
+    columns take the wider ones, with a ragged last workgroup)."""
     say("mx skinny", fmt, M, N, K)
     a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=M + N + K)
     r, _ = mx_case(a32, b32, fmt)
