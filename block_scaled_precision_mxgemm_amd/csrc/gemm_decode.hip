@@ -1,6 +1,6 @@
 // gemm_decode.hip - MX GEMM for decode shapes with few activation rows (M <= 64)
-// against a large weight matrix B (N x K, MXFP8 or MXFP4; K a multiple of 2048
-// up to 16384).  The
+// against a large weight matrix B (N x K, MXFP8 or MXFP4; K a multiple of 1024
+// from 2048 up to 12288 for MXFP8 and 16384 for MXFP4 weights).  The
 // product is bound by the bytes of B, which must stream from HBM exactly
 // once; the weight plane is what quantization shrinks ("Metal tensors で
 // カスタム機械学習オペレーションを最適化する", section "主要内容": inference
@@ -15,14 +15,17 @@
 //     whole kernel; each weight operand it reads from LDS feeds one MFMA per
 //     row block;
 //   * each wave streams its own k band of the fragment rows through a private
-//     LDS ring of kDecStages stages (16 rows x 128 bytes) with direct
-//     global->LDS copies of 8 rows x 128 bytes per instruction (whole cache
-//     lines; this pattern streams as fast as 1 KiB row segments on MI355X,
-//     5.7 TB/s for a 112 MiB read).  A wave waits only for its own copies:
-//     the stages need no workgroup barrier;
-//   * inside a 128-byte stage row the 16-byte chunks are XOR-swizzled with
-//     (row >> 1) & 7 (applied on the global side, so the copy still writes LDS
-//     linearly), which makes the MFMA fragment reads conflict-free;
+//     LDS ring of stages (16 rows x 128 bytes) with direct global->LDS copies
+//     of 8 rows x 128 bytes per instruction (whole cache lines; this pattern
+//     streams as fast as 1 KiB row segments on MI355X, 5.7 TB/s for a
+//     112 MiB read).  A wave waits only for its own copies: the stages need
+//     no workgroup barrier.  MXFP4 weights with K / 1024 odd give each wave
+//     an odd number of 64-byte MFMA operands per row; their stages are
+//     16 rows x 64 bytes (one copy instruction), with a ring twice as deep;
+//   * inside a stage row the 16-byte chunks are XOR-swizzled (128-byte rows:
+//     with (row >> 1) & 7; 64-byte rows: (row >> 2) & 3), applied on the
+//     global side so that the copy still writes LDS linearly, which makes the
+//     MFMA fragment reads conflict-free;
 //   * a fragment's 8 per-wave partial sums meet in LDS after one barrier per
 //     fragment; one wave adds them in a fixed order, so the result is
 //     deterministic and needs no atomics, and keeps the sum in registers: C
@@ -48,8 +51,6 @@ constexpr int kDecStages = 4;
 // 16 x 8192 x 8192 slower, 13.6-13.8 against 12.2 us).
 constexpr int kDecStagesDeep = 8;
 constexpr int kDeepMaxFrags = 1;
-constexpr int kBand = 128;                    // bytes of each weight row per stage and wave
-constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
 // Reduced output fragments a wave keeps in registers until its copies are
 // done.  A store issued inside the stream would sit among the copies in the
 // in-order vector-memory counter and make the next stage waits of that wave
@@ -77,10 +78,19 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0
 // KW: MFMAs (128 k each) per wave per fragment, K / 1024.  MB: blocks of 16
 // activation rows (M <= 16 MB); each weight operand read from LDS feeds one
 // MFMA per block, so the weight stream is the same for every MB.
+// Bytes of each weight row per stage and wave: 128, or 64 for E2M1 weights
+// when a wave's KW operands of 64 bytes do not pair up.
+constexpr int band_bytes(bool bf4, int kw) { return (bf4 && kw % 2 == 1) ? 64 : 128; }
+
 template <bool BF4, int KW, int MB, int D_>
 struct Decode {
   static constexpr int D = D_;
-  static constexpr int MPS = BF4 ? 2 : 1;                // MFMAs per stage (128 bytes of a row)
+  static constexpr int BAND = band_bytes(BF4, KW);
+  static constexpr int STAGE = 16 * BAND;                // one stage: 16 rows
+  static constexpr int LPB = BAND / 16;                  // copy lanes per stage row (16 bytes each)
+  static constexpr int RPC = 64 / LPB;                   // stage rows per copy instruction
+  static constexpr int CPS = 16 / RPC;                   // copy instructions per stage
+  static constexpr int MPS = BF4 ? BAND / 64 : 1;        // MFMAs per stage
   static constexpr int NQ = KW / MPS;                    // stages per fragment
   static constexpr int WB = BF4 ? KW * 64 : KW * 128;    // bytes of a weight row per wave
   static constexpr int SBW = 4 * KW;                     // scale bytes of a row per wave
@@ -89,23 +99,23 @@ struct Decode {
   // scale slots: a fragment's slot is refilled only after its last stage
   static constexpr int NSL = (NQ - 1 + D + NQ - 1) / NQ;
   static constexpr int SZ_SC = NSI * 256;
-  static constexpr int SZ_WAVE = D * kStageBytes + NSL * SZ_SC;
+  static constexpr int SZ_WAVE = D * STAGE + NSL * SZ_SC;
   static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
   static constexpr int SZ_PSLOT = MB * kDecWaves * 64 * 16;  // one fragment's partials
   static constexpr int LDS = OFF_PART + 2 * SZ_PSLOT;
-  // loads of this wave's SBW = 4 KW A scale bytes per block: 16-byte loads
-  // and, when KW % 4 == 2, one 8-byte load for the last 8 bytes.  The wait
-  // counts below count these instructions, so they are written as the
-  // widest loads the compiler could merge them into (separate 8-byte loads
-  // of adjacent bytes were merged, which made the counts one too high).
-  static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8;
-  static constexpr int NSA = NS16 + NS8;
+  // loads of this wave's SBW = 4 KW A scale bytes per block: 16-byte loads,
+  // then 8 and 4 bytes for the rest.  They are issued before any copy, so
+  // the stage waits never count them (the compiler may merge the small ones).
+  static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8, NS4 = (SBW % 8) / 4;
   static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
   static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
   static_assert(MB >= 1 && MB * KW <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
-  static_assert(KW % 2 == 0, "K a multiple of 2048");
+  static_assert(STAGE == CPS * 1024, "whole copy instructions per stage");
+
+  // physical 16-byte chunk of logical chunk c in stage row r: c ^ swz(r)
+  static __device__ __forceinline__ int swz(int r) { return BAND == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
 
   // fp8 operand of the MFMA covering k0 .. k0+127 of row `p` (p at k0):
   // lane group g holds k0 + 16g .. +15 and k0 + 64 + 16g .. +15
@@ -139,8 +149,8 @@ struct Decode {
     int lane, wave, g, r;
     int f_begin, nf;
     uint32_t rb, nb;      // bytes per B row, scale bytes per row
-    int brow;             // lane's row in a copy of 8 rows
-    uint32_t bch[2];      // lane's swizzled chunk offset, rows 0-7 / 8-15
+    int brow;             // lane's row in a copy of RPC rows
+    uint32_t bch[CPS];    // lane's swizzled chunk offset in each copy of a stage
     int srow[NSI];        // lane's row in each scale copy
     uint32_t scol[NSI];   // and its byte in that row's band
     v8i av[MB][KW];       // A operands of this wave's MFMAs, per row block
@@ -150,15 +160,15 @@ struct Decode {
   };
 
   // Vector-memory instructions of the A loads that stage q of the first
-  // fragment needs: lo and hi halves per MFMA, and the scale dwords with q = 0.
-  static constexpr int la(int q) { return MB * (2 * MPS + (q == 0 ? NSA : 0)); }
+  // fragment needs: lo and hi halves per MFMA.
+  static constexpr int la(int q) { return MB * 2 * MPS; }
   static constexpr int la_from(int q) { return q >= NQ ? 0 : la(q) + la_from(q + 1); }
   // Copies issued after stage s's copies and before its wait: the copies of
-  // stages s+1 .. s+D-2 (2 weight copies each, plus the scale copies at every
-  // fragment start) and, in the first fragment, the A loads of stages
+  // stages s+1 .. s+D-2 (CPS weight copies each, plus the scale copies at
+  // every fragment start) and, in the first fragment, the A loads of stages
   // q .. NQ-1 issued by the prologue after stage q's copies.
   static constexpr int younger(int q, bool first) {
-    return 2 * (D - 2) + NSI * ((q + D - 2) / NQ) + (first && q <= D - 2 ? la_from(q) : 0);
+    return CPS * (D - 2) + NSI * ((q + D - 2) / NQ) + (first && q <= D - 2 ? la_from(q) : 0);
   }
 
   template <int N>
@@ -195,7 +205,7 @@ struct Decode {
     if (q == 0) {
       const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * t.nb), 0, 16 * t.nb,
                                                           kRsrcWord3);
-      uint8_t* sc = t.wsm + D * kStageBytes + (fs % NSL) * SZ_SC;
+      uint8_t* sc = t.wsm + D * STAGE + (fs % NSL) * SZ_SC;
 #pragma unroll
       for (int i = 0; i < NSI; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(sc + i * 256), 4,
@@ -203,18 +213,18 @@ struct Decode {
                                                  (uint32_t)(t.wave * SBW), 0, kStreamPolicy);
     }
     const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * t.rb), 0, 16 * t.rb, kRsrcWord3);
-    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * kStageBytes;
-    const uint32_t soff = (uint32_t)(t.wave * WB + qv * kBand);
+    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * STAGE;
+    const uint32_t soff = (uint32_t)(t.wave * WB + qv * BAND);
 #pragma unroll
-    for (int h = 0; h < 2; h++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), 16,
-                                               (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0,
+    for (int h = 0; h < CPS; h++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * RPC * BAND), 16,
+                                               (uint32_t)min(t.brow + RPC * h, last) * t.rb + t.bch[h], soff, 0,
                                                kStreamPolicy);
   }
 
   // A operands for stage q of this wave (rows clamped to M-1; rows >= M are
   // computed and discarded): wave MFMA j = q * MPS + u covers k 128 (w KW + j)
-  // .. +127; its scale is byte g of the dword of blocks 4 (w KW + j) .. +3.
+  // .. +127.
   template <int Q>
   static __device__ __forceinline__ void load_a(State& t) {
     const DecArgs& a = *t.a;
@@ -224,29 +234,39 @@ struct Decode {
       const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.wave * KW * 128;
 #pragma unroll
       for (int u = 0; u < MPS; u++) t.av[mb][Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
-      if constexpr (Q == 0) {
-        // the scale dwords stay raw until the MFMA: extracting a byte here
-        // would wait for this load in the middle of the prologue
-        const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
-#pragma unroll
-        for (int i = 0; i < NS16; i++) {
-          const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
-#pragma unroll
-          for (int e = 0; e < 4; e++) t.sa[mb][4 * i + e] = (uint32_t)d[e];
-        }
-        if constexpr (NS8 == 1) {
-          const v2i d = *reinterpret_cast<const v2i*>(srow + 16 * NS16);
-          t.sa[mb][4 * NS16] = (uint32_t)d[0];
-          t.sa[mb][4 * NS16 + 1] = (uint32_t)d[1];
-        }
-      }
     }
   }
 
-  // Prologue, in this issue order: stage p's copies then A(p), for p = 0 ..;
-  // stages up to D - 2, A up to NQ - 1.
+  // A scales of this wave: MFMA j takes byte g of the dword of blocks
+  // 4 (w KW + j) .. +3.  The dwords stay raw until the MFMA: extracting a byte
+  // here would wait for these loads before the first copy is issued.
+  static __device__ __forceinline__ void load_a_scales(State& t) {
+    const DecArgs& a = *t.a;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      const int m = min(16 * mb + t.r, a.M - 1);
+      const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
+#pragma unroll
+      for (int i = 0; i < NS16; i++) {
+        const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) t.sa[mb][4 * i + e] = (uint32_t)d[e];
+      }
+      if constexpr (NS8 == 1) {
+        const v2i d = *reinterpret_cast<const v2i*>(srow + 16 * NS16);
+        t.sa[mb][4 * NS16] = (uint32_t)d[0];
+        t.sa[mb][4 * NS16 + 1] = (uint32_t)d[1];
+      }
+      if constexpr (NS4 == 1) t.sa[mb][KW - 1] = *reinterpret_cast<const uint32_t*>(srow + SBW - 4);
+    }
+  }
+
+  // Prologue, in this issue order: the A scales, then stage p's copies and
+  // A(p), for p = 0 ..; stages up to D - 2, A up to NQ - 1.
   template <int... P>
   static __device__ __forceinline__ void prologue(State& t, std::integer_sequence<int, P...>) {
+    load_a_scales(t);
+    order_fence();
     (
         [&] {
           if constexpr (P <= D - 2) issue(t, P / NQ, P % NQ, true);
@@ -272,20 +292,20 @@ struct Decode {
       wait_stage<0>();
     // stage s + D - 1, into the buffer read at stage s - 1
     issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ, FIRST);
-    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * kStageBytes;
-    const uint8_t* sc = t.wsm + D * kStageBytes + (f % NSL) * SZ_SC;
+    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * STAGE;
+    const uint8_t* sc = t.wsm + D * STAGE + (f % NSL) * SZ_SC;
     const int g = t.g, r = t.r;
-    const int sw = (r >> 1) & 7;
+    const int sw = swz(r);
 #pragma unroll
     for (int u = 0; u < MPS; u++) {
       const int j = Q * MPS + u;  // this wave's MFMA index inside the fragment
       v8i bv;
       if (BF4) {
-        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 * u + g) ^ sw) << 4));
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * BAND + (((4 * u + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
       } else {
-        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + ((g ^ sw) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 + g) ^ sw) << 4));
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * BAND + ((g ^ sw) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(st + r * BAND + (((4 + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       const int sb = sc[r * SBW + 4 * j + g];
@@ -346,11 +366,11 @@ struct Decode {
     t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
     t.rb = BF4 ? (uint32_t)(a.K >> 1) : (uint32_t)a.K;
     t.nb = (uint32_t)(a.K >> 5);
-    // copy lane l: row l >> 3 (+8), physical chunk l & 7 holding logical chunk
-    // (l & 7) ^ ((row >> 1) & 7)
-    t.brow = t.lane >> 3;
+    // copy h, lane l: stage row l / LPB + RPC h, physical chunk l % LPB
+    // holding logical chunk (l % LPB) ^ swz(row)
+    t.brow = t.lane / LPB;
 #pragma unroll
-    for (int h = 0; h < 2; h++) t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * 16);
+    for (int h = 0; h < CPS; h++) t.bch[h] = (uint32_t)(((t.lane % LPB) ^ swz(t.brow + RPC * h)) * 16);
     // scale copy i, lane l: entry e = 64 i + l is row e / LPR, dword e % LPR
     // (entries past row 15 repeat row 15 into the slot's unused tail)
 #pragma unroll
@@ -387,7 +407,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void decode_ke
   Decode<BF4, KW, MB, D>::run(a);
 }
 
-template <bool BF4, int KW, int MB, int D = kDecStages>
+// Ring depth in stages: the same bytes in flight for 64-byte stages.
+constexpr int ring(bool bf4, int kw, int depth) { return depth * (128 / band_bytes(bf4, kw)); }
+
+template <bool BF4, int KW, int MB, int D = ring(BF4, KW, kDecStages)>
 hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   const int grid = a.nfrags < cus ? a.nfrags : cus;
   hipLaunchKernelGGL((decode_kernel<BF4, KW, MB, D>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
@@ -402,8 +425,9 @@ template <bool BF4, int KW>
 hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
   if (a.M <= 16 || max_blocks(KW) == 1) {
     // few weight fragments per CU: the ring covers a whole fragment
-    if constexpr (Decode<BF4, KW, 1, kDecStagesDeep>::FITS) {
-      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<BF4, KW, 1, kDecStagesDeep>(a, cus, stream);
+    constexpr int deep = ring(BF4, KW, kDecStagesDeep);
+    if constexpr (Decode<BF4, KW, 1, deep>::FITS) {
+      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<BF4, KW, 1, deep>(a, cus, stream);
     }
     return launch_dec<BF4, KW, 1>(a, cus, stream);
   }
@@ -415,22 +439,20 @@ hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
 // state of 14 or 16 MFMAs per wave no longer fits beside the A operands.
 constexpr int max_kw(bool bf4) { return bf4 ? 16 : 12; }
 
-template <bool BF4>
-hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream) {
-  switch (a.K / 1024) {
-    case 2: return launch_dec_m<BF4, 2>(a, cus, stream);
-    case 4: return launch_dec_m<BF4, 4>(a, cus, stream);
-    case 6: return launch_dec_m<BF4, 6>(a, cus, stream);
-    case 8: return launch_dec_m<BF4, 8>(a, cus, stream);
-    case 10: return launch_dec_m<BF4, 10>(a, cus, stream);
-    case 12: return launch_dec_m<BF4, 12>(a, cus, stream);
-    default:
-      if constexpr (max_kw(BF4) >= 16) {
-        return a.K == 14336 ? launch_dec_m<BF4, 14>(a, cus, stream) : launch_dec_m<BF4, 16>(a, cus, stream);
-      } else {
-        return hipErrorInvalidValue;  // excluded by decode_ok
-      }
+template <bool BF4, int KW>
+hipError_t launch_dec_kw(const DecArgs& a, int cus, hipStream_t stream) {
+  if constexpr (KW > max_kw(BF4)) {
+    return hipErrorInvalidValue;  // excluded by decode_ok
+  } else {
+    return launch_dec_m<BF4, KW>(a, cus, stream);
   }
+}
+
+template <bool BF4, int... KW>
+hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream, std::integer_sequence<int, KW...>) {
+  hipError_t err = hipErrorInvalidValue;  // K / 1024 outside 2 .. 16: excluded by decode_ok
+  ((a.K == 1024 * (KW + 2) ? (err = launch_dec_kw<BF4, KW + 2>(a, cus, stream), 0) : 0), ...);
+  return err;
 }
 
 // Rows of A one launch covers: 64 for K <= 4096, 32 for K <= 8192, 16
@@ -441,7 +463,7 @@ int64_t rows_per_launch(int64_t K) { return 16 * max_blocks((int)(K / 1024)); }
 
 }  // namespace
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB) {
-  return M <= 64 && (fmt == 0 || fmt == 1) && (K % 2048) == 0 && K >= 2048 && K <= 1024 * max_kw(fmt == 1) &&
+  return M <= 64 && (fmt == 0 || fmt == 1) && (K % 1024) == 0 && K >= 2048 && K <= 1024 * max_kw(fmt == 1) &&
          (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
 }
 
@@ -465,7 +487,8 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
     a.N = (int)N;
     a.K = (int)K;
     a.nfrags = (int)((N + 15) / 16);
-    err = fmt == 1 ? launch_dec_k<true>(a, cus, stream) : launch_dec_k<false>(a, cus, stream);
+    const auto kws = std::make_integer_sequence<int, 15>{};  // K / 1024 = 2 .. 16
+    err = fmt == 1 ? launch_dec_k<true>(a, cus, stream, kws) : launch_dec_k<false>(a, cus, stream, kws);
   }
   return err;
 }

@@ -118,8 +118,8 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * Each 32-element block product is formed by CDNA4's scaled fp8/fp4 MFMA,
  * which applies the E8M0 scales itself; partial sums accumulate in fp32.
  * Decode shapes with E4M3 activations and E4M3 or E2M1 weights take
- * weight-streaming kernels: for K a multiple of 2048 up to 16384 (E2M1
- * weights) or 12288 (E4M3 weights) and M <= 64 one that reads B once per
+ * weight-streaming kernels: for K a multiple of 1024 from 2048 up to 16384
+ * (E2M1 weights) or 12288 (E4M3 weights) and M <= 64 one that reads B once per
  * launch (one launch per 64, 32 or 16 rows for K <= 4096, <= 8192, above),
  * for other small M (M <= 64) a split-K kernel.
  * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the

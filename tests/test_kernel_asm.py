@@ -108,11 +108,12 @@ def test_kernel_source_is_hazard_free(src):
 def test_decode_kernel_first_wait_counts_the_issued_loads():
     """The decode kernel's stage waits count the vector-memory instructions
     issued after a stage's copies; in the first fragment these include the
-    A operand and A scale loads of the prologue, counted as 2 KW + NSA per
-    row block (NSA = the 16-byte scale loads plus one 8-byte load when 4 KW is
-    not a multiple of 16).  The compiler must issue exactly that many global
-    loads before the first wait, or the wait lets a stage's copies still be
-    in flight."""
+    A operand loads of the prologue, 2 KW per row block (the lo and hi
+    halves of each MFMA operand).  The A scales are loaded before the first
+    copy, so that however the compiler merges those loads they are never
+    among the counted ones.  Between the first copy and the first wait the
+    compiler must issue exactly the counted global loads, or the wait lets a
+    stage's copies still be in flight."""
     import re
     from block_scaled_precision_mxgemm_amd import build as B
     asm = H.compile_to_asm(os.path.join(ROOT, "block_scaled_precision_mxgemm_amd", "csrc", "gemm_decode.hip"),
@@ -123,9 +124,11 @@ def test_decode_kernel_first_wait_counts_the_issued_loads():
         kw, mb = int(m.group(3)), int(m.group(4))
         body = asm[m.end():asm.index(".Lfunc_end", m.end())]
         first_wait = re.search(r"s_waitcnt vmcnt\(", body)
-        assert first_wait, m.group(1)
-        loads = re.findall(r"^\s*global_load_\w+", body[:first_wait.start()], re.M)
-        nsa = (4 * kw) // 16 + ((4 * kw) % 16) // 8
-        assert len(loads) == mb * (2 * kw + nsa), (m.group(1), len(loads), mb * (2 * kw + nsa))
+        first_copy = re.search(r"^\s*buffer_load_dwordx4 .* lds", body, re.M)
+        assert first_wait and first_copy and first_copy.start() < first_wait.start(), m.group(1)
+        scales = re.findall(r"^\s*global_load_\w+", body[:first_copy.start()], re.M)
+        assert 1 <= len(scales) <= mb * kw, (m.group(1), len(scales))
+        loads = re.findall(r"^\s*global_load_\w+", body[first_copy.start():first_wait.start()], re.M)
+        assert len(loads) == mb * 2 * kw, (m.group(1), len(loads), mb * 2 * kw)
         seen += 1
-    assert seen >= 20
+    assert seen >= 60
