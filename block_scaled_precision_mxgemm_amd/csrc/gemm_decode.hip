@@ -10,7 +10,8 @@
 // Design (gfx950):
 //   * one persistent workgroup of 8 waves per CU owns a contiguous range of
 //     16-row blocks of B ("fragments");
-//   * wave w owns the k range [w K/8, (w+1) K/8) of every fragment and holds
+//   * wave w owns the k range [w K/8, (w+1) K/8) of every fragment (but see
+//     the uneven split below) and holds
 //     the matching A operands (1 to 4 blocks of 16 rows) in registers for the
 //     whole kernel; each weight operand it reads from LDS feeds one MFMA per
 //     row block;
@@ -19,13 +20,13 @@
 //     of 8 rows x 128 bytes per instruction (whole cache lines; this pattern
 //     streams as fast as 1 KiB row segments on MI355X, 5.7 TB/s for a
 //     112 MiB read).  A wave waits only for its own copies: the stages need
-//     no workgroup barrier.  MXFP4 weights with K / 1024 odd give each wave
-//     an odd number of 64-byte MFMA operands per row; their stages are
-//     16 rows x 64 bytes (one copy instruction), with a ring twice as deep;
-//   * inside a stage row the 16-byte chunks are XOR-swizzled (128-byte rows:
-//     with (row >> 1) & 7; 64-byte rows: (row >> 2) & 3), applied on the
-//     global side so that the copy still writes LDS linearly, which makes the
-//     MFMA fragment reads conflict-free;
+//     no workgroup barrier.  With MXFP4 weights and K / 1024 odd, one eighth
+//     of a row is an odd number of 64-byte MFMA operands; waves 0-3 then take
+//     one operand more and waves 4-7 one less, so every band is whole
+//     128-byte stages;
+//   * inside a 128-byte stage row the 16-byte chunks are XOR-swizzled with
+//     (row >> 1) & 7 (applied on the global side, so the copy still writes LDS
+//     linearly), which makes the MFMA fragment reads conflict-free;
 //   * a fragment's 8 per-wave partial sums meet in LDS after one barrier per
 //     fragment; one wave adds them in a fixed order, so the result is
 //     deterministic and needs no atomics, and keeps the sum in registers: C
@@ -51,6 +52,8 @@ constexpr int kDecStages = 4;
 // 16 x 8192 x 8192 slower, 13.6-13.8 against 12.2 us).
 constexpr int kDecStagesDeep = 8;
 constexpr int kDeepMaxFrags = 1;
+constexpr int kBand = 128;                    // bytes of each weight row per stage and wave
+constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
 // Reduced output fragments a wave keeps in registers until its copies are
 // done.  A store issued inside the stream would sit among the copies in the
 // in-order vector-memory counter and make the next stage waits of that wave
@@ -75,31 +78,41 @@ struct DecArgs {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// KW: MFMAs (128 k each) per wave per fragment, K / 1024.  MB: blocks of 16
-// activation rows (M <= 16 MB); each weight operand read from LDS feeds one
-// MFMA per block, so the weight stream is the same for every MB.
-// Bytes of each weight row per stage and wave: 128, or 64 for E2M1 weights
-// when a wave's KW operands of 64 bytes do not pair up.
-constexpr int band_bytes(bool bf4, int kw) { return (bf4 && kw % 2 == 1) ? 64 : 128; }
+// K / 1024 = KW MFMAs (128 k each) per wave per fragment on average.  With
+// E2M1 weights (64 bytes per MFMA operand, two per 128-byte stage) and KW
+// odd, waves 0-3 take KW + 1 MFMAs and waves 4-7 KW - 1.
+constexpr bool split_k(bool bf4, int kw) { return bf4 && kw % 2 == 1; }
 
-template <bool BF4, int KW, int MB, int D_>
+// LDS of one wave's ring and scale slots for WK MFMAs per fragment
+constexpr int ring_bytes(bool bf4, int wk, int d) {
+  const int nq = bf4 ? wk / 2 : wk;
+  const int nsi = (16 * wk + 63) / 64;
+  const int nsl = (nq - 1 + d + nq - 1) / nq;
+  return d * kStageBytes + nsl * nsi * 256;
+}
+
+// KW: K / 1024; XK: this wave's MFMAs per fragment are WK = KW + XK (XK = +1
+// for waves 0-3 and -1 for waves 4-7 under the uneven split, else 0).  MB:
+// blocks of 16 activation rows (M <= 16 MB); each weight operand read from
+// LDS feeds one MFMA per block, so the weight stream is the same for every MB.
+template <bool BF4, int KW, int MB, int D_, int XK>
 struct Decode {
   static constexpr int D = D_;
-  static constexpr int BAND = band_bytes(BF4, KW);
-  static constexpr int STAGE = 16 * BAND;                // one stage: 16 rows
-  static constexpr int LPB = BAND / 16;                  // copy lanes per stage row (16 bytes each)
-  static constexpr int RPC = 64 / LPB;                   // stage rows per copy instruction
-  static constexpr int CPS = 16 / RPC;                   // copy instructions per stage
-  static constexpr int MPS = BF4 ? BAND / 64 : 1;        // MFMAs per stage
-  static constexpr int NQ = KW / MPS;                    // stages per fragment
-  static constexpr int WB = BF4 ? KW * 64 : KW * 128;    // bytes of a weight row per wave
-  static constexpr int SBW = 4 * KW;                     // scale bytes of a row per wave
+  static constexpr int WK = KW + XK;                     // MFMAs per fragment of this wave
+  static constexpr int MPS = BF4 ? 2 : 1;                // MFMAs per stage (128 bytes of a row)
+  static constexpr int NQ = WK / MPS;                    // stages per fragment
+  static constexpr int OPB = BF4 ? 64 : 128;             // bytes of a weight row per MFMA
+  static constexpr int SBW = 4 * WK;                     // scale bytes of a row per wave
   static constexpr int LPR = SBW / 4;                    // scale copy lanes per row (4 bytes each)
   static constexpr int NSI = (16 * LPR + 63) / 64;       // scale copies per fragment
   // scale slots: a fragment's slot is refilled only after its last stage
   static constexpr int NSL = (NQ - 1 + D + NQ - 1) / NQ;
   static constexpr int SZ_SC = NSI * 256;
-  static constexpr int SZ_WAVE = D * STAGE + NSL * SZ_SC;
+  // every wave's region has the size of the larger wave kind's
+  static constexpr int SZ_WAVE = XK == 0 ? ring_bytes(BF4, WK, D)
+                                         : (ring_bytes(BF4, KW + 1, D) > ring_bytes(BF4, KW - 1, D)
+                                                ? ring_bytes(BF4, KW + 1, D)
+                                                : ring_bytes(BF4, KW - 1, D));
   static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
   static constexpr int SZ_PSLOT = MB * kDecWaves * 64 * 16;  // one fragment's partials
   static constexpr int LDS = OFF_PART + 2 * SZ_PSLOT;
@@ -109,13 +122,15 @@ struct Decode {
   static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8, NS4 = (SBW % 8) / 4;
   static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
-  static_assert(NQ >= 1 && KW % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
+  static_assert(NQ >= 1 && WK % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
+  static_assert(ring_bytes(BF4, WK, D) == D * kStageBytes + NSL * SZ_SC && SZ_WAVE >= ring_bytes(BF4, WK, D),
+                "region layout");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
-  static_assert(MB >= 1 && MB * KW <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
-  static_assert(STAGE == CPS * 1024, "whole copy instructions per stage");
+  static_assert(MB >= 1 && MB * WK <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
+  static_assert(XK == 0 || split_k(BF4, KW), "uneven split only for E2M1 weights with K / 1024 odd");
 
-  // physical 16-byte chunk of logical chunk c in stage row r: c ^ swz(r)
-  static __device__ __forceinline__ int swz(int r) { return BAND == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
+  // first MFMA (128 k) of wave w's band: w KW, shifted by the uneven split
+  static __device__ __forceinline__ int band_start(int w) { return w * KW + (XK > 0 ? w : XK < 0 ? 8 - w : 0); }
 
   // fp8 operand of the MFMA covering k0 .. k0+127 of row `p` (p at k0):
   // lane group g holds k0 + 16g .. +15 and k0 + 64 + 16g .. +15
@@ -147,14 +162,15 @@ struct Decode {
     uint8_t* smem;  // workgroup LDS
     uint8_t* wsm;   // this wave's ring and scale slots
     int lane, wave, g, r;
+    int kb;               // this wave's first MFMA in a row: k = 128 kb
     int f_begin, nf;
     uint32_t rb, nb;      // bytes per B row, scale bytes per row
-    int brow;             // lane's row in a copy of RPC rows
-    uint32_t bch[CPS];    // lane's swizzled chunk offset in each copy of a stage
+    int brow;             // lane's row in a copy of 8 rows
+    uint32_t bch[2];      // lane's swizzled chunk offset, rows 0-7 / 8-15
     int srow[NSI];        // lane's row in each scale copy
     uint32_t scol[NSI];   // and its byte in that row's band
-    v8i av[MB][KW];       // A operands of this wave's MFMAs, per row block
-    uint32_t sa[MB][KW];  // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
+    v8i av[MB][WK];       // A operands of this wave's MFMAs, per row block
+    uint32_t sa[MB][WK];  // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
     v4f acc[MB][MPS];
     v4f held[HELD][MB];   // reduced fragments w, w + 8, ..., stored at the end
   };
@@ -164,11 +180,11 @@ struct Decode {
   static constexpr int la(int q) { return MB * 2 * MPS; }
   static constexpr int la_from(int q) { return q >= NQ ? 0 : la(q) + la_from(q + 1); }
   // Copies issued after stage s's copies and before its wait: the copies of
-  // stages s+1 .. s+D-2 (CPS weight copies each, plus the scale copies at
-  // every fragment start) and, in the first fragment, the A loads of stages
+  // stages s+1 .. s+D-2 (2 weight copies each, plus the scale copies at every
+  // fragment start) and, in the first fragment, the A loads of stages
   // q .. NQ-1 issued by the prologue after stage q's copies.
   static constexpr int younger(int q, bool first) {
-    return CPS * (D - 2) + NSI * ((q + D - 2) / NQ) + (first && q <= D - 2 ? la_from(q) : 0);
+    return 2 * (D - 2) + NSI * ((q + D - 2) / NQ) + (first && q <= D - 2 ? la_from(q) : 0);
   }
 
   template <int N>
@@ -205,25 +221,25 @@ struct Decode {
     if (q == 0) {
       const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * t.nb), 0, 16 * t.nb,
                                                           kRsrcWord3);
-      uint8_t* sc = t.wsm + D * STAGE + (fs % NSL) * SZ_SC;
+      uint8_t* sc = t.wsm + D * kStageBytes + (fs % NSL) * SZ_SC;
 #pragma unroll
       for (int i = 0; i < NSI; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(sc + i * 256), 4,
                                                  (uint32_t)min(t.srow[i], last) * t.nb + t.scol[i],
-                                                 (uint32_t)(t.wave * SBW), 0, kStreamPolicy);
+                                                 (uint32_t)(4 * t.kb), 0, kStreamPolicy);
     }
     const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * t.rb), 0, 16 * t.rb, kRsrcWord3);
-    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * STAGE;
-    const uint32_t soff = (uint32_t)(t.wave * WB + qv * BAND);
+    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * kStageBytes;
+    const uint32_t soff = (uint32_t)(t.kb * OPB + qv * kBand);
 #pragma unroll
-    for (int h = 0; h < CPS; h++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * RPC * BAND), 16,
-                                               (uint32_t)min(t.brow + RPC * h, last) * t.rb + t.bch[h], soff, 0,
+    for (int h = 0; h < 2; h++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), 16,
+                                               (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0,
                                                kStreamPolicy);
   }
 
   // A operands for stage q of this wave (rows clamped to M-1; rows >= M are
-  // computed and discarded): wave MFMA j = q * MPS + u covers k 128 (w KW + j)
+  // computed and discarded): wave MFMA j = q * MPS + u covers k 128 (kb + j)
   // .. +127.
   template <int Q>
   static __device__ __forceinline__ void load_a(State& t) {
@@ -231,21 +247,21 @@ struct Decode {
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       const int m = min(16 * mb + t.r, a.M - 1);
-      const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.wave * KW * 128;
+      const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.kb * 128;
 #pragma unroll
       for (int u = 0; u < MPS; u++) t.av[mb][Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
     }
   }
 
   // A scales of this wave: MFMA j takes byte g of the dword of blocks
-  // 4 (w KW + j) .. +3.  The dwords stay raw until the MFMA: extracting a byte
+  // 4 (kb + j) .. +3.  The dwords stay raw until the MFMA: extracting a byte
   // here would wait for these loads before the first copy is issued.
   static __device__ __forceinline__ void load_a_scales(State& t) {
     const DecArgs& a = *t.a;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       const int m = min(16 * mb + t.r, a.M - 1);
-      const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.wave * SBW;
+      const uint8_t* srow = a.SA + (int64_t)m * t.nb + t.kb * 4;
 #pragma unroll
       for (int i = 0; i < NS16; i++) {
         const v4i d = *reinterpret_cast<const v4i*>(srow + 16 * i);
@@ -257,7 +273,7 @@ struct Decode {
         t.sa[mb][4 * NS16] = (uint32_t)d[0];
         t.sa[mb][4 * NS16 + 1] = (uint32_t)d[1];
       }
-      if constexpr (NS4 == 1) t.sa[mb][KW - 1] = *reinterpret_cast<const uint32_t*>(srow + SBW - 4);
+      if constexpr (NS4 == 1) t.sa[mb][WK - 1] = *reinterpret_cast<const uint32_t*>(srow + SBW - 4);
     }
   }
 
@@ -265,6 +281,9 @@ struct Decode {
   // A(p), for p = 0 ..; stages up to D - 2, A up to NQ - 1.
   template <int... P>
   static __device__ __forceinline__ void prologue(State& t, std::integer_sequence<int, P...>) {
+    // an assembly comment naming the counted loads, for the static check of
+    // the compiled code
+    asm volatile("; decode prologue wk=%0 mb=%1" ::"i"(WK), "i"(MB));
     load_a_scales(t);
     order_fence();
     (
@@ -292,20 +311,20 @@ struct Decode {
       wait_stage<0>();
     // stage s + D - 1, into the buffer read at stage s - 1
     issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ, FIRST);
-    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * STAGE;
-    const uint8_t* sc = t.wsm + D * STAGE + (f % NSL) * SZ_SC;
+    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * kStageBytes;
+    const uint8_t* sc = t.wsm + D * kStageBytes + (f % NSL) * SZ_SC;
     const int g = t.g, r = t.r;
-    const int sw = swz(r);
+    const int sw = (r >> 1) & 7;
 #pragma unroll
     for (int u = 0; u < MPS; u++) {
       const int j = Q * MPS + u;  // this wave's MFMA index inside the fragment
       v8i bv;
       if (BF4) {
-        const v4i lo = *reinterpret_cast<const v4i*>(st + r * BAND + (((4 * u + g) ^ sw) << 4));
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 * u + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
       } else {
-        const v4i lo = *reinterpret_cast<const v4i*>(st + r * BAND + ((g ^ sw) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(st + r * BAND + (((4 + g) ^ sw) << 4));
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + ((g ^ sw) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       const int sb = sc[r * SBW + 4 * j + g];
@@ -349,8 +368,7 @@ struct Decode {
     }
   }
 
-  static __device__ __forceinline__ void run(const DecArgs& a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  static __device__ __forceinline__ void run(const DecArgs& a, uint8_t* smem) {
     State t;
     t.a = &a;
     t.smem = smem;
@@ -358,6 +376,7 @@ struct Decode {
     t.lane = tid & 63;
     t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     t.wsm = smem + t.wave * SZ_WAVE;
+    t.kb = band_start(t.wave);
     t.g = t.lane >> 4;
     t.r = t.lane & 15;
     // balanced contiguous split of the fragments over the workgroups (each
@@ -366,11 +385,11 @@ struct Decode {
     t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
     t.rb = BF4 ? (uint32_t)(a.K >> 1) : (uint32_t)a.K;
     t.nb = (uint32_t)(a.K >> 5);
-    // copy h, lane l: stage row l / LPB + RPC h, physical chunk l % LPB
-    // holding logical chunk (l % LPB) ^ swz(row)
-    t.brow = t.lane / LPB;
+    // copy lane l: row l >> 3 (+8), physical chunk l & 7 holding logical chunk
+    // (l & 7) ^ ((row >> 1) & 7)
+    t.brow = t.lane >> 3;
 #pragma unroll
-    for (int h = 0; h < CPS; h++) t.bch[h] = (uint32_t)(((t.lane % LPB) ^ swz(t.brow + RPC * h)) * 16);
+    for (int h = 0; h < 2; h++) t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * 16);
     // scale copy i, lane l: entry e = 64 i + l is row e / LPR, dword e % LPR
     // (entries past row 15 repeat row 15 into the slot's unused tail)
 #pragma unroll
@@ -401,16 +420,26 @@ struct Decode {
   }
 };
 
+// the kernel's layout (the same for both wave kinds of an uneven split)
+template <bool BF4, int KW, int MB, int D>
+using DecLayout = Decode<BF4, KW, MB, D, split_k(BF4, KW) ? 1 : 0>;
+
 template <bool BF4, int KW, int MB, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void decode_kernel(DecArgs a) {
-  static_assert(Decode<BF4, KW, MB, D>::FITS, "fits the 160 KiB LDS of a gfx950 CU");
-  Decode<BF4, KW, MB, D>::run(a);
+  static_assert(DecLayout<BF4, KW, MB, D>::FITS, "fits the 160 KiB LDS of a gfx950 CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DecLayout<BF4, KW, MB, D>::LDS];
+  if constexpr (split_k(BF4, KW)) {
+    static_assert(Decode<BF4, KW, MB, D, 1>::LDS == Decode<BF4, KW, MB, D, -1>::LDS, "one layout");
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+      Decode<BF4, KW, MB, D, 1>::run(a, smem);
+    else
+      Decode<BF4, KW, MB, D, -1>::run(a, smem);
+  } else {
+    Decode<BF4, KW, MB, D, 0>::run(a, smem);
+  }
 }
 
-// Ring depth in stages: the same bytes in flight for 64-byte stages.
-constexpr int ring(bool bf4, int kw, int depth) { return depth * (128 / band_bytes(bf4, kw)); }
-
-template <bool BF4, int KW, int MB, int D = ring(BF4, KW, kDecStages)>
+template <bool BF4, int KW, int MB, int D = kDecStages>
 hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   const int grid = a.nfrags < cus ? a.nfrags : cus;
   hipLaunchKernelGGL((decode_kernel<BF4, KW, MB, D>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
@@ -425,9 +454,8 @@ template <bool BF4, int KW>
 hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
   if (a.M <= 16 || max_blocks(KW) == 1) {
     // few weight fragments per CU: the ring covers a whole fragment
-    constexpr int deep = ring(BF4, KW, kDecStagesDeep);
-    if constexpr (Decode<BF4, KW, 1, deep>::FITS) {
-      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<BF4, KW, 1, deep>(a, cus, stream);
+    if constexpr (DecLayout<BF4, KW, 1, kDecStagesDeep>::FITS) {
+      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<BF4, KW, 1, kDecStagesDeep>(a, cus, stream);
     }
     return launch_dec<BF4, KW, 1>(a, cus, stream);
   }

@@ -209,9 +209,9 @@ def test_mx_blockpow2_recipe_full():
 # and 4 row blocks with a partly filled last block, and the later launches
 # (M = 33, 64 at K = 8192; 40 at 6144; 20 at 12288; 64 at 10240; 33 at 5120;
 # 64 at 7168); K = 6144 .. 16384 cover every register budget.  K / 1024 odd
-# (3072 .. 15360) gives E2M1 weights 64-byte stages and a ring twice as deep,
-# and E4M3 weights an odd number of 128-byte stages, both with a 4-byte A
-# scale remainder per wave.  K = 14336 and 16384 with E4M3 weights, 4608 and
+# (3072 .. 15360) splits K unevenly for E2M1 weights (waves 0-3 one MFMA
+# more, waves 4-7 one less) and gives E4M3 weights an odd number of stages,
+# with a 4-byte A scale remainder per wave.  K = 14336 and 16384 with E4M3 weights, 4608 and
 # 1536 take the split-K skinny kernel instead.
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (7, 1000, 1536), (16, 1001, 4608), (13, 250, 8192),

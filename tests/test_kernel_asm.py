@@ -108,27 +108,42 @@ def test_kernel_source_is_hazard_free(src):
 def test_decode_kernel_first_wait_counts_the_issued_loads():
     """The decode kernel's stage waits count the vector-memory instructions
     issued after a stage's copies; in the first fragment these include the
-    A operand loads of the prologue, 2 KW per row block (the lo and hi
-    halves of each MFMA operand).  The A scales are loaded before the first
-    copy, so that however the compiler merges those loads they are never
-    among the counted ones.  Between the first copy and the first wait the
-    compiler must issue exactly the counted global loads, or the wait lets a
-    stage's copies still be in flight."""
+    A operand loads of the prologue, 2 WK per row block (the lo and hi
+    halves of each of the wave's WK MFMA operands).  The A scales are loaded
+    before the first copy, so that however the compiler merges those loads
+    they are never among the counted ones.  Between the first copy and the
+    first wait the compiler must issue exactly the counted global loads, or
+    the wait lets a stage's copies still be in flight.  With E2M1 weights and
+    K / 1024 odd the kernel has two wave kinds (WK = KW + 1 for waves 0-3,
+    KW - 1 for waves 4-7) behind one branch on the wave index; the prologue
+    of each kind starts at an assembly comment that names WK and MB."""
     import re
     from block_scaled_precision_mxgemm_amd import build as B
     asm = H.compile_to_asm(os.path.join(ROOT, "block_scaled_precision_mxgemm_amd", "csrc", "gemm_decode.hip"),
                            B.FLAGS, B.HIPCC)
-    seen = 0
+
+    seen = split = 0
     for m in re.finditer(r"^(_ZN3mxg12_GLOBAL__N_113decode_kernelILb([01])ELi(\d+)ELi(\d+)ELi(\d+)EEEv\S*):", asm,
                          re.M):
-        kw, mb = int(m.group(3)), int(m.group(4))
+        name, bf4, kw, mb = m.group(1), m.group(2) == "1", int(m.group(3)), int(m.group(4))
         body = asm[m.end():asm.index(".Lfunc_end", m.end())]
-        first_wait = re.search(r"s_waitcnt vmcnt\(", body)
-        first_copy = re.search(r"^\s*buffer_load_dwordx4 .* lds", body, re.M)
-        assert first_wait and first_copy and first_copy.start() < first_wait.start(), m.group(1)
-        scales = re.findall(r"^\s*global_load_\w+", body[:first_copy.start()], re.M)
-        assert 1 <= len(scales) <= mb * kw, (m.group(1), len(scales))
-        loads = re.findall(r"^\s*global_load_\w+", body[first_copy.start():first_wait.start()], re.M)
-        assert len(loads) == mb * 2 * kw, (m.group(1), len(loads), mb * 2 * kw)
+        # the prologue of each wave kind starts at its marker comment
+        wks = []
+        for p in re.finditer(r"; decode prologue wk=(\d+) mb=(\d+)", body):
+            wk = int(p.group(1))
+            assert int(p.group(2)) == mb, name
+            part = body[p.end():]
+            first_wait = re.search(r"s_waitcnt vmcnt\(", part)
+            first_copy = re.search(r"^\s*buffer_load_dwordx4 .* lds", part, re.M)
+            assert first_wait and first_copy and first_copy.start() < first_wait.start(), name
+            assert re.search(r"^\s*global_load_\w+", part[:first_copy.start()], re.M), name   # the A scales
+            loads = re.findall(r"^\s*global_load_\w+", part[first_copy.start():first_wait.start()], re.M)
+            assert len(loads) == mb * 2 * wk, (name, wk, len(loads), mb * 2 * wk)
+            wks.append(wk)
+        if bf4 and kw % 2 == 1:
+            assert sorted(set(wks)) == [kw - 1, kw + 1], (name, wks)
+            split += 1
+        else:
+            assert set(wks) == {kw}, (name, wks)
         seen += 1
-    assert seen >= 60
+    assert seen >= 60 and split >= 12
