@@ -53,7 +53,7 @@ int validate_epi(const float* bias, int act, int out_type) {
 // E4M3 or E2M1 weights), or the tiled / ping-pong kernels (every format pair).
 int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
            int64_t N, int64_t K, int fmt, hipStream_t st) {
-  if (mxg::decode_ok(M, K, fmt, SA, SB)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
+  if (mxg::decode_ok(M, K, fmt, SA, SB, e)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
   if (M <= mxg::kSkinnyMaxM && (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4))
     return to_status(mxg::launch_mx_skinny(A, SA, B, SB, e, M, N, K, fmt, st));
   return to_status(mxg::launch_mx_tiled(A, SA, B, SB, e, M, N, K, fmt, st));

@@ -67,12 +67,14 @@ constexpr int kHeld = 4;
 constexpr int kStreamPolicy = 2;
 
 struct DecArgs {
-  const uint8_t* A;
+  const uint8_t* A;   // at this launch's first row and K chunk
   const uint8_t* SA;
-  const uint8_t* B;
+  const uint8_t* B;   // at this launch's K chunk
   const uint8_t* SB;
   Epi e;       // output: C (this launch's first row), bias, activation, element type
-  int M, N, K;
+  int M, N, K; // K: this launch's chunk of the reduction
+  int ldk;     // the whole K: the row strides of A, B and the scale planes follow it
+  int accum;   // 1: fp32 C already holds the sum over earlier K chunks; add to it
   int nfrags;  // ceil(N / 16)
 };
 
@@ -153,7 +155,19 @@ struct Decode {
   static __device__ __forceinline__ void store_c(const DecArgs& a, int frag, int mb, v4f s, int g, int r) {
     const int m = 16 * mb + r;
     const int n = frag * 16 + 4 * g;
-    if (m < a.M) epi_store4<false>(a.e, a.N, m, n, s, (a.N & 3) == 0 && n + 3 < a.N);
+    if (m >= a.M) return;
+    const bool vec = (a.N & 3) == 0 && n + 3 < a.N;
+    if (a.accum) {
+      const float* prev = reinterpret_cast<const float*>(a.e.C) + (int64_t)m * a.N + n;
+      if (vec) {
+        s += *reinterpret_cast<const v4f*>(prev);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (n + i < a.N) s[i] += prev[i];
+      }
+    }
+    epi_store4<false>(a.e, a.N, m, n, s, vec);
   }
 
   // Per-wave state (all in registers once inlined).
@@ -247,7 +261,7 @@ struct Decode {
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       const int m = min(16 * mb + t.r, a.M - 1);
-      const uint8_t* row = a.A + (int64_t)m * a.K + (int64_t)t.kb * 128;
+      const uint8_t* row = a.A + (int64_t)m * a.ldk + (int64_t)t.kb * 128;
 #pragma unroll
       for (int u = 0; u < MPS; u++) t.av[mb][Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
     }
@@ -383,8 +397,8 @@ struct Decode {
     // has at least one: the grid is at most the fragment count)
     t.f_begin = (int)((int64_t)a.nfrags * blockIdx.x / gridDim.x);
     t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
-    t.rb = BF4 ? (uint32_t)(a.K >> 1) : (uint32_t)a.K;
-    t.nb = (uint32_t)(a.K >> 5);
+    t.rb = BF4 ? (uint32_t)(a.ldk >> 1) : (uint32_t)a.ldk;
+    t.nb = (uint32_t)(a.ldk >> 5);
     // copy lane l: row l >> 3 (+8), physical chunk l & 7 holding logical chunk
     // (l & 7) ^ ((row >> 1) & 7)
     t.brow = t.lane >> 3;
@@ -489,10 +503,19 @@ hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream, std::inte
 // 33 .. 64 rows: 2 x 26-29 us, against 110-128 us for the split-K kernel).
 int64_t rows_per_launch(int64_t K) { return 16 * max_blocks((int)(K / 1024)); }
 
+// Longest K taken (in chunks above the per-launch range).
+constexpr int64_t kDecMaxK = 131072;
+
+// K / 1024 of chunk i of P: as equal as whole multiples of 1024 allow
+int chunk_kw(int kw, int P, int i) { return kw / P + (i < kw % P ? 1 : 0); }
+
 }  // namespace
-bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB) {
-  return M <= 64 && (fmt == 0 || fmt == 1) && (K % 1024) == 0 && K >= 2048 && K <= 1024 * max_kw(fmt == 1) &&
-         (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0;
+bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB, const Epi& e) {
+  if (!(M <= 64 && (fmt == 0 || fmt == 1) && (K % 1024) == 0 && K >= 2048 && (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0))
+    return false;
+  // above one launch's K range the running sum is kept in C between chunks,
+  // which needs fp32 output
+  return K <= 1024 * max_kw(fmt == 1) || (e.out == kOutF32 && K <= kDecMaxK);
 }
 
 hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
@@ -502,21 +525,44 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
   if (cus <= 0) cus = 1;
-  const int64_t step = rows_per_launch(K);
+  const int kw = (int)(K / 1024);
+  int P = 1;                               // K chunks
+  int64_t step = rows_per_launch(K);       // rows per launch
+  if (e.out == kOutF32) {
+    // fp32 C: one launch per K chunk covers all M rows, so that B streams
+    // once; the chunks are the fewest whose A operands fit beside M / 16 row
+    // blocks.  The first chunk writes C, each later one adds its partial sum,
+    // and only the last applies bias and activation; the order is fixed, so
+    // the result is deterministic.
+    const int blocks = (int)((M + 15) / 16);
+    const int limit = blocks <= 1 ? max_kw(fmt == 1) : blocks <= 2 ? 8 : 4;  // max_blocks(KW) >= the blocks
+    P = (kw + limit - 1) / limit;
+    step = 64;
+  }
+  // (16-bit C: each launch takes all of K, which decode_ok keeps in range,
+  // and launches of fewer rows stream B again)
+  const int64_t wbytes = fmt == 1 ? 2 : 1;  // K elements per weight byte
   for (int64_t m0 = 0; m0 < M && err == hipSuccess; m0 += step) {
-    DecArgs a{};
-    a.A = (const uint8_t*)A + m0 * K;  // E4M3 activations: one byte per element
-    a.SA = SA + m0 * (K / 32);
-    a.B = (const uint8_t*)B;
-    a.SB = SB;
-    a.e = e;
-    a.e.C = (uint8_t*)e.C + m0 * N * epi_elem_bytes(e.out);
-    a.M = (int)(M - m0 < step ? M - m0 : step);
-    a.N = (int)N;
-    a.K = (int)K;
-    a.nfrags = (int)((N + 15) / 16);
-    const auto kws = std::make_integer_sequence<int, 15>{};  // K / 1024 = 2 .. 16
-    err = fmt == 1 ? launch_dec_k<true>(a, cus, stream, kws) : launch_dec_k<false>(a, cus, stream, kws);
+    int64_t k0 = 0;
+    for (int c = 0; c < P && err == hipSuccess; c++) {
+      const int64_t kc = 1024 * (int64_t)chunk_kw(kw, P, c);
+      DecArgs a{};
+      a.A = (const uint8_t*)A + m0 * K + k0;  // E4M3 activations: one byte per element
+      a.SA = SA + m0 * (K / 32) + k0 / 32;
+      a.B = (const uint8_t*)B + k0 / wbytes;
+      a.SB = SB + k0 / 32;
+      a.e = c == P - 1 ? e : Epi{e.C, nullptr, kOutF32, kActNone};
+      a.e.C = (uint8_t*)e.C + m0 * N * epi_elem_bytes(e.out);
+      a.M = (int)(M - m0 < step ? M - m0 : step);
+      a.N = (int)N;
+      a.K = (int)kc;
+      a.ldk = (int)K;
+      a.accum = c > 0;
+      a.nfrags = (int)((N + 15) / 16);
+      const auto kws = std::make_integer_sequence<int, 15>{};  // K / 1024 = 2 .. 16
+      err = fmt == 1 ? launch_dec_k<true>(a, cus, stream, kws) : launch_dec_k<false>(a, cus, stream, kws);
+      k0 += kc;
+    }
   }
   return err;
 }

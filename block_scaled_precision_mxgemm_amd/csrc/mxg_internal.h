@@ -41,10 +41,11 @@ hipError_t launch_mx_pp128(const void* A, const uint8_t* SA, const void* B, cons
 hipError_t launch_f16_pp128(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream);
 
-// Decode kernel for M <= 64 (MX fp8 x fp8 or fp8 x fp4): K one of 2048,
-// 4096, 8192 (A's k range per wave is held in registers), 4-byte aligned
-// scale planes.
-bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB);
+// Decode kernel for M <= 64 (MX fp8 x fp8 or fp8 x fp4): K a multiple of
+// 1024 from 2048 (A's k range per wave is held in registers, which bounds one
+// launch's K; longer K runs in chunks that add into an fp32 C), 4-byte
+// aligned scale planes.
+bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB, const Epi& e);
 hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                             int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
 

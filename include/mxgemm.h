@@ -118,10 +118,13 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * Each 32-element block product is formed by CDNA4's scaled fp8/fp4 MFMA,
  * which applies the E8M0 scales itself; partial sums accumulate in fp32.
  * Decode shapes with E4M3 activations and E4M3 or E2M1 weights take
- * weight-streaming kernels: for K a multiple of 1024 from 2048 up to 16384
- * (E2M1 weights) or 12288 (E4M3 weights) and M <= 64 one that reads B once per
- * launch (one launch per 64, 32 or 16 rows for K <= 4096, <= 8192, above),
- * for other small M (M <= 64) a split-K kernel.
+ * weight-streaming kernels: for M <= 64 and K a multiple of 1024 from 2048,
+ * one that reads B once per launch (fp32 C: all rows per launch, K in chunks
+ * of up to 16384 (E2M1 weights) or 12288 (E4M3 weights), fewer as M grows,
+ * each chunk adding into C, K up to 131072; 16-bit C through
+ * mxgemm_run_fused: all of K per launch, K up to 16384 / 12288, one launch per
+ * 64, 32 or 16 rows for K <= 4096, <= 8192, above); for other small M
+ * (M <= 64) a split-K kernel.
  * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the
  * workloads this library is tested on; the MFMA's internal alignment of
  * wide-range products within one instruction is the dominant error term.

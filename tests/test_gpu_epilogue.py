@@ -9,7 +9,9 @@ epilogue fused into every MX GEMM kernel (bias, GELU, fp32 / bf16 / fp16 C).
 * The fused GEMM must equal mxgemm_run followed by mxgemm_epilogue bit for bit
   (the same fp32 accumulators through the same device arithmetic), and match
   the oracle through epilogue_gate; with no bias, no activation and fp32
-  output it must equal mxgemm_run.
+  output it must equal mxgemm_run.  (Exception: decode shapes that the fp32
+  path splits into K chunks take another schedule for 16-bit outputs; those
+  are held to the oracle only.)
 """
 import numpy as np
 import pytest
@@ -109,13 +111,16 @@ def test_epilogue_gelu_against_oracle(out_type):
 # 128 x 128 tiled kernel (ragged), a ragged shape with
 # >= 256 tiles (plain fp32 takes the 256 x 256 tiled kernel, a general
 # epilogue the 128 x 128 one), the decode kernel (1, 3 row blocks; two
-# launches at K = 8192) and the split-K skinny kernel.
+# K chunks at K = 8192 for 33 rows, 20480 and, with E4M3 weights, 14336,
+# where 16-bit outputs take two row launches or the split-K kernel instead)
+# and the split-K skinny kernel.
 CASES = [("mxfp8_8192", 4096, 4096, 256, 0, 20000), ("mxfp8_2048", 4096, 4352, 256, 2, 20000),
          ("mxfp8_2048", 512, 640, 384, 0, None), ("mxfp8_2048", 512, 640, 384, 4, None),
          ("mxfp8_2048", 300, 257, 512, 0, None), ("prefill_8192x14336x4096", 520, 530, 1056, 1, None),
          ("mxfp8_2048", 4100, 4100, 128, 0, 20000), ("decode_16x28672x8192", 16, 1000, 2048, 1, None),
          ("decode_16x28672x8192", 48, 1000, 4096, 0, None), ("decode_16x28672x8192", 33, 1001, 8192, 1, None),
-         ("decode_16x28672x8192", 40, 512, 1536, 0, None), ("decode_16x28672x8192", 7, 1003, 1536, 1, None)]
+         ("decode_16x28672x8192", 40, 512, 1536, 0, None), ("decode_16x28672x8192", 7, 1003, 1536, 1, None),
+         ("decode_16x28672x8192", 17, 1001, 20480, 1, None), ("decode_16x28672x8192", 16, 600, 14336, 0, None)]
 
 EPILOGUES = [(True, oracle.ACT_GELU, oracle.OUT_BF16), (True, oracle.ACT_NONE, oracle.OUT_F16),
              (False, oracle.ACT_GELU, oracle.OUT_F32), (True, oracle.ACT_GELU, oracle.OUT_F16)]
@@ -149,13 +154,23 @@ def test_fused_gemm(name, M, N, K, fmt, npts):
         I, J = mxin.sample_points(M, N, npts)
         ref, ab = oracle.mx_gemm(qa_o, sa_o, ea, qb_o, sb_o, eb, M, N, K, points=(I, J))
     extra = MFMA_ALIGNMENT_TERMS
+    # With fp32 C the decode kernel covers all M rows in one launch per K
+    # chunk, as many chunks as the A operands of M / 16 row blocks need, and
+    # keeps the running sum in C; a 16-bit C takes all of K per launch (fewer
+    # rows each) or, beyond one launch's K, the split-K kernel.  Where fp32
+    # C needs several chunks, the two sum in another order (both are checked
+    # against the oracle).
+    blocks = (M + 15) // 16
+    limit = (16 if fmt == 1 else 12) if blocks <= 1 else 8 if blocks <= 2 else 4
+    chunked = fmt in (0, 1) and M <= 64 and K % 1024 == 0 and K >= 2048 and K // 1024 > limit
     for use_bias, act, out_type in EPILOGUES:
         bb = bias if use_bias else None
         fused = b.mxgemm_run_fused(qa, sa, qb, sb, fmt, bias=bb, act=act, out_type=out_type)
         dec = b.mxgemm_epilogue(plain, bb, act, out_type)
         torch.cuda.synchronize()
-        assert np.array_equal(_bits(fused), _bits(dec)), ("fused differs from the decomposed path", use_bias, act,
-                                                       out_type)
+        if not (chunked and out_type != oracle.OUT_F32):
+            assert np.array_equal(_bits(fused), _bits(dec)), ("fused differs from the decomposed path", use_bias,
+                                                           act, out_type)
         got = _vals(fused)[I, J]
         r = oracle.epilogue_gate(got, ref, ab, K, J, bias_np if use_bias else None, act, out_type,
                                  extra_terms=extra)

@@ -197,22 +197,25 @@ def test_mx_blockpow2_recipe_full():
     assert r["ok"], r
 
 
-# The decode kernel (K a multiple of 1024 from 2048 up to 16384 with E2M1
-# weights, up to 12288 with E4M3 weights; M <= 64 in 1, 2 or 4 blocks of 16
-# rows per launch, fewer blocks and more launches as K grows) gives each of
+# The decode kernel (K a multiple of 1024 from 2048 per launch up to 16384
+# with E2M1 weights, up to 12288 with E4M3 weights; M <= 64 in 1, 2 or 4
+# blocks of 16 rows per launch, fewer blocks as K grows) gives each of
 # its 8 waves one eighth of K and streams that band of 16-row weight fragments
 # through a per-wave LDS ring: N not a multiple of 16 (or of 4) exercises the
 # clamped last weight rows and the scalar output tail; one fragment per
 # workgroup (N = 16, 64, 250, 300: the ring's prologue runs past the last
 # stage) and several (N = 1001, 4165, 5000 and the full decode workload) cover
 # the ring, the scale slots and the partial-sum slots; M = 17 .. 64 covers 2
-# and 4 row blocks with a partly filled last block, and the later launches
-# (M = 33, 64 at K = 8192; 40 at 6144; 20 at 12288; 64 at 10240; 33 at 5120;
-# 64 at 7168); K = 6144 .. 16384 cover every register budget.  K / 1024 odd
+# and 4 row blocks with a partly filled last block, and K chunks (M = 33, 64
+# at K = 8192; 40 at 6144; 20 at 12288; 64 at 10240; 33 at 5120; 64 at 7168);
+# K = 6144 .. 16384 cover every register budget.  K / 1024 odd
 # (3072 .. 15360) splits K unevenly for E2M1 weights (waves 0-3 one MFMA
 # more, waves 4-7 one less) and gives E4M3 weights an odd number of stages,
-# with a 4-byte A scale remainder per wave.  K = 14336 and 16384 with E4M3 weights, 4608 and
-# 1536 take the split-K skinny kernel instead.
+# with a 4-byte A scale remainder per wave.  With fp32 C one launch per K
+# chunk covers all rows, the chunks being as many as the A operands of M / 16
+# row blocks need (33 .. 64 rows above K = 4096, 17 .. 32 above 8192, any M
+# above one launch's range: 14336 and 16384 with E4M3 weights, 17408 ..
+# 28672), each adding into C; 4608 and 1536 take the split-K skinny kernel.
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (7, 1000, 1536), (16, 1001, 4608), (13, 250, 8192),
                                    (16, 4165, 4096), (3, 64, 8192), (16, 16, 2048), (9, 5000, 8192),
@@ -223,7 +226,8 @@ def test_mx_blockpow2_recipe_full():
                                    (1, 300, 3072), (20, 250, 3072), (64, 1001, 3072), (16, 1001, 5120),
                                    (16, 5000, 5120), (33, 777, 5120), (17, 4165, 7168), (64, 300, 7168),
                                    (16, 1001, 9216), (20, 5000, 9216), (9, 700, 11264), (16, 1000, 13312),
-                                   (5, 4165, 15360)])
+                                   (5, 4165, 15360), (16, 1000, 16384), (33, 500, 17408), (16, 1001, 25600),
+                                   (64, 300, 28672)])
 def test_mx_gemm_decode_kernel_full(fmt, M, N, K):
     say("mx decode kernel", fmt, M, N, K)
     a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=7 * M + N + K + fmt)
