@@ -1,6 +1,7 @@
 // gemm_decode.hip - MX GEMM for decode shapes with few activation rows (M <= 64)
 // against a large weight matrix B (N x K, MXFP8 or MXFP4; K a multiple of 1024
-// from 2048 up to 12288 for MXFP8 and 16384 for MXFP4 weights).  The
+// from 2048; one launch takes up to 12288 of it with MXFP8 and 16384 with
+// MXFP4 weights, longer K runs in chunks that add into an fp32 C).  The
 // product is bound by the bytes of B, which must stream from HBM exactly
 // once; the weight plane is what quantization shrinks ("Metal tensors で
 // カスタム機械学習オペレーションを最適化する", section "主要内容": inference
@@ -189,10 +190,10 @@ struct Decode {
     v4f held[HELD][MB];   // reduced fragments w, w + 8, ..., stored at the end
   };
 
-  // Vector-memory instructions of the A loads that stage q of the first
-  // fragment needs: lo and hi halves per MFMA.
-  static constexpr int la(int q) { return MB * 2 * MPS; }
-  static constexpr int la_from(int q) { return q >= NQ ? 0 : la(q) + la_from(q + 1); }
+  // Vector-memory instructions of the A loads that one stage of the first
+  // fragment needs (lo and hi halves per MFMA), and those of stages q .. NQ-1.
+  static constexpr int la() { return MB * 2 * MPS; }
+  static constexpr int la_from(int q) { return q >= NQ ? 0 : la() + la_from(q + 1); }
   // Copies issued after stage s's copies and before its wait: the copies of
   // stages s+1 .. s+D-2 (2 weight copies each, plus the scale copies at every
   // fragment start) and, in the first fragment, the A loads of stages
