@@ -29,9 +29,9 @@
 //     (row >> 1) & 7 (applied on the global side, so the copy still writes LDS
 //     linearly), which makes the MFMA fragment reads conflict-free;
 //   * a fragment's 8 per-wave partial sums meet in LDS after one barrier per
-//     fragment; one wave adds them in a fixed order, so the result is
-//     deterministic and needs no atomics, and keeps the sum in registers: C
-//     is stored after the stream.
+//     fragment; one wave per 16-row block adds them in a fixed order, so the
+//     result is deterministic and needs no atomics, and keeps the sum in
+//     registers: C is stored after the stream.
 #include <utility>
 
 #include "mxg_device.h"
@@ -55,8 +55,8 @@ constexpr int kDecStagesDeep = 8;
 constexpr int kDeepMaxFrags = 1;
 constexpr int kBand = 128;                    // bytes of each weight row per stage and wave
 constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
-// Reduced output fragments a wave keeps in registers until its copies are
-// done.  A store issued inside the stream would sit among the copies in the
+// Reduced output blocks (16 x 16) a wave keeps in registers until its
+// copies are done.  A store issued inside the stream would sit among the copies in the
 // in-order vector-memory counter and make the next stage waits of that wave
 // also wait for the store and for one more stage; with the barrier per
 // fragment every wave would then lose that time.
@@ -123,13 +123,12 @@ struct Decode {
   // then 8 and 4 bytes for the rest.  They are issued before any copy, so
   // the stage waits never count them (the compiler may merge the small ones).
   static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8, NS4 = (SBW % 8) / 4;
-  static constexpr int HELD = kHeld / MB;                // reduced fragments kept in registers
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
   static_assert(NQ >= 1 && WK % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
   static_assert(ring_bytes(BF4, WK, D) == D * kStageBytes + NSL * SZ_SC && SZ_WAVE >= ring_bytes(BF4, WK, D),
                 "region layout");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
-  static_assert(MB >= 1 && MB * WK <= 16 && HELD >= 1, "A operands of all blocks in 128 VGPRs");
+  static_assert(MB >= 1 && MB * WK <= 16, "A operands of all blocks in 128 VGPRs");
   static_assert(XK == 0 || split_k(BF4, KW), "uneven split only for E2M1 weights with K / 1024 odd");
 
   // first MFMA (128 k) of wave w's band: w KW, shifted by the uneven split
@@ -187,7 +186,7 @@ struct Decode {
     v8i av[MB][WK];       // A operands of this wave's MFMAs, per row block
     uint32_t sa[MB][WK];  // their scale dwords (blocks 4j .. 4j+3); byte g is extracted at the MFMA
     v4f acc[MB][MPS];
-    v4f held[HELD][MB];   // reduced fragments w, w + 8, ..., stored at the end
+    v4f held[kHeld];      // reduced blocks u = w, w + 8, ... (u = MB f + mb), stored at the end
   };
 
   // Vector-memory instructions of the A loads that one stage of the first
@@ -367,15 +366,18 @@ struct Decode {
     // slot is written again two fragments later, after the next barrier,
     // which the reducing wave reaches only once it has read it
     wg_barrier();
-    if (t.wave == f % kDecWaves) {
-      const int j = f / kDecWaves;  // wave f % 8 reduces fragments f % 8 + 8j
+    // the MB row blocks of the fragment are reduced by MB different waves:
+    // block u = MB f + mb by wave u % 8, as its (u / 8)-th
 #pragma unroll
-      for (int mb = 0; mb < MB; mb++) {
+    for (int mb = 0; mb < MB; mb++) {
+      const int u = f * MB + mb;
+      if (t.wave == u % kDecWaves) {
         const v4f c = reduce(t.smem, f & 1, mb, t.lane);
-        if (j < HELD) {
+        const int j = u / kDecWaves;
+        if (j < kHeld) {
 #pragma unroll
-          for (int i = 0; i < HELD; i++)
-            if (i == j) t.held[i][mb] = c;
+          for (int i = 0; i < kHeld; i++)
+            if (i == j) t.held[i] = c;
         } else {
           store_c(*t.a, t.f_begin + f, mb, c, t.g, t.r);  // past the held ones: correct, with stricter waits
         }
@@ -424,12 +426,9 @@ struct Decode {
     fragment<true>(t, 0, std::make_integer_sequence<int, NQ>{});
     for (int f = 1; f < t.nf; f++) fragment<false>(t, f, std::make_integer_sequence<int, NQ>{});
 #pragma unroll
-    for (int i = 0; i < HELD; i++) {
-      const int f = t.wave + kDecWaves * i;
-      if (f < t.nf) {
-#pragma unroll
-        for (int mb = 0; mb < MB; mb++) store_c(a, t.f_begin + f, mb, t.held[i][mb], t.g, t.r);
-      }
+    for (int i = 0; i < kHeld; i++) {
+      const int u = t.wave + kDecWaves * i;
+      if (u / MB < t.nf) store_c(a, t.f_begin + u / MB, u % MB, t.held[i], t.g, t.r);
     }
     wait_vm<0>();  // no copy into LDS may still be in flight when the workgroup ends
   }
