@@ -56,12 +56,16 @@ def _mx_operands(name, M, N, K, fmt, seed):
     return qa, sa, qb, sb
 
 
-# ping-pong (256 tiles of 256 x 256), 128 x 128 tiled (ragged N), decode and
-# split-K skinny kernels
+# ping-pong (256 tiles of 256 x 256), 128 x 128 tiled (ragged N), decode
+# (one launch; two K chunks adding into C, for 40 rows at K = 8192 and for
+# K = 20480 / 14336 beyond one launch's range) and split-K skinny kernels
 @pytest.mark.parametrize("name,M,N,K,fmt", [("mxfp8_8192", 4096, 4096, 256, 0),
                                             ("mxfp8_2048", 512, 384, 512, 0),
                                             ("decode_16x28672x8192", 16, 1000, 2048, 1),
                                             ("decode_16x28672x8192", 48, 1000, 4096, 0),
+                                            ("decode_16x28672x8192", 40, 1000, 8192, 1),
+                                            ("decode_16x28672x8192", 16, 1000, 20480, 1),
+                                            ("decode_16x28672x8192", 16, 600, 14336, 0),
                                             ("decode_16x28672x8192", 40, 512, 1536, 0)])
 def test_mx_gemm_graph_replay(name, M, N, K, fmt):
     say("graph replay mx", name, M, N, K, fmt)
