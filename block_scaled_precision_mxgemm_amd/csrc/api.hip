@@ -54,8 +54,20 @@ int validate_epi(const float* bias, int act, int out_type) {
 int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
            int64_t N, int64_t K, int fmt, hipStream_t st) {
   if (mxg::decode_ok(M, K, fmt, SA, SB, e)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
-  if (M <= mxg::kSkinnyMaxM && (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4))
+  if (M <= mxg::kSkinnyMaxM && (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4)) {
+    // K not a multiple of 1024, up to 16 rows, fp32 C: the decode kernel
+    // takes the largest multiple of 1024 below K, the split-K kernel adds the
+    // rest (with more rows the split-K kernel alone measured faster at
+    // N = 4096)
+    const int64_t k1 = K - K % 1024;
+    const mxg::Epi plain{e.C, nullptr, mxg::kOutF32, mxg::kActNone};
+    if (M <= 16 && e.out == mxg::kOutF32 && mxg::decode_ok(M, k1, fmt, SA, SB, plain)) {
+      const hipError_t err = mxg::launch_mx_decode(A, SA, B, SB, plain, M, N, K, fmt, st, k1);
+      if (err != hipSuccess) return to_status(err);
+      return to_status(mxg::launch_mx_skinny(A, SA, B, SB, e, M, N, K, fmt, st, k1));
+    }
     return to_status(mxg::launch_mx_skinny(A, SA, B, SB, e, M, N, K, fmt, st));
+  }
   return to_status(mxg::launch_mx_tiled(A, SA, B, SB, e, M, N, K, fmt, st));
 }
 

@@ -519,15 +519,16 @@ bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* 
 }
 
 hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
-                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream, int64_t kn) {
+  if (kn < 0) kn = K;
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
   if (cus <= 0) cus = 1;
-  const int kw = (int)(K / 1024);
+  const int kw = (int)(kn / 1024);
   int P = 1;                               // K chunks
-  int64_t step = rows_per_launch(K);       // rows per launch
+  int64_t step = rows_per_launch(kn);      // rows per launch
   if (e.out == kOutF32) {
     // fp32 C: one launch per K chunk covers all M rows, so that B streams
     // once; the chunks are the fewest whose A operands fit beside M / 16 row

@@ -33,8 +33,10 @@ struct SkArgs {
   const uint8_t* B;
   const uint8_t* SB;
   Epi e;             // output: C, bias, activation, element type
-  int M, N, K;
+  int M, N, K;       // K: the k range of this launch (A, B and scales start at its first element)
   int64_t lda, ldb;  // row strides in bytes
+  int64_t lds;       // row stride of the scale planes in bytes
+  int accum;         // 1: fp32 C already holds the sum over the k before this range; add to it
   int nslices;       // ceil(K / 128)
 };
 
@@ -78,7 +80,7 @@ struct Skinny {
         const uint8_t* brow = a.B + (int64_t)n * a.ldb;
         if (live) {
           G.b[u][j] = BF4 ? load_fp4(brow, k0, g, a.K) : load_fp8(brow, k0, g, a.K);
-          G.sb[u][j] = load_scale(a.SB + (int64_t)n * nb, sl * 4 + g, nb);
+          G.sb[u][j] = load_scale(a.SB + (int64_t)n * a.lds, sl * 4 + g, nb);
         } else {
           G.b[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
           G.sb[u][j] = 127;
@@ -90,7 +92,7 @@ struct Skinny {
         const uint8_t* arow = a.A + (int64_t)m * a.lda;
         if (live) {
           G.a[u][t] = load_fp8(arow, k0, g, a.K);
-          G.sa[u][t] = load_scale(a.SA + (int64_t)m * nb, sl * 4 + g, nb);
+          G.sa[u][t] = load_scale(a.SA + (int64_t)m * a.lds, sl * 4 + g, nb);
         } else {
           G.a[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
           G.sa[u][t] = 127;
@@ -152,7 +154,18 @@ struct Skinny {
         for (int w = 0; w < W - 1; w++) v += red[w][t][j][lane];
         if (m >= a.M) continue;
         const int n = n0 + j * 16 + 4 * g;
-        epi_store4<false>(a.e, a.N, m, n, v, (a.N & 3) == 0 && n + 3 < a.N);
+        const bool vec = (a.N & 3) == 0 && n + 3 < a.N;
+        if (a.accum) {
+          const float* prev = reinterpret_cast<const float*>(a.e.C) + (int64_t)m * a.N + n;
+          if (vec) {
+            v += *reinterpret_cast<const v4f*>(prev);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+              if (n + i < a.N) v[i] += prev[i];
+          }
+        }
+        epi_store4<false>(a.e, a.N, m, n, v, vec);
       }
     }
   }
@@ -195,19 +208,22 @@ hipError_t launch_by_m(const SkArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
-                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream, int64_t k0, int64_t kn) {
+  if (kn < 0) kn = K - k0;
   SkArgs a{};
-  a.A = (const uint8_t*)A;
-  a.SA = SA;
-  a.B = (const uint8_t*)B;
-  a.SB = SB;
+  a.A = (const uint8_t*)A + k0;  // E4M3 activations: one byte per element
+  a.SA = SA + k0 / 32;
+  a.B = (const uint8_t*)B + ((fmt == 0) ? k0 : k0 / 2);
+  a.SB = SB + k0 / 32;
   a.e = e;
   a.M = (int)M;
   a.N = (int)N;
-  a.K = (int)K;
+  a.K = (int)kn;
   a.lda = K;
   a.ldb = (fmt == 0) ? K : K / 2;
-  a.nslices = (int)((K + 127) / 128);
+  a.lds = K / 32;
+  a.accum = k0 > 0;
+  a.nslices = (int)((kn + 127) / 128);
   return (fmt == 0) ? launch_by_m<false>(a, stream) : launch_by_m<true>(a, stream);
 }
 

@@ -17,8 +17,12 @@ hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, vo
 // C through the epilogue `e` (output pointer, bias, activation, output type).
 hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
+// Split-K skinny kernel (M <= kSkinnyMaxM, fmt 0 or 1) over the k range
+// [k0, k0 + kn) of a product whose rows hold K elements (kn < 0: to K).  With
+// k0 > 0, C is fp32 and already holds the sum over k < k0, which is added.
 hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
-                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream, int64_t k0 = 0,
+                            int64_t kn = -1);
 hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int64_t N, int64_t K,
                             int b_is_nk, hipStream_t stream);
 hipError_t launch_deq_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, float* C, int64_t M,
@@ -45,9 +49,11 @@ hipError_t launch_f16_pp128(const uint16_t* A, const uint16_t* B, float* C, int6
 // 1024 from 2048 (A's k range per wave is held in registers, which bounds one
 // launch's K; longer K runs in chunks that add into an fp32 C), 4-byte
 // aligned scale planes.
+// launch_mx_decode covers k < kn of rows that hold K elements (kn < 0: all
+// of K; kn a multiple of 1024 that decode_ok(M, kn, ...) accepts).
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB, const Epi& e);
 hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
-                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
+                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream, int64_t kn = -1);
 
 // Stand-alone epilogue: Y = out(act(X + bias)) for an M x N fp32 matrix X,
 // written through `e` (the decomposed form of the fused GEMM epilogue).

@@ -124,7 +124,8 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * each chunk adding into C, K up to 131072; 16-bit C through
  * mxgemm_run_fused: all of K per launch, K up to 16384 / 12288, one launch per
  * 64, 32 or 16 rows for K <= 4096, <= 8192, above); for other small M
- * (M <= 64) a split-K kernel.
+ * (M <= 64) a split-K kernel, which with fp32 C and M <= 16 only adds the
+ * last K mod 1024 elements to the decode kernel's sum over the rest.
  * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the
  * workloads this library is tested on; the MFMA's internal alignment of
  * wide-range products within one instruction is the dominant error term.

@@ -112,15 +112,17 @@ def test_epilogue_gelu_against_oracle(out_type):
 # >= 256 tiles (plain fp32 takes the 256 x 256 tiled kernel, a general
 # epilogue the 128 x 128 one), the decode kernel (1, 3 row blocks; two
 # K chunks at K = 8192 for 33 rows, 20480 and, with E4M3 weights, 14336,
-# where 16-bit outputs take two row launches or the split-K kernel instead)
-# and the split-K skinny kernel.
+# where 16-bit outputs take two row launches or the split-K kernel instead;
+# K = 4608 split between the decode and split-K kernels) and the split-K
+# skinny kernel.
 CASES = [("mxfp8_8192", 4096, 4096, 256, 0, 20000), ("mxfp8_2048", 4096, 4352, 256, 2, 20000),
          ("mxfp8_2048", 512, 640, 384, 0, None), ("mxfp8_2048", 512, 640, 384, 4, None),
          ("mxfp8_2048", 300, 257, 512, 0, None), ("prefill_8192x14336x4096", 520, 530, 1056, 1, None),
          ("mxfp8_2048", 4100, 4100, 128, 0, 20000), ("decode_16x28672x8192", 16, 1000, 2048, 1, None),
          ("decode_16x28672x8192", 48, 1000, 4096, 0, None), ("decode_16x28672x8192", 33, 1001, 8192, 1, None),
          ("decode_16x28672x8192", 40, 512, 1536, 0, None), ("decode_16x28672x8192", 7, 1003, 1536, 1, None),
-         ("decode_16x28672x8192", 17, 1001, 20480, 1, None), ("decode_16x28672x8192", 16, 600, 14336, 0, None)]
+         ("decode_16x28672x8192", 17, 1001, 20480, 1, None), ("decode_16x28672x8192", 16, 600, 14336, 0, None),
+         ("decode_16x28672x8192", 13, 1001, 4608, 1, None)]
 
 EPILOGUES = [(True, oracle.ACT_GELU, oracle.OUT_BF16), (True, oracle.ACT_NONE, oracle.OUT_F16),
              (False, oracle.ACT_GELU, oracle.OUT_F32), (True, oracle.ACT_GELU, oracle.OUT_F16)]
@@ -160,9 +162,14 @@ def test_fused_gemm(name, M, N, K, fmt, npts):
     # rows each) or, beyond one launch's K, the split-K kernel.  Where fp32
     # C needs several chunks, the two sum in another order (both are checked
     # against the oracle).
+    # With fp32 C and up to 16 rows, K not a multiple of 1024 (above 2048)
+    # also splits: the decode kernel takes the multiples of 1024, the split-K
+    # kernel adds the rest; a 16-bit C takes the split-K kernel for all of K.
     blocks = (M + 15) // 16
     limit = (16 if fmt == 1 else 12) if blocks <= 1 else 8 if blocks <= 2 else 4
-    chunked = fmt in (0, 1) and M <= 64 and K % 1024 == 0 and K >= 2048 and K // 1024 > limit
+    decode_rows = fmt in (0, 1) and M <= 64
+    chunked = decode_rows and ((K % 1024 == 0 and K >= 2048 and K // 1024 > limit) or
+                               (M <= 16 and K % 1024 != 0 and K - K % 1024 >= 2048))
     for use_bias, act, out_type in EPILOGUES:
         bb = bias if use_bias else None
         fused = b.mxgemm_run_fused(qa, sa, qb, sb, fmt, bias=bb, act=act, out_type=out_type)

@@ -215,7 +215,11 @@ def test_mx_blockpow2_recipe_full():
 # chunk covers all rows, the chunks being as many as the A operands of M / 16
 # row blocks need (33 .. 64 rows above K = 4096, 17 .. 32 above 8192, any M
 # above one launch's range: 14336 and 16384 with E4M3 weights, 17408 ..
-# 28672), each adding into C; 4608 and 1536 take the split-K skinny kernel.
+# 28672), each adding into C.  K not a multiple of 1024 (11008, 4608, 3104,
+# 2080) with up to 16 rows takes the decode kernel for the multiples of 1024
+# and the split-K kernel for the rest (736, 512, 32, 32 elements), which adds
+# into C; 1536 (below 2048 + 1024) and more rows take the split-K kernel
+# alone.
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (7, 1000, 1536), (16, 1001, 4608), (13, 250, 8192),
                                    (16, 4165, 4096), (3, 64, 8192), (16, 16, 2048), (9, 5000, 8192),
@@ -227,7 +231,8 @@ def test_mx_blockpow2_recipe_full():
                                    (16, 5000, 5120), (33, 777, 5120), (17, 4165, 7168), (64, 300, 7168),
                                    (16, 1001, 9216), (20, 5000, 9216), (9, 700, 11264), (16, 1000, 13312),
                                    (5, 4165, 15360), (16, 1000, 16384), (33, 500, 17408), (16, 1001, 25600),
-                                   (64, 300, 28672)])
+                                   (64, 300, 28672), (16, 700, 11008), (40, 1001, 11008), (5, 300, 3104),
+                                   (9, 129, 2080)])
 def test_mx_gemm_decode_kernel_full(fmt, M, N, K):
     say("mx decode kernel", fmt, M, N, K)
     a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=7 * M + N + K + fmt)
