@@ -240,6 +240,19 @@ def test_mx_gemm_decode_kernel_full(fmt, M, N, K):
     assert r["ok"], r
 
 
+# Decode extremes: one weight row (N = 1) and fewer than 16 (the clamped rows
+# of a single fragment), the longest K (131072: 8 chunks with E2M1 weights,
+# 11 with E4M3) and, at 131040, 127 whole multiples of 1024 in chunks plus a
+# 992-element remainder on the split-K kernel.
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 2048), (3, 7, 4096), (16, 15, 3072), (2, 40, 131072), (1, 17, 131040)])
+def test_mx_gemm_decode_extremes(fmt, M, N, K):
+    say("mx decode extremes", fmt, M, N, K)
+    a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=3 * M + N + K + fmt)
+    r, _ = mx_case(a32, b32, fmt)
+    assert r["ok"], r
+
+
 # Scale planes at an odd byte address: the ABI takes any alignment for them;
 # the ping-pong and decode kernels need 4-byte aligned scale rows, so these
 # shapes must fall back (256-wide tiled, skinny and 128-wide tiled kernels
@@ -330,6 +343,13 @@ def test_deterministic():
     d1 = gpu_mx(q16, s16, qb, sb, 0, 16, 520).cpu().numpy()
     d2 = gpu_mx(q16, s16, qb, sb, 0, 16, 520).cpu().numpy()
     assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+    # decode in two K chunks adding into C (40 rows at K = 8192)
+    a32, b32 = mx_sources("decode_16x28672x8192", 40, 520, 8192, seed=10)
+    qa, sa = gpu_quantize(a32, 0)
+    qb, sb = gpu_quantize(b32, oracle.E2M1)
+    e1 = gpu_mx(qa, sa, qb, sb, 1, 40, 520).cpu().numpy()
+    e2 = gpu_mx(qa, sa, qb, sb, 1, 40, 520).cpu().numpy()
+    assert np.array_equal(e1.view(np.uint32), e2.view(np.uint32))
 
 
 # -------------------------------------------------------------- fp16 GEMM
