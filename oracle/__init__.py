@@ -75,9 +75,9 @@ def _load():
     lib.mxref_fp16_value.restype = ctypes.c_double
     lib.mxref_quantize.argtypes = [p, i64, i64, ci, p, p]
     lib.mxref_quantize.restype = ci
-    lib.mxref_gemm.argtypes = [p, p, ci, p, p, ci, i64, i64, i64, p, p]
+    lib.mxref_gemm.argtypes = [p, p, ci, p, p, ci, i64, i64, i64, p, p, p]
     lib.mxref_gemm.restype = ci
-    lib.mxref_gemm_points.argtypes = [p, p, ci, p, p, ci, i64, i64, i64, p, p, i64, p, p]
+    lib.mxref_gemm_points.argtypes = [p, p, ci, p, p, ci, i64, i64, i64, p, p, i64, p, p, p]
     lib.mxref_gemm_points.restype = ci
     lib.mxref_fp16_gemm.argtypes = [p, p, i64, i64, i64, ci, p, p]
     lib.mxref_fp16_gemm.restype = ci
@@ -169,12 +169,16 @@ def _check_operand(q, s, rows, K, elem, name):
         raise ValueError(name + ": shape mismatch")
 
 
-def mx_gemm(a_q, a_s, elem_a, b_q, b_s, elem_b, M, N, K, points=None):
+def mx_gemm(a_q, a_s, elem_a, b_q, b_s, elem_b, M, N, K, points=None, step_max=False):
     """float64 reference C and the magnitude sum |A||B| (same shape).
 
     A is M x K codes with M x K/32 scales; B is N x K codes with N x K/32
     scales (both K contiguous).  With ``points=(I, J)`` only those output
-    elements are computed and 1-D arrays are returned.
+    elements are computed and 1-D arrays are returned.  With
+    ``step_max=True`` a third array is returned: for each output element the
+    sum, over the 128-element steps of K (k = 128t .. 128t+127), of the
+    largest scaled product magnitude in the step (a tolerance input, see
+    ``gate``).
     """
     a_q = np.ascontiguousarray(a_q)
     a_s = np.ascontiguousarray(a_s)
@@ -186,18 +190,21 @@ def mx_gemm(a_q, a_s, elem_a, b_q, b_s, elem_b, M, N, K, points=None):
     if points is None:
         C = np.empty((M, N), dtype=np.float64)
         ABS = np.empty((M, N), dtype=np.float64)
+        SMAX = np.empty((M, N), dtype=np.float64) if step_max else None
         rc = lib.mxref_gemm(_ptr(a_q), _ptr(a_s), elem_a, _ptr(b_q), _ptr(b_s), elem_b,
-                            M, N, K, _ptr(C), _ptr(ABS))
+                            M, N, K, _ptr(C), _ptr(ABS), None if SMAX is None else _ptr(SMAX))
     else:
         I = np.ascontiguousarray(points[0], dtype=np.int64)
         J = np.ascontiguousarray(points[1], dtype=np.int64)
         C = np.empty(I.shape[0], dtype=np.float64)
         ABS = np.empty(I.shape[0], dtype=np.float64)
+        SMAX = np.empty(I.shape[0], dtype=np.float64) if step_max else None
         rc = lib.mxref_gemm_points(_ptr(a_q), _ptr(a_s), elem_a, _ptr(b_q), _ptr(b_s), elem_b,
-                                   M, N, K, _ptr(I), _ptr(J), I.shape[0], _ptr(C), _ptr(ABS))
+                                   M, N, K, _ptr(I), _ptr(J), I.shape[0], _ptr(C), _ptr(ABS),
+                                   None if SMAX is None else _ptr(SMAX))
     if rc != 0:
         raise ValueError("oracle mx_gemm: bad arguments")
-    return C, ABS
+    return (C, ABS, SMAX) if step_max else (C, ABS)
 
 
 def fp16_gemm(a_bits, b_bits, M, N, K, b_is_nk, points=None):
@@ -231,42 +238,58 @@ def fp16_gemm(a_bits, b_bits, M, N, K, b_is_nk, points=None):
 U = 2.0 ** -24  # unit roundoff of fp32
 
 
-def gate(c_test, c_ref, abs_ref, K, extra_terms=0):
-    """Checksum gate: |c_test - c_ref| <= (K + extra_terms) * 2^-24 * sum|a b|
-    for every element, NaN positions identical, +-Inf positions and signs
-    identical.
+def gate(c_test, c_ref, abs_ref, K, step_max=None, kappa=0.0):
+    """Checksum gate: for every element
+
+        |c_test - c_ref| <= K * 2^-24 * sum|a b|  [+ kappa * step_max]
+
+    NaN positions identical, +-Inf positions and signs identical.
 
     The fp8 x fp8 (or fp4, fp16) products times power-of-two scales are exact
     in fp32, so with fp32 accumulation the only admissible error is
-    accumulation error; the bound is the classical recursive-summation bound
-    with K terms (extra_terms = 0).  A caller whose arithmetic has a known
-    additional per-dtype error (RIGEL's gate keeps one tolerance per data type:
-    "Resumo Técnico: RIGEL", section "Metodologia: O Harness RIGEL") passes it
-    as extra_terms, in the same units.  Returns a dict with 'ok', 'n_bad',
-    'max_ratio' (error over the K-term bound), 'nan_mismatch', 'n_exact'.
+    accumulation error: the classical recursive-summation bound with K terms
+    (the default, kappa = 0).  A matrix unit that adds the products of one
+    128-element step in a single operation may align them to the step's
+    largest product and drop low bits; such a path states its per-step
+    error, in units of that step's largest product magnitude, as ``kappa``
+    and passes ``step_max`` (from ``mx_gemm(..., step_max=True)``).  One
+    tolerance per data path, as RIGEL's gate keeps one per data type
+    ("Resumo Técnico: RIGEL", section "Metodologia: O Harness RIGEL").
+
+    Returns a dict with 'ok', 'n_bad', 'max_ratio' (error over the strict
+    K-term bound, reported whatever the tolerance), 'max_ratio_tol' (error
+    over the tolerance applied), 'nan_mismatch', 'inf_mismatch', 'n_exact'.
     """
     t = np.asarray(c_test, dtype=np.float64)
     r = np.asarray(c_ref, dtype=np.float64)
     a = np.asarray(abs_ref, dtype=np.float64)
     if t.shape != r.shape or r.shape != a.shape:
         raise ValueError("gate: shape mismatch")
+    if kappa != 0.0 and (step_max is None or np.shape(step_max) != r.shape):
+        raise ValueError("gate: kappa needs step_max of the reference's shape")
     nan_t, nan_r = np.isnan(t), np.isnan(r)
     nan_mismatch = int(np.count_nonzero(nan_t != nan_r))
     inf_t, inf_r = np.isinf(t), np.isinf(r)
     inf_mismatch = int(np.count_nonzero((inf_t != inf_r) | (inf_t & inf_r & (np.sign(t) != np.sign(r)))))
     fin = ~(nan_t | nan_r | inf_t | inf_r)
-    tol = K * U * a[fin]
+    strict = K * U * a[fin]
+    tol = strict if kappa == 0.0 else strict + kappa * np.asarray(step_max, dtype=np.float64)[fin]
     err = np.abs(t[fin] - r[fin])
-    bad = err > (K + extra_terms) * U * a[fin]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+    bad = err > tol
+
+    def _ratio(bound):
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+        return float(q.max()) if q.size else 0.0
+
     n_exact = int(np.count_nonzero(t[fin] == r[fin].astype(np.float32).astype(np.float64)))
     n_bad = int(np.count_nonzero(bad)) + nan_mismatch + inf_mismatch
     return {
         "ok": n_bad == 0,
         "n_bad": n_bad,
         "n": int(t.size),
-        "max_ratio": float(ratio.max()) if ratio.size else 0.0,
+        "max_ratio": _ratio(strict),
+        "max_ratio_tol": _ratio(tol),
         "nan_mismatch": nan_mismatch,
         "inf_mismatch": inf_mismatch,
         "n_exact": n_exact,
@@ -328,10 +351,10 @@ def _half_ulp(a, out_type):
     return np.ldexp(1.0, (e + 1 - P).astype(np.int64)) * 0.5 * 2.0
 
 
-def epilogue_gate(out_vals, c_ref, abs_ref, K, cols, bias, act, out_type, extra_terms=0):
+def epilogue_gate(out_vals, c_ref, abs_ref, K, cols, bias, act, out_type, step_max=None, kappa=0.0):
     """Gate for the fused output: |out - act(c_ref + bias)| within
 
-      d_c   = (K + extra_terms) 2^-24 sum|a b|   (accumulation, as in gate())
+      d_c   = K 2^-24 sum|a b| [+ kappa step_max]  (the GEMM's bound, as in gate())
       d_y   = d_c + 2^-24 |y|                     (the fp32 bias add)
       d_g   = L d_y + |y|/2 (GELU_ERF_ERR + 2^-22) + 2^-23 |g|   (with GELU;
               L the largest slope of GELU)
@@ -353,7 +376,9 @@ def epilogue_gate(out_vals, c_ref, abs_ref, K, cols, bias, act, out_type, extra_
     inf_mismatch = int(np.count_nonzero((inf_t != inf_r) | (inf_t & inf_r & (np.sign(t) != np.sign(ref_r)))))
     fin = ~(nan_t | nan_r | inf_t | inf_r)
     t, ref, c, ab, y_ref = t[fin], ref[fin], c[fin], ab[fin], y_ref[fin]
-    d = (K + extra_terms) * U * ab
+    d = K * U * ab
+    if kappa != 0.0:
+        d = d + kappa * np.asarray(step_max, dtype=np.float64).ravel()[fin]
     ymag = np.maximum(np.abs(y_ref), np.abs(t))
     if bias is not None:
         d = d + U * ymag

@@ -299,35 +299,53 @@ static double element(const uint8_t *row, int elem, int64_t k)
  * short significands, exact in float64; multiplying by a power of two is
  * exact; only the sum across blocks rounds (relative error below
  * (K/32) * 2^-53).  abs_out receives sum_k |a_ik * b_jk| * scales, the
- * magnitude that sets the accumulation-error bound. */
+ * magnitude that sets the accumulation-error bound.  When smax_out is not
+ * NULL it receives, for the steps k = 128t .. 128t+127 of K (four blocks
+ * each, the last step possibly shorter), the sum over the steps of the
+ * largest |a_ik * b_jk| * scales inside the step: the magnitude a matrix
+ * unit that adds one step's products in a single operation aligns them to
+ * (a tolerance input only; the value of C does not depend on it). */
 static void mx_point(const uint8_t *A, const uint8_t *sA, int elemA,
                      const uint8_t *B, const uint8_t *sB, int elemB,
-                     int64_t K, int64_t i, int64_t j, double *out, double *abs_out)
+                     int64_t K, int64_t i, int64_t j, double *out, double *abs_out,
+                     double *smax_out)
 {
     int64_t nb = K / 32;
     int64_t rowbytesA = (elemA == MXREF_E2M1) ? K / 2 : K;
     int64_t rowbytesB = (elemB == MXREF_E2M1) ? K / 2 : K;
     const uint8_t *ra = A + i * rowbytesA, *rb = B + j * rowbytesB;
-    double acc = 0.0, acc_abs = 0.0;
+    double acc = 0.0, acc_abs = 0.0, smax_sum = 0.0, step_max = 0.0;
     for (int64_t b = 0; b < nb; b++) {
-        double part = 0.0, part_abs = 0.0;
+        double part = 0.0, part_abs = 0.0, part_max = 0.0;
         double scale = tab_ue8m0[sA[i * nb + b]] * tab_ue8m0[sB[j * nb + b]];
         for (int64_t k = b * 32; k < b * 32 + 32; k++) {
             double p = element(ra, elemA, k) * element(rb, elemB, k);
             part += p;
             part_abs += fabs(p);
+            if (!(fabs(p) <= part_max))
+                part_max = fabs(p); /* NaN propagates */
         }
         acc += part * scale;
         acc_abs += part_abs * scale;
+        if (!(part_max * scale <= step_max))
+            step_max = part_max * scale;
+        if (b % 4 == 3 || b == nb - 1) {
+            smax_sum += step_max;
+            step_max = 0.0;
+        }
     }
     *out = acc;
     *abs_out = acc_abs;
+    if (smax_out)
+        *smax_out = smax_sum;
 }
 
-/* Full product: C and ABS are M x N float64, row-major. */
+/* Full product: C and ABS (and SMAX unless NULL) are M x N float64,
+ * row-major. */
 int mxref_gemm(const uint8_t *A, const uint8_t *sA, int elemA,
                const uint8_t *B, const uint8_t *sB, int elemB,
-               int64_t M, int64_t N, int64_t K, double *C, double *ABS)
+               int64_t M, int64_t N, int64_t K, double *C, double *ABS,
+               double *SMAX)
 {
     if (K <= 0 || K % 32 != 0 || M < 0 || N < 0)
         return -1;
@@ -339,17 +357,17 @@ int mxref_gemm(const uint8_t *A, const uint8_t *sA, int elemA,
     for (int64_t i = 0; i < M; i++)
         for (int64_t j = 0; j < N; j++)
             mx_point(A, sA, elemA, B, sB, elemB, K, i, j,
-                     &C[i * N + j], &ABS[i * N + j]);
+                     &C[i * N + j], &ABS[i * N + j], SMAX ? &SMAX[i * N + j] : NULL);
     return 0;
 }
 
-/* Sampled product: only the npts points (I[p], J[p]); C and ABS have npts
- * entries.  Same arithmetic as mxref_gemm. */
+/* Sampled product: only the npts points (I[p], J[p]); C, ABS and SMAX
+ * (unless NULL) have npts entries.  Same arithmetic as mxref_gemm. */
 int mxref_gemm_points(const uint8_t *A, const uint8_t *sA, int elemA,
                       const uint8_t *B, const uint8_t *sB, int elemB,
                       int64_t M, int64_t N, int64_t K,
                       const int64_t *I, const int64_t *J, int64_t npts,
-                      double *C, double *ABS)
+                      double *C, double *ABS, double *SMAX)
 {
     if (K <= 0 || K % 32 != 0)
         return -1;
@@ -362,7 +380,8 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *sA, int elemA,
     make_tables();
 #pragma omp parallel for schedule(dynamic, 64)
     for (int64_t p = 0; p < npts; p++)
-        mx_point(A, sA, elemA, B, sB, elemB, K, I[p], J[p], &C[p], &ABS[p]);
+        mx_point(A, sA, elemA, B, sB, elemB, K, I[p], J[p], &C[p], &ABS[p],
+                 SMAX ? &SMAX[p] : NULL);
     return 0;
 }
 

@@ -1,0 +1,248 @@
+"""Error model of one scaled-MFMA instruction, measured through the C ABI.
+
+At K = 128 every output element of mxgemm_run is one
+v_mfma_scale_f32_16x16x128_f8f6f4 result added to a zero accumulator (the
+split-K kernel for E4M3 activations with M <= 64, the tiled kernel for the
+other format pairs), so C[i][j] minus the exact sum of its 128 scaled products
+is that instruction's own error.  The codes are crafted directly (no
+quantizer): a dominant product beside many small ones at gaps of 0 to 40
+binades, cancelling pairs of large products, random codes over the whole
+element range at unit and at varying block scales,
+for every operand-format pair.  The model the parity gate uses is asserted on
+all of them:
+
+    |result - exact| <= MFMA_STEP_KAPPA * max_k |a_k b_k| + 2^-24 |exact|
+
+(the second term is the rounding of the result to fp32).  A second test keeps
+the reason for the model on record: the K-term bound alone (128 * 2^-24 *
+sum|a b| at K = 128) fails on the dominant-product data, so for this
+instruction that bound cannot hold by itself.  A third checks that a
+non-zero accumulator is not part of the alignment (a second step's small
+products beside a large running sum are kept to fp32 accuracy).
+
+The exact sums come from the oracle (float64; one step's block partials are
+exact and the four-block sum rounds at 2^-53 relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import read_golden_rows
+from gpu_util import FMT_ELEMS, MFMA_STEP_KAPPA, binding, nan_canary, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+E4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+E5 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+E2 = np.array([float(v) for _, v in read_golden_rows("e2m1_values.txt")])
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert binding().mxgemm_device_supported()
+    yield
+
+
+def _table(elem):
+    return {oracle.E4M3: E4, oracle.E5M2: E5, oracle.E2M1: E2}[elem]
+
+
+def _finite_codes(elem):
+    t = _table(elem)
+    return np.flatnonzero(np.isfinite(t)).astype(np.uint8)
+
+
+def _code_of(elem, value):
+    t = _table(elem)
+    hit = np.flatnonzero(t == value)
+    assert hit.size, (elem, value)
+    return np.uint8(hit[0])
+
+
+def _largest(elem):
+    t = _table(elem)
+    return float(np.nanmax(np.where(np.isfinite(t), t, np.nan)))
+
+
+def _smallest(elem):
+    t = np.abs(_table(elem))
+    return float(t[(t > 0) & np.isfinite(t)].min())
+
+
+def _pack(vals_codes, elem):
+    """rows x K element codes -> the operand's byte plane (E2M1: two per
+    byte, even k in the low nibble)."""
+    if elem != oracle.E2M1:
+        return np.ascontiguousarray(vals_codes.astype(np.uint8))
+    c = vals_codes.astype(np.uint8)
+    return np.ascontiguousarray(c[:, 0::2] | (c[:, 1::2] << 4))
+
+
+def _operands(elem, rows, rng, families):
+    """rows x 128 codes and rows x 4 scale bytes, cycling over the families."""
+    K = 128
+    codes = np.zeros((rows, K), dtype=np.uint8)
+    scales = np.full((rows, 4), 127, dtype=np.uint8)
+    fin = _finite_codes(elem)
+    big, tiny = _largest(elem), _smallest(elem)
+    one = _code_of(elem, 1.0)
+    for r in range(rows):
+        fam = families[r % len(families)]
+        if fam == "ones":
+            codes[r] = one
+            codes[r, rng.random(K) < 0.5] |= 0x80 if elem != oracle.E2M1 else 0x8
+        elif fam == "dominant":
+            # one large element, the rest small, at block-scale gaps of
+            # 0 .. 40 binades
+            gap = int(rng.integers(0, 21))
+            small = fin[(np.abs(_table(elem)[fin]) > 0) & (np.abs(_table(elem)[fin]) <= 2 * tiny + 1e-30)]
+            codes[r] = rng.choice(small, size=K)
+            k = int(rng.integers(0, 32))
+            neg = (0x80 if elem != oracle.E2M1 else 0x8) if rng.random() < 0.5 else 0
+            codes[r, k] = _code_of(elem, big) | neg
+            scales[r, 0] = 127 + gap
+            scales[r, 1:] = 127 - gap
+        elif fam == "cancel":
+            # +X and -X in one step beside small terms: the result is the small part
+            small = fin[(np.abs(_table(elem)[fin]) > 0) & (np.abs(_table(elem)[fin]) <= 4 * tiny + 1e-30)]
+            codes[r] = rng.choice(small, size=K)
+            neg = 0x80 if elem != oracle.E2M1 else 0x8
+            codes[r, 3] = _code_of(elem, big)
+            codes[r, 40] = _code_of(elem, big) | neg
+            gap = int(rng.integers(0, 16))
+            scales[r, 0] = scales[r, 1] = 127 + gap
+            scales[r, 2] = scales[r, 3] = 127 - gap
+        elif fam == "plus_ones":
+            codes[r] = one
+        elif fam == "random":
+            codes[r] = rng.choice(fin, size=K)
+        elif fam == "random_positive":
+            pos = fin[_table(elem)[fin] > 0]
+            codes[r] = rng.choice(pos, size=K)
+        elif fam == "staircase":
+            # one positive element per binade below the largest, repeated:
+            # every product lands at a different alignment position
+            pos = fin[_table(elem)[fin] > 0]
+            pos = pos[np.argsort(_table(elem)[pos])][::-1]
+            codes[r] = pos[np.arange(K) % len(pos)]
+            rng.shuffle(codes[r])
+        elif fam == "near_threshold":
+            # the largest element once, then positive elements 2^-9 .. 2^-15
+            # below it (what an alignment window of about 13 bits drops or
+            # truncates), all of one sign
+            t = _table(elem)
+            pos = fin[t[fin] > 0]
+            lo = big * 2.0 ** -int(rng.integers(9, 16))
+            cand = pos[(t[pos] <= lo) & (t[pos] >= lo / 4)]
+            if cand.size == 0:
+                cand = pos[t[pos] <= lo] if (t[pos] <= lo).any() else pos
+            codes[r] = rng.choice(cand, size=K)
+            codes[r, int(rng.integers(0, K))] = _code_of(elem, big)
+        elif fam == "random_scaled":
+            codes[r] = rng.choice(fin, size=K)
+            scales[r] = rng.integers(107, 148, size=4)
+        else:
+            raise ValueError(fam)
+    return _pack(codes, elem), scales
+
+
+FAMILIES_A = ["ones", "random", "random_scaled", "ones", "plus_ones", "random_positive", "plus_ones",
+              "plus_ones"]
+FAMILIES_B = ["dominant", "cancel", "random", "random_scaled", "dominant", "random_positive", "staircase",
+              "near_threshold"]
+
+
+def _run_single_steps(fmt, seed, M=16, N=8192, fam_a=FAMILIES_A, fam_b=FAMILIES_B):
+    ea, eb = FMT_ELEMS[fmt]
+    rng = np.random.default_rng(seed)
+    aq, sa = _operands(ea, M, rng, fam_a)
+    bq, sb = _operands(eb, N, rng, fam_b)
+    b = binding()
+    out = nan_canary(M, N)
+    b.mxgemm_run(to_dev(aq), to_dev(sa), to_dev(bq), to_dev(sb), fmt, out=out)
+    torch.cuda.synchronize()
+    c = out.cpu().numpy().astype(np.float64)
+    ref, ab, sm = oracle.mx_gemm(aq, sa, ea, bq, sb, eb, M, N, 128, step_max=True)
+    return c, ref, ab, sm
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5])
+def test_single_instruction_error_model(fmt):
+    c, ref, ab, sm = _run_single_steps(fmt, 1000 + fmt)
+    assert np.isfinite(ref).all() and np.isfinite(c).all()
+    err = np.abs(c - ref)
+    excess = np.maximum(err - 2.0 ** -24 * np.abs(ref) - 2.0 ** -50 * ab, 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(sm > 0, excess / np.where(sm > 0, sm, 1.0), np.where(excess > 0, np.inf, 0.0))
+    worst = float(rel.max())
+    frac_exact = float(np.mean(c == ref.astype(np.float32)))
+    say("fmt %d: max (err - fp32 rounding) / max|product| = %.3g = 2^%.2f (kappa 2^%.1f); %.1f%% of results "
+        "equal fp32(exact)" % (fmt, worst, np.log2(worst) if worst > 0 else -np.inf, np.log2(MFMA_STEP_KAPPA),
+                               100 * frac_exact))
+    bad = np.argwhere(rel > MFMA_STEP_KAPPA)
+    assert bad.size == 0, [(int(i), int(j), c[i, j], ref[i, j], sm[i, j]) for i, j in bad[:5]]
+
+
+@pytest.mark.parametrize("fmt", [0, 3, 5])
+def test_strict_bound_alone_fails_for_one_instruction(fmt):
+    """The reason for the model: on the dominant-product rows the K-term bound
+    (128 * 2^-24 * sum|a b|) is exceeded, i.e. the instruction drops small
+    products that fp32 summation would keep."""
+    c, ref, ab, sm = _run_single_steps(fmt, 2000 + fmt)
+    r = oracle.gate(c, ref, ab, 128)
+    say("fmt %d: strict gate %s" % (fmt, {k: r[k] for k in ("ok", "n_bad", "n", "max_ratio")}))
+    assert not r["ok"] and r["max_ratio"] > 4
+    assert oracle.gate(c, ref, ab, 128, step_max=sm, kappa=MFMA_STEP_KAPPA)["ok"]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_accumulator_is_not_aligned_with_the_products(fmt):
+    """K = 256, two instructions per element: the first step holds a single
+    product X (exact), the second 128 products whose sum S is 2^-12 .. 2^-17
+    of X.  The result must be X + S to fp32 accuracy plus the second step's
+    own model term and a few units of fp32 rounding (4 u |C|; measured up to
+    about 2.7 u): the incoming accumulator does not take part in the
+    product alignment (were it aligned like a product, S would be dropped as
+    the small products beside a dominant one are, an error far above this
+    bound for most elements, which the test also checks)."""
+    ea, eb = FMT_ELEMS[fmt]
+    M, N, K = 16, 2048, 256
+    rng = np.random.default_rng(3000 + fmt)
+    aq_codes = np.full((M, K), _code_of(ea, 1.0), dtype=np.uint8)
+    sa = np.full((M, 8), 127, dtype=np.uint8)
+    big = _largest(eb)
+    fin = _finite_codes(eb)
+    tb = _table(eb)
+    mid = fin[(np.abs(tb[fin]) >= 1.0) & (np.abs(tb[fin]) <= 4.0)]
+    bq_codes = np.zeros((N, K), dtype=np.uint8)
+    sb = np.full((N, 8), 127, dtype=np.uint8)
+    step2max = np.zeros(N)
+    for j in range(N):
+        bq_codes[j, int(rng.integers(0, 128))] = _code_of(eb, big)
+        bq_codes[j, 128:] = rng.choice(mid, size=128)
+        # |S| / X is about 28 * 2^-s2 / (big * 2^s1); aim at 2^-t
+        t = float(rng.uniform(12, 17))
+        total = int(round(t + np.log2(28.0 / big)))
+        s1 = int(min(max(total, 0), 8))
+        s2 = total - s1
+        sb[j, :4] = 127 + s1
+        sb[j, 4:] = 127 - s2
+        step2max[j] = np.abs(tb[bq_codes[j, 128:]]).max() * 2.0 ** -s2
+    aq, bq = _pack(aq_codes, ea), _pack(bq_codes, eb)
+    b = binding()
+    out = nan_canary(M, N)
+    b.mxgemm_run(to_dev(aq), to_dev(sa), to_dev(bq), to_dev(sb), fmt, out=out)
+    torch.cuda.synchronize()
+    c = out.cpu().numpy().astype(np.float64)
+    ref, ab = oracle.mx_gemm(aq, sa, ea, bq, sb, eb, M, N, K)
+    x = big * np.exp2(sb[:, 0].astype(np.float64) - 127)
+    s_part = ref - x[None, :]
+    err = np.abs(c - ref)
+    tol = 4 * 2.0 ** -24 * np.abs(ref) + MFMA_STEP_KAPPA * step2max[None, :] + 2.0 ** -50 * ab
+    say("fmt %d: max err / (4 u |C| + second-step model term) = %.3g; median |S| / that bound = %.3g"
+        % (fmt, float((err / tol).max()), float(np.median(np.abs(s_part) / tol))))
+    assert (err <= tol).all()
+    assert np.mean(np.abs(s_part) > 4 * tol) > 0.9

@@ -35,7 +35,7 @@ def test_mx_workload(name, fmt, npts):
     say("workload", name, w.M, w.N, w.K)
     a32, b32 = mxin.mx_sources(w)
     pts = None if npts is None else mxin.sample_points(w.M, w.N, npts)
-    r, c = mx_case(a32, b32, fmt, points=pts, extra_terms=0)   # the K-term bound, no allowance
+    r, c = mx_case(a32, b32, fmt, points=pts)   # the strict K-term bound
     say("  gate", r)
     assert r["ok"], r
     assert not np.isnan(c).any(), "unwritten outputs"

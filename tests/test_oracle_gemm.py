@@ -241,22 +241,65 @@ def test_gate_accepts_fp32_rounding_and_rejects_corruption():
     assert not r["ok"] and r["nan_mismatch"] == 1
 
 
-def test_gate_allowance_keeps_detection():
-    """The scaled-MFMA allowance (extra terms in the bound) still rejects a
-    wrong scale byte and a flipped code on a realistic operand pair."""
+def test_step_max_bruteforce():
+    """The per-step magnitude the gate's matrix-unit term uses: for each
+    output element, the sum over the 128-element steps of K of the largest
+    |a_ik b_jk| * scales in the step, against a direct numpy evaluation over
+    torch/OCP-decoded values (a ragged last step included)."""
+    rng = np.random.default_rng(21)
+    for ea, eb, M, N, K in ((oracle.E4M3, oracle.E4M3, 5, 7, 416), (oracle.E4M3, oracle.E2M1, 3, 4, 256),
+                            (oracle.E5M2, oracle.E4M3, 4, 3, 96)):
+        aq, as_ = _rand_operand(rng, M, K, ea, 100, 150)
+        bq, bs = _rand_operand(rng, N, K, eb, 100, 150)
+        C, ABS, SMAX = oracle.mx_gemm(aq, as_, ea, bq, bs, eb, M, N, K, step_max=True)
+        A = _decode(aq, ea, K) * np.exp2(as_.astype(np.float64) - 127).repeat(32, 1)
+        B = _decode(bq, eb, K) * np.exp2(bs.astype(np.float64) - 127).repeat(32, 1)
+        P = np.abs(A[:, None, :] * B[None, :, :])          # M x N x K
+        want = np.zeros((M, N))
+        for k0 in range(0, K, 128):
+            want += P[:, :, k0:k0 + 128].max(axis=2)
+        assert np.array_equal(SMAX, want)
+        C2, ABS2 = oracle.mx_gemm(aq, as_, ea, bq, bs, eb, M, N, K)
+        assert np.array_equal(C, C2) and np.array_equal(ABS, ABS2)
+        pts = (np.array([0, M - 1, 1]), np.array([N - 1, 0, 2]))
+        _, _, SP = oracle.mx_gemm(aq, as_, ea, bq, bs, eb, M, N, K, points=pts, step_max=True)
+        assert np.array_equal(SP, want[pts])
+
+
+def test_gate_model_term_keeps_detection():
+    """The matrix-unit term of the gate (kappa times the per-step largest
+    product) still rejects a wrong scale byte and a flipped code on a
+    realistic operand pair, and is what lets a single-step dominant-product
+    error pass where the K-term bound alone does not."""
+    from gpu_util import MFMA_STEP_KAPPA
+
     rng = np.random.default_rng(13)
     M, N, K = 32, 32, 1024
     a = rng.standard_normal((M, K)).astype(np.float32)
     b = rng.standard_normal((N, K)).astype(np.float32)
     aq, as_ = oracle.quantize(a, oracle.E4M3)
     bq, bs = oracle.quantize(b, oracle.E4M3)
-    C, ABS = oracle.mx_gemm(aq, as_, oracle.E4M3, bq, bs, oracle.E4M3, M, N, K)
-    assert oracle.gate(C.astype(np.float32), C, ABS, K, extra_terms=2048)["ok"]
+    C, ABS, SM = oracle.mx_gemm(aq, as_, oracle.E4M3, bq, bs, oracle.E4M3, M, N, K, step_max=True)
+    kw = dict(step_max=SM, kappa=MFMA_STEP_KAPPA)
+    assert oracle.gate(C.astype(np.float32), C, ABS, K, **kw)["ok"]
     as2 = as_.copy()
     as2[4, 9] += 1
     C2, _ = oracle.mx_gemm(aq, as2, oracle.E4M3, bq, bs, oracle.E4M3, M, N, K)
-    assert not oracle.gate(C2.astype(np.float32), C, ABS, K, extra_terms=2048)["ok"]
+    assert not oracle.gate(C2.astype(np.float32), C, ABS, K, **kw)["ok"]
     bq2 = bq.copy()
     bq2[3, 100] ^= 0x40
     C3, _ = oracle.mx_gemm(aq, as_, oracle.E4M3, bq2, bs, oracle.E4M3, M, N, K)
-    assert not oracle.gate(C3.astype(np.float32), C, ABS, K, extra_terms=2048)["ok"]
+    assert not oracle.gate(C3.astype(np.float32), C, ABS, K, **kw)["ok"]
+    # one step: 448 * 1 against 127 products of 2^-9; dropping the small ones
+    # (an error of 127 * 2^-9 = 0.248) fails the K-term bound (128 * 2^-24 *
+    # 448.25 = 0.0034) and passes with the model term when kappa * 448 covers it
+    aq = np.full((1, 128), 0x01, dtype=np.uint8)
+    aq[0, 0] = 0x7E
+    bq = np.full((1, 128), 0x38, dtype=np.uint8)
+    s1 = np.full((1, 4), 127, dtype=np.uint8)
+    C, ABS, SM = oracle.mx_gemm(aq, s1, oracle.E4M3, bq, s1, oracle.E4M3, 1, 1, 128, step_max=True)
+    assert C[0, 0] == 448 + 127 * 2.0 ** -9 and SM[0, 0] == 448
+    dropped = np.array([[448.0]], dtype=np.float32)
+    r = oracle.gate(dropped, C, ABS, 128)
+    assert not r["ok"] and r["max_ratio"] > 50
+    assert oracle.gate(dropped, C, ABS, 128, step_max=SM, kappa=2.0 ** -10)["ok"]
