@@ -15,15 +15,28 @@ from __future__ import annotations
 _BINDING_NAMES = (
     "mxgemm_quantize",
     "mxgemm_run",
+    "mxgemm_run_fused",
+    "mxgemm_epilogue",
     "fp16gemm_run",
     "mxgemm_run_dequant_fp16",
+    "mxgemm_mfma_ceiling",
     "mxgemm_device_supported",
     "MXGemmError",
     "E4M3",
+    "E5M2",
     "E2M1",
     "FMT_FP8_FP8",
     "FMT_FP8_FP4",
     "FMT_FP4_FP4",
+    "FMT_BF8_BF8",
+    "FMT_FP8_BF8",
+    "FMT_BF8_FP8",
+    "OUT_F32",
+    "OUT_BF16",
+    "OUT_F16",
+    "ACT_NONE",
+    "ACT_GELU",
+    "CEIL_FP16",
     "library_path",
 )
 

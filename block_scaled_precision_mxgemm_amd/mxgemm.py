@@ -32,6 +32,8 @@ OUT_BF16 = 1
 OUT_F16 = 2
 ACT_NONE = 0
 ACT_GELU = 1
+# kind of mxgemm_mfma_ceiling beside the FMT_* pairs
+CEIL_FP16 = 16
 _OUT_DTYPES = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_F16: torch.float16}
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxgemm.so")
@@ -67,6 +69,8 @@ def _load():
     lib.mxgemm_epilogue.restype = ci
     lib.fp16gemm_run.argtypes = [p, p, p, i64, i64, i64, ci, p]
     lib.fp16gemm_run.restype = ci
+    lib.mxgemm_mfma_ceiling.argtypes = [p, i64, p, i64, ci, i64, ci, p, p, p]
+    lib.mxgemm_mfma_ceiling.restype = ci
     lib.mxgemm_device_supported.argtypes = []
     lib.mxgemm_device_supported.restype = ci
     lib.mxgemm_status_string.argtypes = [ci]
@@ -228,6 +232,36 @@ def fp16gemm_run(a: torch.Tensor, b: torch.Tensor, b_is_nk: bool, out: torch.Ten
     rc = _load().fp16gemm_run(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, 1 if b_is_nk else 0,
                               _stream(stream))
     _check(rc, "fp16gemm_run")
+    return out
+
+
+def mxgemm_mfma_ceiling(ops: torch.Tensor, scales: torch.Tensor | None, kind: int, iters: int, workgroups: int,
+                        out: torch.Tensor | None = None, clocks: torch.Tensor | None = None, stream=None):
+    """Measurement helper: run `iters` rounds of the large GEMM's 32-MFMA
+    compute phase per wave on fragments taken from the bytes of `ops` (and
+    scale registers from `scales`), `workgroups` workgroups of 8 waves, no
+    memory traffic.  kind: an FMT_* pair or CEIL_FP16.  Returns `out`
+    (workgroups * 512 floats).  Flops: workgroups * 8 * iters * 32 * 65536
+    (CEIL_FP16: workgroups * 8 * iters * 64 * 16384).  clocks (optional,
+    workgroups * 2 int32): shader cycles and 100 MHz ticks of each
+    workgroup's first wave over its MFMA loop."""
+    if not ops.is_cuda or not ops.is_contiguous():
+        raise ValueError("ops must be a contiguous GPU tensor")
+    if scales is not None and (not scales.is_cuda or not scales.is_contiguous()):
+        raise ValueError("scales must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty(workgroups * 512, dtype=torch.float32, device=ops.device)
+    if out.dtype != torch.float32 or out.numel() < workgroups * 512 or not out.is_contiguous():
+        raise ValueError("out must hold workgroups * 512 contiguous floats")
+    if clocks is not None and (clocks.dtype != torch.int32 or clocks.numel() < 2 * workgroups
+                               or not clocks.is_contiguous()):
+        raise ValueError("clocks must hold workgroups * 2 contiguous int32")
+    rc = _load().mxgemm_mfma_ceiling(ops.data_ptr(), ops.numel() * ops.element_size(),
+                                     None if scales is None else scales.data_ptr(),
+                                     0 if scales is None else scales.numel() * scales.element_size(),
+                                     kind, iters, workgroups, out.data_ptr(),
+                                     None if clocks is None else clocks.data_ptr(), _stream(stream))
+    _check(rc, "mxgemm_mfma_ceiling")
     return out
 
 

@@ -126,9 +126,13 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * 64, 32 or 16 rows for K <= 4096, <= 8192, above); for other small M
  * (M <= 64) a split-K kernel, which with fp32 C and M <= 16 only adds the
  * last K mod 1024 elements to the decode kernel's sum over the rest.
- * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk| on the
- * workloads this library is tested on; the MFMA's internal alignment of
- * wide-range products within one instruction is the dominant error term.
+ * Result accuracy: |C - exact| <= K * 2^-24 * sum_k |a_ik b_jk|
+ * + 2^-7 * sum_t max_{k in step t} |a_ik b_jk| (steps of 128 K elements,
+ * products taken with their scales).  The second term is the scaled MFMA's
+ * own: it adds a step's products in one operation and drops bits far below
+ * the largest of them (measured at most 2^-8.6 of it per instruction; none
+ * for E2M1 x E2M1).  It matters for short K or block scales that vary; on
+ * long-K, same-magnitude data the first term alone holds.
  * Returns MXG_OK or an error status.  The result is deterministic.
  */
 int mxgemm_run(const void *A, const uint8_t *scaleA,
@@ -214,10 +218,61 @@ int mxgemm_run_dequant_fp16(const void *A, const uint8_t *scaleA,
                             float *C, int64_t M, int64_t N, int64_t K, int fmt,
                             void *stream);
 
-/* 1 if the current HIP device is gfx950, 0 if not, negative MXG_* on error. */
+/*
+ * mxgemm_mfma_ceiling - measurement helper (not part of the product path):
+ * the matrix-core rate the chip sustains on given operand bytes with no
+ * memory traffic, the measured ceiling reported beside the published peak
+ * ("Resumo Técnico: RIGEL", section "Metodologia: O Harness RIGEL": compute
+ * ceilings are triangulated by measurement, not taken from the data sheet).
+ *
+ * Every wave of `workgroups` workgroups of 8 waves (two per SIMD, like the
+ * large GEMM) loads 12 operand fragments (32 bytes per lane, from positions
+ * spread over `ops`) and, for kind MXG_FMT_*, 3 scale registers (from
+ * `scales`), then runs `iters` rounds of the GEMM's compute phase: 32
+ * 16x16x128 scaled MFMAs of that format pair (8 A x 4 B fragments).  For kind
+ * MXG_CEIL_FP16 it runs 64 fp16 16x16x32 MFMAs per round on fp16 bits from
+ * `ops` (scales unused).  Flops per launch: workgroups * 8 * iters * 32 *
+ * 65536 (fp16: workgroups * 8 * iters * 64 * 16384).
+ *
+ *   ops          device, >= 32 bytes, 16-byte aligned (read only): operand codes
+ *   scales       device, >= 4 bytes, 4-byte aligned (read only); NULL for fp16
+ *   kind         MXG_FMT_* or MXG_CEIL_FP16
+ *   iters        1 .. 2^30;  workgroups  1 .. 2^20
+ *   out          device, workgroups * 512 floats, 16-byte aligned (written):
+ *                per-lane sums of the accumulators (keeps the work live)
+ *   clocks       device, workgroups * 2 uint32, 4-byte aligned (written), or
+ *                NULL: for each workgroup, the shader-clock cycles
+ *                (s_memtime) and the 100 MHz constant-clock ticks
+ *                (s_memrealtime) of its first wave's MFMA loop; their ratio
+ *                times 100 MHz is the shader clock under this load
+ * Returns MXG_OK or an error status.
+ */
+#define MXG_CEIL_FP16 16
+int mxgemm_mfma_ceiling(const void *ops, int64_t op_bytes, const uint8_t *scales,
+                        int64_t scale_bytes, int kind, int64_t iters, int workgroups,
+                        float *out, uint32_t *clocks, void *stream);
+
+/*
+ * mxgemm_device_supported - the hardware gate: 1 if the current HIP device is
+ * gfx950 (the only target this library is built for; its scaled fp8/fp4
+ * MFMA instructions exist nowhere else), 0 if not, a negative MXG_* status
+ * if the runtime cannot be queried.  Every other entry point applies the same
+ * check and returns MXG_EUNSUPPORTED instead of launching.  The RIGEL summary
+ * ("Resumo Técnico: RIGEL", section "Contradições e Portões de Versão")
+ * found its low-precision matrix formats present only behind a version gate
+ * and binaries refusing to load elsewhere; here the gate is explicit and
+ * queried at run time.  Thread-safe; the per-device answer is cached.
+ */
 int mxgemm_device_supported(void);
 
-/* Static, NUL-terminated description of a status code. */
+/*
+ * mxgemm_status_string - static, NUL-terminated description of a status
+ * code (never NULL; unknown codes get "unknown status").  Errors are
+ * reported as a status plus no side effect, the convention of the WWDC26
+ * session 330 summary, section "Scale Factor 付き量子化 tensor を作成する"
+ * (a failed creation returns an error object and a nil tensor): a call that
+ * returns nonzero has enqueued nothing and written nothing.
+ */
 const char *mxgemm_status_string(int status);
 
 #ifdef __cplusplus

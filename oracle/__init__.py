@@ -93,6 +93,8 @@ def _load():
     lib.mxref_epilogue.restype = ci
     lib.mxref_num_threads.argtypes = []
     lib.mxref_num_threads.restype = ci
+    lib.mxref_set_num_threads.argtypes = [ci]
+    lib.mxref_set_num_threads.restype = ci
     _lib = lib
     return lib
 
@@ -104,6 +106,11 @@ def _ptr(a: np.ndarray) -> int:
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
     return int(_load().mxref_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Set the threads of the oracle's OpenMP loops; returns the count in effect."""
+    return int(_load().mxref_set_num_threads(int(n)))
 
 
 # ----------------------------------------------------------------- tables

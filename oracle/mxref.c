@@ -435,6 +435,20 @@ int mxref_fp16_gemm_points(const uint16_t *A, const uint16_t *B, int64_t M,
     return 0;
 }
 
+/* Set the number of threads of the parallel loops (n >= 1); returns the
+ * number now in effect. */
+int mxref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* Number of threads the parallel loops above use. */
 int mxref_num_threads(void)
 {

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["mxgemm_quantize", "mxgemm_run", "fp16gemm_run", "mxgemm_run_dequant_fp16",
                                   "mxgemm_run_fused", "mxgemm_epilogue", "mxgemm_device_supported",
-                                  "mxgemm_status_string"])
+                                  "mxgemm_status_string", "mxgemm_mfma_ceiling"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -102,3 +102,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mxgemm, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(mxgemm.MXGemmError):
         mxgemm.raw_library()
+
+
+def test_ceiling_validation_codes(lib):
+    f = lib.mxgemm_mfma_ceiling
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    A = 0x1000
+    assert f(None, 4096, A, 64, 0, 10, 1, A, None, None) == 1        # null operands
+    assert f(A, 16, A, 64, 0, 10, 1, A, None, None) == 1             # fewer than 32 operand bytes
+    assert f(A, 4096, None, 0, 0, 10, 1, A, None, None) == 1         # MX kind without scales
+    assert f(A, 4096, A, 64, 9, 10, 1, A, None, None) == 1           # unknown kind
+    assert f(A, 4096, A, 64, 0, 0, 1, A, None, None) == 1            # no iterations
+    assert f(A, 4096, A, 64, 0, 10, 0, A, None, None) == 1           # no workgroups
+    assert f(0x1004, 4096, A, 64, 0, 10, 1, A, None, None) == 2      # misaligned operands
+    assert f(A, 4096, 0x1001, 64, 0, 10, 1, A, None, None) == 2      # misaligned scales
+    assert f(A, 4096, A, 64, 0, 10, 1, A, 0x1002, None) == 2         # misaligned clocks
