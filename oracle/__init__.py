@@ -34,6 +34,8 @@ import numpy as np
 E4M3 = 0
 E5M2 = 1
 E2M1 = 4
+INT4 = 8
+INT2 = 9
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mxref.c")
@@ -69,6 +71,10 @@ def _load():
     lib.mxref_e5m2_value.restype = ctypes.c_double
     lib.mxref_e2m1_value.argtypes = [ctypes.c_uint8]
     lib.mxref_e2m1_value.restype = ctypes.c_double
+    lib.mxref_int4_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_int4_value.restype = ctypes.c_double
+    lib.mxref_int2_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_int2_value.restype = ctypes.c_double
     lib.mxref_ue8m0_value.argtypes = [ctypes.c_uint8]
     lib.mxref_ue8m0_value.restype = ctypes.c_double
     lib.mxref_fp16_value.argtypes = [ctypes.c_uint16]
@@ -134,6 +140,18 @@ def e2m1_table() -> np.ndarray:
     return np.array([lib.mxref_e2m1_value(c) for c in range(16)], dtype=np.float64)
 
 
+def int4_table() -> np.ndarray:
+    """float64[16]: value of every two's complement INT4 code (-8..7)."""
+    lib = _load()
+    return np.array([lib.mxref_int4_value(c) for c in range(16)], dtype=np.float64)
+
+
+def int2_table() -> np.ndarray:
+    """float64[4]: value of every two's complement INT2 code (-2..1)."""
+    lib = _load()
+    return np.array([lib.mxref_int2_value(c) for c in range(4)], dtype=np.float64)
+
+
 def ue8m0_table() -> np.ndarray:
     """float64[256]: 2^(e-127) for every scale byte, NaN for 255."""
     lib = _load()
@@ -145,8 +163,13 @@ def fp16_value(bits: int) -> float:
 
 
 def row_bytes(K: int, elem: int) -> int:
-    """Bytes per operand row: K for E4M3 and E5M2, K/2 for packed E2M1."""
-    return K // 2 if elem == E2M1 else K
+    """Bytes per operand row: K for E4M3 and E5M2, K/2 for packed E2M1 and
+    INT4, K/4 for packed INT2."""
+    if elem in (E2M1, INT4):
+        return K // 2
+    if elem == INT2:
+        return K // 4
+    return K
 
 
 # --------------------------------------------------------------- quantize
@@ -154,8 +177,9 @@ def row_bytes(K: int, elem: int) -> int:
 def quantize(x: np.ndarray, elem: int):
     """Quantize fp32 rows (K contiguous) to (codes uint8, scales uint8).
 
-    codes: rows x K (E4M3, E5M2) or rows x K/2 (E2M1, even k in the low nibble);
-    scales: rows x K/32 UE8M0 bytes.
+    codes: rows x K (E4M3, E5M2), rows x K/2 (E2M1, INT4: even k in the low
+    nibble) or rows x K/4 (INT2: k in bits 2 (k mod 4)); scales: rows x K/32
+    UE8M0 bytes.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, K = x.shape
@@ -163,7 +187,7 @@ def quantize(x: np.ndarray, elem: int):
     s = np.zeros((rows, K // 32), dtype=np.uint8)
     rc = _load().mxref_quantize(_ptr(x), rows, K, elem, _ptr(q), _ptr(s))
     if rc != 0:
-        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E5M2/E2M1)")
+        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E5M2/E2M1/INT4/INT2)")
     return q, s
 
 

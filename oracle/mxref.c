@@ -36,6 +36,15 @@
  *     element codes 0.
  *   - E2M1 codes are packed two per byte, the even K index in the low nibble.
  *   - UE8M0 byte e means 2^(e-127); e = 255 is NaN.
+ *   - Integer elements (the 4-bit and 2-bit integer tensor types the WWDC26
+ *     session 330 summary lists, section "量子化データ型のネイティブサポート",
+ *     combined with a block-wise scale as its section "2-bit 量子化の限界圧縮
+ *     を探る" suggests): two's complement codes, INT4 in -8..7 (two per byte,
+ *     even K index in the low nibble) and INT2 in -2..1 (four per byte, K
+ *     index k in bits 2(k mod 4)); the block exponent takes emax = the
+ *     exponent of the largest power of two the range holds (2 for INT4, 0
+ *     for INT2), as emax does for the float formats; elements are rounded to
+ *     nearest, ties to even, and saturated to the range (+7 / -8, +1 / -2).
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,6 +56,24 @@
 #define MXREF_E4M3 0
 #define MXREF_E5M2 1
 #define MXREF_E2M1 4
+#define MXREF_INT4 8
+#define MXREF_INT2 9
+
+static int known_elem(int elem)
+{
+    return elem == MXREF_E4M3 || elem == MXREF_E5M2 || elem == MXREF_E2M1 ||
+           elem == MXREF_INT4 || elem == MXREF_INT2;
+}
+
+/* Bytes of one operand row of K elements. */
+static int64_t row_bytes(int elem, int64_t K)
+{
+    if (elem == MXREF_E2M1 || elem == MXREF_INT4)
+        return K / 2;
+    if (elem == MXREF_INT2)
+        return K / 4;
+    return K;
+}
 
 /* ---------------------------------------------------------------- decode */
 
@@ -89,6 +116,20 @@ double mxref_e2m1_value(uint8_t nibble)
     int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
     double v = (e == 0) ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
     return s ? -v : v;
+}
+
+/* Two's complement 4-bit code (0..15) -> -8..7. */
+double mxref_int4_value(uint8_t code)
+{
+    int c = code & 15;
+    return (double)(c < 8 ? c : c - 16);
+}
+
+/* Two's complement 2-bit code (0..3) -> -2..1. */
+double mxref_int2_value(uint8_t code)
+{
+    int c = code & 3;
+    return (double)(c < 2 ? c : c - 4);
 }
 
 /* UE8M0 scale byte -> 2^(e-127); 255 is NaN. */
@@ -190,8 +231,23 @@ static uint8_t encode_e2m1(double v)
     return (uint8_t)(code | (neg << 3));
 }
 
+/* Round v to the nearest integer (ties to even), saturate to [qmin, qmax],
+ * and return its two's complement code in `bits` bits. */
+static uint8_t encode_int(double v, int qmin, int qmax, int bits)
+{
+    double r = nearbyint(v); /* default mode: nearest, ties even */
+    int q;
+    if (r > qmax)
+        r = qmax;
+    if (r < qmin)
+        r = qmin;
+    q = (int)r;
+    return (uint8_t)(q & ((1 << bits) - 1));
+}
+
 /* Quantize X[rows][K] (fp32, K contiguous) to codes Q and scales S.
- *   E4M3, E5M2: Q is rows x K bytes.   E2M1: Q is rows x K/2 bytes, two per byte.
+ *   E4M3, E5M2: Q is rows x K bytes.   E2M1, INT4: Q is rows x K/2 bytes, two
+ *   per byte.   INT2: Q is rows x K/4 bytes, four per byte.
  *   S is rows x K/32 UE8M0 bytes.
  * Returns 0, or -1 on a bad argument (K not a multiple of 32, unknown elem). */
 int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
@@ -207,6 +263,10 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
         emax = 15; /* 57344 = 1.75 * 2^15 */
     else if (elem == MXREF_E2M1)
         emax = 2; /* 6 = 1.5 * 2^2 */
+    else if (elem == MXREF_INT4)
+        emax = 2; /* 4 <= 7 < 8 */
+    else if (elem == MXREF_INT2)
+        emax = 0; /* 1 */
     else
         return -1;
 
@@ -227,8 +287,10 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
                 s[r * nb + b] = 255;
                 for (i = 0; i < 32; i++) {
                     int64_t k = b * 32 + i;
-                    if (elem != MXREF_E2M1)
+                    if (elem == MXREF_E4M3 || elem == MXREF_E5M2)
                         q[r * K + k] = 0;
+                    else if (elem == MXREF_INT2)
+                        q[r * (K / 4) + k / 4] &= (uint8_t)~(3u << (2 * (k & 3)));
                     else
                         q[r * (K / 2) + k / 2] &= (uint8_t)((k & 1) ? 0x0F : 0xF0);
                 }
@@ -247,8 +309,13 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
                     q[r * K + k] = encode_e4m3(v);
                 } else if (elem == MXREF_E5M2) {
                     q[r * K + k] = encode_e5m2(v);
+                } else if (elem == MXREF_INT2) {
+                    uint8_t c = encode_int(v, -2, 1, 2);
+                    uint8_t *p = q + r * (K / 4) + k / 4;
+                    int sh = 2 * (int)(k & 3);
+                    *p = (uint8_t)((*p & ~(3u << sh)) | (c << sh));
                 } else {
-                    uint8_t nib = encode_e2m1(v);
+                    uint8_t nib = (elem == MXREF_INT4) ? encode_int(v, -8, 7, 4) : encode_e2m1(v);
                     uint8_t *p = q + r * (K / 2) + k / 2;
                     if (k & 1)
                         *p = (uint8_t)((*p & 0x0F) | (nib << 4));
@@ -263,7 +330,7 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
 
 /* ------------------------------------------------------------------ GEMM */
 
-static double tab_e4m3[256], tab_e5m2[256], tab_e2m1[16], tab_ue8m0[256];
+static double tab_e4m3[256], tab_e5m2[256], tab_e2m1[16], tab_int4[16], tab_int2[4], tab_ue8m0[256];
 static int tabs_ready = 0;
 
 static void make_tables(void)
@@ -277,6 +344,10 @@ static void make_tables(void)
         tab_e5m2[i] = mxref_e5m2_value((uint8_t)i);
     for (i = 0; i < 16; i++)
         tab_e2m1[i] = mxref_e2m1_value((uint8_t)i);
+    for (i = 0; i < 16; i++)
+        tab_int4[i] = mxref_int4_value((uint8_t)i);
+    for (i = 0; i < 4; i++)
+        tab_int2[i] = mxref_int2_value((uint8_t)i);
     for (i = 0; i < 256; i++)
         tab_ue8m0[i] = mxref_ue8m0_value((uint8_t)i);
     tabs_ready = 1;
@@ -289,6 +360,10 @@ static double element(const uint8_t *row, int elem, int64_t k)
         return tab_e4m3[row[k]];
     if (elem == MXREF_E5M2)
         return tab_e5m2[row[k]];
+    if (elem == MXREF_INT4)
+        return tab_int4[(row[k >> 1] >> ((k & 1) * 4)) & 15];
+    if (elem == MXREF_INT2)
+        return tab_int2[(row[k >> 2] >> ((k & 3) * 2)) & 3];
     return tab_e2m1[(row[k >> 1] >> ((k & 1) * 4)) & 15];
 }
 
@@ -311,8 +386,8 @@ static void mx_point(const uint8_t *A, const uint8_t *sA, int elemA,
                      double *smax_out)
 {
     int64_t nb = K / 32;
-    int64_t rowbytesA = (elemA == MXREF_E2M1) ? K / 2 : K;
-    int64_t rowbytesB = (elemB == MXREF_E2M1) ? K / 2 : K;
+    int64_t rowbytesA = row_bytes(elemA, K);
+    int64_t rowbytesB = row_bytes(elemB, K);
     const uint8_t *ra = A + i * rowbytesA, *rb = B + j * rowbytesB;
     double acc = 0.0, acc_abs = 0.0, smax_sum = 0.0, step_max = 0.0;
     for (int64_t b = 0; b < nb; b++) {
@@ -349,8 +424,7 @@ int mxref_gemm(const uint8_t *A, const uint8_t *sA, int elemA,
 {
     if (K <= 0 || K % 32 != 0 || M < 0 || N < 0)
         return -1;
-    if ((elemA != MXREF_E4M3 && elemA != MXREF_E5M2 && elemA != MXREF_E2M1) ||
-        (elemB != MXREF_E4M3 && elemB != MXREF_E5M2 && elemB != MXREF_E2M1))
+    if (!known_elem(elemA) || !known_elem(elemB))
         return -1;
     make_tables();
 #pragma omp parallel for schedule(dynamic, 1)
@@ -371,8 +445,7 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *sA, int elemA,
 {
     if (K <= 0 || K % 32 != 0)
         return -1;
-    if ((elemA != MXREF_E4M3 && elemA != MXREF_E5M2 && elemA != MXREF_E2M1) ||
-        (elemB != MXREF_E4M3 && elemB != MXREF_E5M2 && elemB != MXREF_E2M1))
+    if (!known_elem(elemA) || !known_elem(elemB))
         return -1;
     for (int64_t p = 0; p < npts; p++)
         if (I[p] < 0 || I[p] >= M || J[p] < 0 || J[p] >= N)
