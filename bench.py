@@ -459,45 +459,50 @@ def mx_operands(name, dev):
     ta = torch.from_numpy(a32).to(dev)
     tb = torch.from_numpy(b32).to(dev)
     del a32, b32
-    elem = {"e4m3": mx.E4M3, "e5m2": mx.E5M2, "e2m1": mx.E2M1}
+    elem = {"e4m3": mx.E4M3, "e5m2": mx.E5M2, "e2m1": mx.E2M1, "int4": mx.INT4, "int2": mx.INT2}
     qa, sa = mx.mxgemm_quantize(ta, elem[w.elem_a])
     qb, sb = mx.mxgemm_quantize(tb, elem[w.elem_b])
     torch.cuda.synchronize()
     return w, ta, tb, qa, sa, qb, sb
 
 
-def bench_decode(dev):
-    """MXFP8 activations x MXFP4 weights, 16 x 28672 x 8192, weights rotated
-    over copies larger in total than the MALL so every launch reads HBM."""
+def bench_decode(dev, name="decode_16x28672x8192"):
+    """MXFP8 activations x the workload's weights (E2M1, INT4 or INT2),
+    16 x 28672 x 8192, weights rotated over copies larger in total than the
+    MALL so every launch reads HBM."""
     import torch
 
     from block_scaled_precision_mxgemm_amd import inputs as mxin
     from block_scaled_precision_mxgemm_amd import mxgemm as mx
 
-    w = mxin.WORKLOADS["decode_16x28672x8192"]
+    w = mxin.WORKLOADS[name]
+    elem, fmt, kname = {"e2m1": (mx.E2M1, mx.FMT_FP8_FP4, "fp4"), "int4": (mx.INT4, mx.FMT_FP8_INT4, "int4"),
+                        "int2": (mx.INT2, mx.FMT_FP8_INT2, "int2")}[w.elem_b]
     a32, _ = mxin.mx_sources(w, N=1)
     qa, sa = mx.mxgemm_quantize(torch.from_numpy(a32).to(dev), mx.E4M3)
-    copies = 5
+    wb = w.N * w.K // (2 if elem != mx.INT2 else 4)
+    copies = max(5, int(math.ceil(600e6 / (wb + w.N * w.K // 32))))   # > 2x the 256 MB MALL in total
     weights = []
     for b32 in mxin.decode_weight_copies(w, copies):
         tb = torch.from_numpy(b32).to(dev)
         del b32
-        weights.append(mx.mxgemm_quantize(tb, mx.E2M1))
+        weights.append(mx.mxgemm_quantize(tb, elem))
         del tb
     torch.cuda.synchronize()
     c = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-    nbytes = (w.M * w.K + w.M * w.K // 32 + w.N * w.K // 2 + w.N * w.K // 32 + w.M * w.N * 4)
-    cold = time_windows(lambda i=0: mx.mxgemm_run(qa, sa, weights[i % copies][0], weights[i % copies][1],
-                                                   mx.FMT_FP8_FP4, out=c))
-    warm = time_windows(lambda i=0: mx.mxgemm_run(qa, sa, weights[0][0], weights[0][1], mx.FMT_FP8_FP4, out=c))
+    nbytes = (w.M * w.K + w.M * w.K // 32 + wb + w.N * w.K // 32 + w.M * w.N * 4)
+    cold = time_windows(lambda i=0: mx.mxgemm_run(qa, sa, weights[i % copies][0], weights[i % copies][1], fmt,
+                                                   out=c))
+    warm = time_windows(lambda i=0: mx.mxgemm_run(qa, sa, weights[0][0], weights[0][1], fmt, out=c))
     rec = timed_entry(cold, nbytes=nbytes)
-    rec.update({"kernel": "decode_kernel<fp8 x fp4, K=8192> (LDS-staged weight stream)", "us": rec["ms"] * 1e3,
-                "us_best": rec["ms_min"] * 1e3, "algorithmic_bytes": nbytes,
-                "traffic": traffic_entry("decode_16x28672x8192"), "weight_copies_rotated": copies,
-                "warm_us_mall_resident": warm["ms_median"] * 1e3,
+    rec.update({"kernel": "decode_kernel<fp8 x %s, K=8192> (LDS-staged weight stream)" % kname,
+                "us": rec["ms"] * 1e3, "us_best": rec["ms_min"] * 1e3, "algorithmic_bytes": nbytes,
+                "weight_copies_rotated": copies, "warm_us_mall_resident": warm["ms_median"] * 1e3,
                 "warm_GB/s": nbytes / (warm["ms_median"] * 1e-3) / 1e9})
-    log("decode: cold %.2f us (%.0f GB/s, %.1f%% of HBM), warm %.2f us" % (rec["us"], rec["GB/s"],
-                                                                          100 * rec["hbm_frac"], warm["ms_median"] * 1e3))
+    if name == "decode_16x28672x8192":
+        rec["traffic"] = traffic_entry("decode_16x28672x8192")
+    log("%s: cold %.2f us (%.0f GB/s, %.1f%% of HBM), warm %.2f us" % (
+        name, rec["us"], rec["GB/s"], 100 * rec["hbm_frac"], warm["ms_median"] * 1e3))
     return rec
 
 
@@ -507,7 +512,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["all", "headline", "decode", "fp16", "prefill", "small", "ceiling"],
+    ap.add_argument("--only", choices=["all", "headline", "decode", "int", "fp16", "prefill", "small", "ceiling"],
                     default="all", help="run a subset (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for each of the two sampled large configurations")
@@ -679,6 +684,9 @@ def main():
 
     if only in ("all", "decode"):
         extra["decode_16x28672x8192"] = bench_decode(dev)
+    if only in ("all", "decode", "int"):
+        for name in ("decode_int4_16x28672x8192", "decode_int2_16x28672x8192"):
+            extra[name] = bench_decode(dev, name)
 
     cpu = None
     if not args.no_cpu_baseline and only == "all":

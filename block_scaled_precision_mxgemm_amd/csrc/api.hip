@@ -36,7 +36,7 @@ int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* 
                 int64_t N, int64_t K, int fmt) {
   if (!A || !SA || !B || !SB || !C) return MXG_EINVAL;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
-  if (fmt < MXG_FMT_FP8_FP8 || fmt > MXG_FMT_BF8_FP8) return MXG_EINVAL;
+  if (fmt < MXG_FMT_FP8_FP8 || fmt > MXG_FMT_FP8_INT2) return MXG_EINVAL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXG_EALIGN;
   return MXG_OK;
 }
@@ -48,13 +48,31 @@ int validate_epi(const float* bias, int act, int out_type) {
   return MXG_OK;
 }
 
+bool int_weights(int fmt) { return fmt == MXG_FMT_FP8_INT4 || fmt == MXG_FMT_FP8_INT2; }
+
 // Kernel choice for an MX product (arguments validated): the weight-streaming
 // decode kernel, the split-K skinny kernel (both for E4M3 activations against
-// E4M3 or E2M1 weights), or the tiled / ping-pong kernels (every format pair).
+// E4M3, E2M1, INT4 or INT2 weights), or the tiled / ping-pong kernels (every
+// float format pair).  Integer weights with more than 64 rows of activations
+// run the split-K kernel once per 64 rows (B is read once per 64 rows: a
+// correct path for such shapes, not a tuned one).
 int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
            int64_t N, int64_t K, int fmt, hipStream_t st) {
   if (mxg::decode_ok(M, K, fmt, SA, SB, e)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
-  if (M <= mxg::kSkinnyMaxM && (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4)) {
+  if (int_weights(fmt) && M > mxg::kSkinnyMaxM) {
+    const int64_t eb = mxg::epi_elem_bytes(e.out);
+    for (int64_t m0 = 0; m0 < M; m0 += mxg::kSkinnyMaxM) {
+      mxg::Epi ec = e;
+      ec.C = (uint8_t*)e.C + m0 * N * eb;
+      const int64_t mc = M - m0 < mxg::kSkinnyMaxM ? M - m0 : mxg::kSkinnyMaxM;
+      const hipError_t err = mxg::launch_mx_skinny((const uint8_t*)A + m0 * K, SA + m0 * (K / 32), B, SB, ec, mc,
+                                                   N, K, fmt, st);
+      if (err != hipSuccess) return to_status(err);
+    }
+    return MXG_OK;
+  }
+  if (M <= mxg::kSkinnyMaxM &&
+      (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4 || int_weights(fmt))) {
     // K not a multiple of 1024, up to 16 rows, fp32 C: the decode kernel
     // takes the largest multiple of 1024 below K, the split-K kernel adds the
     // rest (with more rows the split-K kernel alone measured faster at
@@ -76,6 +94,7 @@ static_assert(MXG_OUT_F32 == mxg::kOutF32 && MXG_OUT_BF16 == mxg::kOutBF16 && MX
 static_assert(MXG_ACT_NONE == mxg::kActNone && MXG_ACT_GELU == mxg::kActGelu, "activation ids");
 static_assert(MXG_ELEM_E4M3 == mxg::kFmtFp8 && MXG_ELEM_E5M2 == mxg::kFmtBf8 && MXG_ELEM_E2M1 == mxg::kFmtFp4,
               "element ids are the MFMA format ids");
+static_assert(MXG_ELEM_INT4 == mxg::kElemInt4 && MXG_ELEM_INT2 == mxg::kElemInt2, "integer element ids");
 
 }  // namespace
 
@@ -108,7 +127,9 @@ int mxgemm_device_supported(void) {
 int mxgemm_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, uint8_t* S, void* stream) {
   if (!X || !Q || !S) return MXG_EINVAL;
   if (!dim_ok(rows) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
-  if (elem != MXG_ELEM_E4M3 && elem != MXG_ELEM_E5M2 && elem != MXG_ELEM_E2M1) return MXG_EINVAL;
+  if (elem != MXG_ELEM_E4M3 && elem != MXG_ELEM_E5M2 && elem != MXG_ELEM_E2M1 && elem != MXG_ELEM_INT4 &&
+      elem != MXG_ELEM_INT2)
+    return MXG_EINVAL;
   if (!aligned16(X) || !aligned16(Q)) return MXG_EALIGN;
   const int d = check_device();
   if (d != MXG_OK) return d;

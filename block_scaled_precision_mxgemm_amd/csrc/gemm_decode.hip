@@ -81,14 +81,22 @@ struct DecArgs {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Weight formats W: kFmtFp8 (E4M3, 128 bytes per 128-k MFMA operand),
+// kFmtFp4 (E2M1, 64 bytes), kElemInt4 (64 bytes, remapped in registers to
+// an E4M3 operand), kElemInt2 (32 bytes, remapped to an E2M1 operand).
+constexpr int op_bytes(int w) { return w == kFmtFp8 ? 128 : w == kElemInt2 ? 32 : 64; }
+// MFMA operand format the weights are fed as
+constexpr int mfma_fmt(int w) { return (w == kFmtFp8 || w == kElemInt4) ? kFmtFp8 : kFmtFp4; }
+
 // K / 1024 = KW MFMAs (128 k each) per wave per fragment on average.  With
-// E2M1 weights (64 bytes per MFMA operand, two per 128-byte stage) and KW
-// odd, waves 0-3 take KW + 1 MFMAs and waves 4-7 KW - 1.
-constexpr bool split_k(bool bf4, int kw) { return bf4 && kw % 2 == 1; }
+// two MFMA operands per 128-byte stage (E2M1, INT4) and KW odd, waves 0-3
+// take KW + 1 MFMAs and waves 4-7 KW - 1.  (INT2, four operands per stage,
+// takes K / 1024 multiples of 4 only.)
+constexpr bool split_k(int w, int kw) { return op_bytes(w) == 64 && kw % 2 == 1; }
 
 // LDS of one wave's ring and scale slots for WK MFMAs per fragment
-constexpr int ring_bytes(bool bf4, int wk, int d) {
-  const int nq = bf4 ? wk / 2 : wk;
+constexpr int ring_bytes(int w, int wk, int d) {
+  const int nq = wk / (128 / op_bytes(w));
   const int nsi = (16 * wk + 63) / 64;
   const int nsl = (nq - 1 + d + nq - 1) / nq;
   return d * kStageBytes + nsl * nsi * 256;
@@ -98,13 +106,14 @@ constexpr int ring_bytes(bool bf4, int wk, int d) {
 // for waves 0-3 and -1 for waves 4-7 under the uneven split, else 0).  MB:
 // blocks of 16 activation rows (M <= 16 MB); each weight operand read from
 // LDS feeds one MFMA per block, so the weight stream is the same for every MB.
-template <bool BF4, int KW, int MB, int D_, int XK>
+template <int W, int KW, int MB, int D_, int XK>
 struct Decode {
   static constexpr int D = D_;
   static constexpr int WK = KW + XK;                     // MFMAs per fragment of this wave
-  static constexpr int MPS = BF4 ? 2 : 1;                // MFMAs per stage (128 bytes of a row)
+  static constexpr int OPB = op_bytes(W);                // bytes of a weight row per MFMA
+  static constexpr int MPS = 128 / OPB;                  // MFMAs per stage (128 bytes of a row)
   static constexpr int NQ = WK / MPS;                    // stages per fragment
-  static constexpr int OPB = BF4 ? 64 : 128;             // bytes of a weight row per MFMA
+  static constexpr int kBFmt = mfma_fmt(W);              // MFMA format of the weight operand
   static constexpr int SBW = 4 * WK;                     // scale bytes of a row per wave
   static constexpr int LPR = SBW / 4;                    // scale copy lanes per row (4 bytes each)
   static constexpr int NSI = (16 * LPR + 63) / 64;       // scale copies per fragment
@@ -112,10 +121,10 @@ struct Decode {
   static constexpr int NSL = (NQ - 1 + D + NQ - 1) / NQ;
   static constexpr int SZ_SC = NSI * 256;
   // every wave's region has the size of the larger wave kind's
-  static constexpr int SZ_WAVE = XK == 0 ? ring_bytes(BF4, WK, D)
-                                         : (ring_bytes(BF4, KW + 1, D) > ring_bytes(BF4, KW - 1, D)
-                                                ? ring_bytes(BF4, KW + 1, D)
-                                                : ring_bytes(BF4, KW - 1, D));
+  static constexpr int SZ_WAVE = XK == 0 ? ring_bytes(W, WK, D)
+                                         : (ring_bytes(W, KW + 1, D) > ring_bytes(W, KW - 1, D)
+                                                ? ring_bytes(W, KW + 1, D)
+                                                : ring_bytes(W, KW - 1, D));
   static constexpr int OFF_PART = kDecWaves * SZ_WAVE;
   static constexpr int SZ_PSLOT = MB * kDecWaves * 64 * 16;  // one fragment's partials
   static constexpr int LDS = OFF_PART + 2 * SZ_PSLOT;
@@ -125,11 +134,11 @@ struct Decode {
   static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8, NS4 = (SBW % 8) / 4;
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
   static_assert(NQ >= 1 && WK % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
-  static_assert(ring_bytes(BF4, WK, D) == D * kStageBytes + NSL * SZ_SC && SZ_WAVE >= ring_bytes(BF4, WK, D),
+  static_assert(ring_bytes(W, WK, D) == D * kStageBytes + NSL * SZ_SC && SZ_WAVE >= ring_bytes(W, WK, D),
                 "region layout");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
   static_assert(MB >= 1 && MB * WK <= 16, "A operands of all blocks in 128 VGPRs");
-  static_assert(XK == 0 || split_k(BF4, KW), "uneven split only for E2M1 weights with K / 1024 odd");
+  static_assert(XK == 0 || split_k(W, KW), "uneven split only for two operands per stage with K / 1024 odd");
 
   // first MFMA (128 k) of wave w's band: w KW, shifted by the uneven split
   static __device__ __forceinline__ int band_start(int w) { return w * KW + (XK > 0 ? w : XK < 0 ? 8 - w : 0); }
@@ -333,19 +342,42 @@ struct Decode {
     for (int u = 0; u < MPS; u++) {
       const int j = Q * MPS + u;  // this wave's MFMA index inside the fragment
       v8i bv;
-      if (BF4) {
+      if constexpr (W == kFmtFp4) {
+        // lane group g: k 32g .. 32g+31 of operand u (16 bytes)
         const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 * u + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-      } else {
+      } else if constexpr (W == kFmtFp8) {
+        // lane group g: k 16g .. 16g+15 and 64+16g .. 64+16g+15
         const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + ((g ^ sw) << 4));
         const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else if constexpr (W == kElemInt4) {
+        const uint8_t* row = st + r * kBand;
+        // the fp8 operand's k ranges, 8 bytes of INT4 codes each (bytes 8g
+        // and 32 + 8g of operand u), remapped to E4M3 codes
+        const v2i lo = *reinterpret_cast<const v2i*>(row + (((4 * u + (g >> 1)) ^ sw) << 4) + 8 * (g & 1));
+        const v2i hi = *reinterpret_cast<const v2i*>(row + (((4 * u + 2 + (g >> 1)) ^ sw) << 4) + 8 * (g & 1));
+        uint32_t e[8];
+        int4x8_to_e4m3((uint32_t)lo[0], e[0], e[1]);
+        int4x8_to_e4m3((uint32_t)lo[1], e[2], e[3]);
+        int4x8_to_e4m3((uint32_t)hi[0], e[4], e[5]);
+        int4x8_to_e4m3((uint32_t)hi[1], e[6], e[7]);
+        bv = v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], (int)e[4], (int)e[5], (int)e[6], (int)e[7]};
+      } else {
+        // the fp4 operand's k range, 8 bytes of INT2 codes (byte 8g of
+        // operand u), remapped to E2M1 codes
+        const uint8_t* row = st + r * kBand;
+        const v2i c = *reinterpret_cast<const v2i*>(row + (((2 * u + (g >> 1)) ^ sw) << 4) + 8 * (g & 1));
+        uint32_t e[4];
+        int2x16_to_e2m1((uint32_t)c[0], e[0], e[1]);
+        int2x16_to_e2m1((uint32_t)c[1], e[2], e[3]);
+        bv = v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], 0, 0, 0, 0};
       }
       const int sb = sc[r * SBW + 4 * j + g];
 #pragma unroll
       for (int mb = 0; mb < MB; mb++)
         t.acc[mb][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bv, t.av[mb][j], t.acc[mb][u], BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8, 0, sb, 0,
+            bv, t.av[mb][j], t.acc[mb][u], kBFmt, kFmtFp8, 0, sb, 0,
             (int)__builtin_amdgcn_ubfe(t.sa[mb][j], 8 * g, 8));
     }
   }
@@ -400,7 +432,7 @@ struct Decode {
     // has at least one: the grid is at most the fragment count)
     t.f_begin = (int)((int64_t)a.nfrags * blockIdx.x / gridDim.x);
     t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
-    t.rb = BF4 ? (uint32_t)(a.ldk >> 1) : (uint32_t)a.ldk;
+    t.rb = (uint32_t)(a.ldk / (128 / OPB));
     t.nb = (uint32_t)(a.ldk >> 5);
     // copy lane l: row l >> 3 (+8), physical chunk l & 7 holding logical chunk
     // (l & 7) ^ ((row >> 1) & 7)
@@ -435,28 +467,28 @@ struct Decode {
 };
 
 // the kernel's layout (the same for both wave kinds of an uneven split)
-template <bool BF4, int KW, int MB, int D>
-using DecLayout = Decode<BF4, KW, MB, D, split_k(BF4, KW) ? 1 : 0>;
+template <int W, int KW, int MB, int D>
+using DecLayout = Decode<W, KW, MB, D, split_k(W, KW) ? 1 : 0>;
 
-template <bool BF4, int KW, int MB, int D>
+template <int W, int KW, int MB, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void decode_kernel(DecArgs a) {
-  static_assert(DecLayout<BF4, KW, MB, D>::FITS, "fits the 160 KiB LDS of a gfx950 CU");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DecLayout<BF4, KW, MB, D>::LDS];
-  if constexpr (split_k(BF4, KW)) {
-    static_assert(Decode<BF4, KW, MB, D, 1>::LDS == Decode<BF4, KW, MB, D, -1>::LDS, "one layout");
+  static_assert(DecLayout<W, KW, MB, D>::FITS, "fits the 160 KiB LDS of a gfx950 CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DecLayout<W, KW, MB, D>::LDS];
+  if constexpr (split_k(W, KW)) {
+    static_assert(Decode<W, KW, MB, D, 1>::LDS == Decode<W, KW, MB, D, -1>::LDS, "one layout");
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-      Decode<BF4, KW, MB, D, 1>::run(a, smem);
+      Decode<W, KW, MB, D, 1>::run(a, smem);
     else
-      Decode<BF4, KW, MB, D, -1>::run(a, smem);
+      Decode<W, KW, MB, D, -1>::run(a, smem);
   } else {
-    Decode<BF4, KW, MB, D, 0>::run(a, smem);
+    Decode<W, KW, MB, D, 0>::run(a, smem);
   }
 }
 
-template <bool BF4, int KW, int MB, int D = kDecStages>
+template <int W, int KW, int MB, int D = kDecStages>
 hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
   const int grid = a.nfrags < cus ? a.nfrags : cus;
-  hipLaunchKernelGGL((decode_kernel<BF4, KW, MB, D>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<W, KW, MB, D>), dim3(grid), dim3(kDecWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -464,37 +496,49 @@ hipError_t launch_dec(const DecArgs& a, int cus, hipStream_t stream) {
 // fit 128 registers per lane (MB KW <= 16).
 constexpr int max_blocks(int kw) { return kw <= 4 ? 4 : kw <= 8 ? 2 : 1; }
 
-template <bool BF4, int KW>
+template <int W, int KW>
 hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
   if (a.M <= 16 || max_blocks(KW) == 1) {
     // few weight fragments per CU: the ring covers a whole fragment
-    if constexpr (DecLayout<BF4, KW, 1, kDecStagesDeep>::FITS) {
-      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<BF4, KW, 1, kDecStagesDeep>(a, cus, stream);
+    if constexpr (DecLayout<W, KW, 1, kDecStagesDeep>::FITS) {
+      if (a.nfrags <= kDeepMaxFrags * cus) return launch_dec<W, KW, 1, kDecStagesDeep>(a, cus, stream);
     }
-    return launch_dec<BF4, KW, 1>(a, cus, stream);
+    return launch_dec<W, KW, 1>(a, cus, stream);
   }
-  if (a.M <= 32 || max_blocks(KW) == 2) return launch_dec<BF4, KW, (max_blocks(KW) >= 2 ? 2 : 1)>(a, cus, stream);
-  return launch_dec<BF4, KW, max_blocks(KW)>(a, cus, stream);
+  if (W == kElemInt2 || a.M <= 32 || max_blocks(KW) == 2)  // INT2: at most 2 blocks (decode_ok)
+    return launch_dec<W, KW, (max_blocks(KW) >= 2 ? 2 : 1)>(a, cus, stream);
+  if constexpr (W != kElemInt2) return launch_dec<W, KW, max_blocks(KW)>(a, cus, stream);
+  return hipErrorInvalidValue;
 }
 
 // Largest K / 1024: with fp8 weights (one MFMA per stage) the per-stage
-// state of 14 or 16 MFMAs per wave no longer fits beside the A operands.
-constexpr int max_kw(bool bf4) { return bf4 ? 16 : 12; }
+// state of 14 or 16 MFMAs per wave no longer fits beside the A operands, and
+// with INT4 weights the remapped operands of 16 MFMAs per wave (the compiler
+// spills above 14).
+constexpr int max_kw(int w) { return w == kFmtFp8 ? 12 : w == kElemInt4 ? 14 : 16; }
+// K / 1024 the kernel takes for a weight format: INT2 stages hold four MFMA
+// operands, so every wave's band must be whole stages without a split
+constexpr bool kw_ok(int w, int kw) { return kw >= 2 && kw <= max_kw(w) && (w != kElemInt2 || kw % 4 == 0); }
 
-template <bool BF4, int KW>
+template <int W, int KW>
 hipError_t launch_dec_kw(const DecArgs& a, int cus, hipStream_t stream) {
-  if constexpr (KW > max_kw(BF4)) {
+  if constexpr (!kw_ok(W, KW)) {
     return hipErrorInvalidValue;  // excluded by decode_ok
   } else {
-    return launch_dec_m<BF4, KW>(a, cus, stream);
+    return launch_dec_m<W, KW>(a, cus, stream);
   }
 }
 
-template <bool BF4, int... KW>
+template <int W, int... KW>
 hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream, std::integer_sequence<int, KW...>) {
   hipError_t err = hipErrorInvalidValue;  // K / 1024 outside 2 .. 16: excluded by decode_ok
-  ((a.K == 1024 * (KW + 2) ? (err = launch_dec_kw<BF4, KW + 2>(a, cus, stream), 0) : 0), ...);
+  ((a.K == 1024 * (KW + 2) ? (err = launch_dec_kw<W, KW + 2>(a, cus, stream), 0) : 0), ...);
   return err;
+}
+
+// weight format of a (validated) format pair taken by the decode kernel
+int weight_format(int fmt) {
+  return fmt == 1 ? kFmtFp4 : fmt == 6 ? kElemInt4 : fmt == 7 ? kElemInt2 : kFmtFp8;
 }
 
 // Rows of A one launch covers: 64 for K <= 4096, 32 for K <= 8192, 16
@@ -511,11 +555,17 @@ int chunk_kw(int kw, int P, int i) { return kw / P + (i < kw % P ? 1 : 0); }
 
 }  // namespace
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB, const Epi& e) {
-  if (!(M <= 64 && (fmt == 0 || fmt == 1) && (K % 1024) == 0 && K >= 2048 && (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0))
+  if (!(M <= 64 && (fmt == 0 || fmt == 1 || fmt == 6 || fmt == 7) && (K % 1024) == 0 && K >= 2048 &&
+        (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0))
     return false;
+  const int w = weight_format(fmt);
+  // INT2: every chunk a multiple of 4096, and at most two blocks of 16 rows
+  // (four blocks of A operands beside four remapped weight operands per
+  // stage do not fit the registers)
+  if (w == kElemInt2 && ((K % 4096) != 0 || M > 32)) return false;
   // above one launch's K range the running sum is kept in C between chunks,
   // which needs fp32 output
-  return K <= 1024 * max_kw(fmt == 1) || (e.out == kOutF32 && K <= kDecMaxK);
+  return K <= 1024 * max_kw(w) || (e.out == kOutF32 && K <= kDecMaxK);
 }
 
 hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
@@ -536,17 +586,20 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
     // and only the last applies bias and activation; the order is fixed, so
     // the result is deterministic.
     const int blocks = (int)((M + 15) / 16);
-    const int limit = blocks <= 1 ? max_kw(fmt == 1) : blocks <= 2 ? 8 : 4;  // max_blocks(KW) >= the blocks
+    const int limit = blocks <= 1 ? max_kw(weight_format(fmt)) : blocks <= 2 ? 8 : 4;  // max_blocks(KW) >= the blocks
     P = (kw + limit - 1) / limit;
+    // INT2 chunks must stay multiples of 4096: the fewest such chunks
+    if (weight_format(fmt) == kElemInt2) P = (kw / 4 + limit / 4 - 1) / (limit / 4);
     step = 64;
   }
   // (16-bit C: each launch takes all of K, which decode_ok keeps in range,
   // and launches of fewer rows stream B again)
-  const int64_t wbytes = fmt == 1 ? 2 : 1;  // K elements per weight byte
+  const int w = weight_format(fmt);
+  const int64_t wbytes = 128 / op_bytes(w);  // K elements per weight byte
   for (int64_t m0 = 0; m0 < M && err == hipSuccess; m0 += step) {
     int64_t k0 = 0;
     for (int c = 0; c < P && err == hipSuccess; c++) {
-      const int64_t kc = 1024 * (int64_t)chunk_kw(kw, P, c);
+      const int64_t kc = w == kElemInt2 ? 4096 * (int64_t)chunk_kw(kw / 4, P, c) : 1024 * (int64_t)chunk_kw(kw, P, c);
       DecArgs a{};
       a.A = (const uint8_t*)A + m0 * K + k0;  // E4M3 activations: one byte per element
       a.SA = SA + m0 * (K / 32) + k0 / 32;
@@ -561,7 +614,10 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
       a.accum = c > 0;
       a.nfrags = (int)((N + 15) / 16);
       const auto kws = std::make_integer_sequence<int, 15>{};  // K / 1024 = 2 .. 16
-      err = fmt == 1 ? launch_dec_k<true>(a, cus, stream, kws) : launch_dec_k<false>(a, cus, stream, kws);
+      err = w == kFmtFp4     ? launch_dec_k<kFmtFp4>(a, cus, stream, kws)
+            : w == kElemInt4 ? launch_dec_k<kElemInt4>(a, cus, stream, kws)
+            : w == kElemInt2 ? launch_dec_k<kElemInt2>(a, cus, stream, kws)
+                             : launch_dec_k<kFmtFp8>(a, cus, stream, kws);
       k0 += kc;
     }
   }

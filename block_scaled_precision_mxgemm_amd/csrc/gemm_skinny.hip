@@ -40,8 +40,11 @@ struct SkArgs {
   int nslices;       // ceil(K / 128)
 };
 
-template <int MT, int NF, bool BF4, int U, int W>
+// WF: weight format (kFmtFp8, kFmtFp4, kElemInt4 or kElemInt2; the integer
+// codes are remapped in registers to E4M3 / E2M1 MFMA operands)
+template <int MT, int NF, int WF, int U, int W>
 struct Skinny {
+  static constexpr int BFMT = (WF == kFmtFp8 || WF == kElemInt4) ? kFmtFp8 : kFmtFp4;  // MFMA format of B
   struct Group {
     v8i a[U][MT];
     v8i b[U][NF];
@@ -62,6 +65,27 @@ struct Skinny {
     if (k0 + 32 * g < K) lo = *reinterpret_cast<const v4i*>(row + (k0 >> 1) + 16 * g);
     return v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
   }
+  // INT4 codes of the fp8 operand's k ranges (8 bytes each), remapped to E4M3
+  static __device__ __forceinline__ v8i load_int4(const uint8_t* row, int k0, int g, int K) {
+    v2i lo = {0, 0}, hi = {0, 0};
+    if (k0 + 16 * g < K) lo = *reinterpret_cast<const v2i*>(row + (k0 >> 1) + 8 * g);
+    if (k0 + 64 + 16 * g < K) hi = *reinterpret_cast<const v2i*>(row + (k0 >> 1) + 32 + 8 * g);
+    uint32_t e[8];
+    int4x8_to_e4m3((uint32_t)lo[0], e[0], e[1]);
+    int4x8_to_e4m3((uint32_t)lo[1], e[2], e[3]);
+    int4x8_to_e4m3((uint32_t)hi[0], e[4], e[5]);
+    int4x8_to_e4m3((uint32_t)hi[1], e[6], e[7]);
+    return v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], (int)e[4], (int)e[5], (int)e[6], (int)e[7]};
+  }
+  // INT2 codes of the fp4 operand's k range (8 bytes), remapped to E2M1
+  static __device__ __forceinline__ v8i load_int2(const uint8_t* row, int k0, int g, int K) {
+    v2i c = {0, 0};
+    if (k0 + 32 * g < K) c = *reinterpret_cast<const v2i*>(row + (k0 >> 2) + 8 * g);
+    uint32_t e[4];
+    int2x16_to_e2m1((uint32_t)c[0], e[0], e[1]);
+    int2x16_to_e2m1((uint32_t)c[1], e[2], e[3]);
+    return v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], 0, 0, 0, 0};
+  }
   static __device__ __forceinline__ int load_scale(const uint8_t* srow, int blk, int nb) {
     return (blk < nb) ? (int)srow[blk] : 127;
   }
@@ -79,7 +103,10 @@ struct Skinny {
         const int n = min(n0 + j * 16 + r, a.N - 1);
         const uint8_t* brow = a.B + (int64_t)n * a.ldb;
         if (live) {
-          G.b[u][j] = BF4 ? load_fp4(brow, k0, g, a.K) : load_fp8(brow, k0, g, a.K);
+          G.b[u][j] = WF == kFmtFp4     ? load_fp4(brow, k0, g, a.K)
+                      : WF == kElemInt4 ? load_int4(brow, k0, g, a.K)
+                      : WF == kElemInt2 ? load_int2(brow, k0, g, a.K)
+                                        : load_fp8(brow, k0, g, a.K);
           G.sb[u][j] = load_scale(a.SB + (int64_t)n * a.lds, sl * 4 + g, nb);
         } else {
           G.b[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -108,8 +135,8 @@ struct Skinny {
       for (int t = 0; t < MT; t++)
 #pragma unroll
         for (int j = 0; j < NF; j++)
-          acc[t][j] = mfma_scaled_16x16x128<BF4 ? kFmtFp4 : kFmtFp8, kFmtFp8>(G.b[u][j], G.a[u][t], acc[t][j],
-                                                                             G.sb[u][j], G.sa[u][t]);
+          acc[t][j] = mfma_scaled_16x16x128<BFMT, kFmtFp8>(G.b[u][j], G.a[u][t], acc[t][j], G.sb[u][j],
+                                                           G.sa[u][t]);
   }
 
   static __device__ __forceinline__ void run(const SkArgs& a) {
@@ -171,38 +198,38 @@ struct Skinny {
   }
 };
 
-template <int MT, int NF, bool BF4, int U, int W>
+template <int MT, int NF, int WF, int U, int W>
 __global__ __attribute__((amdgpu_flat_work_group_size(W * 64, W * 64))) void skinny_kernel(SkArgs a) {
-  Skinny<MT, NF, BF4, U, W>::run(a);
+  Skinny<MT, NF, WF, U, W>::run(a);
 }
 
-template <int MT, int NF, bool BF4, int U, int W = 4>
+template <int MT, int NF, int WF, int U, int W = 4>
 hipError_t launch_sk(const SkArgs& a, hipStream_t stream) {
   const int grid = (a.N + NF * 16 - 1) / (NF * 16);
-  hipLaunchKernelGGL((skinny_kernel<MT, NF, BF4, U, W>), dim3(grid), dim3(W * 64), 0, stream, a);
+  hipLaunchKernelGGL((skinny_kernel<MT, NF, WF, U, W>), dim3(grid), dim3(W * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 // Column width (fragments per workgroup) and K split: the widest of NFMAX,
 // 2, 1 fragments that still gives every CU a workgroup, with 8 waves
 // splitting K when narrower than NFMAX.
-template <int MT, int NFMAX, bool BF4>
+template <int MT, int NFMAX, int WF>
 hipError_t launch_by_n(const SkArgs& a, hipStream_t stream) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   const int64_t frags = (a.N + 15) / 16;
-  if (frags >= NFMAX * (int64_t)cus) return launch_sk<MT, NFMAX, BF4, 2, 4>(a, stream);
-  if (NFMAX > 2 && frags >= 2 * (int64_t)cus) return launch_sk<MT, (NFMAX > 2 ? 2 : 1), BF4, 2, 8>(a, stream);
-  return launch_sk<MT, 1, BF4, 2, 8>(a, stream);
+  if (frags >= NFMAX * (int64_t)cus) return launch_sk<MT, NFMAX, WF, 2, 4>(a, stream);
+  if (NFMAX > 2 && frags >= 2 * (int64_t)cus) return launch_sk<MT, (NFMAX > 2 ? 2 : 1), WF, 2, 8>(a, stream);
+  return launch_sk<MT, 1, WF, 2, 8>(a, stream);
 }
 
-template <bool BF4>
+template <int WF>
 hipError_t launch_by_m(const SkArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_by_n<1, 4, BF4>(a, stream);
-  if (a.M <= 32) return launch_by_n<2, 4, BF4>(a, stream);
-  return launch_by_n<4, 2, BF4>(a, stream);
+  if (a.M <= 16) return launch_by_n<1, 4, WF>(a, stream);
+  if (a.M <= 32) return launch_by_n<2, 4, WF>(a, stream);
+  return launch_by_n<4, 2, WF>(a, stream);
 }
 
 }  // namespace
@@ -213,18 +240,24 @@ hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, con
   SkArgs a{};
   a.A = (const uint8_t*)A + k0;  // E4M3 activations: one byte per element
   a.SA = SA + k0 / 32;
-  a.B = (const uint8_t*)B + ((fmt == 0) ? k0 : k0 / 2);
+  const int64_t wpb = fmt == 0 ? 1 : fmt == 7 ? 4 : 2;  // weight elements per byte
+  a.B = (const uint8_t*)B + k0 / wpb;
   a.SB = SB + k0 / 32;
   a.e = e;
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)kn;
   a.lda = K;
-  a.ldb = (fmt == 0) ? K : K / 2;
+  a.ldb = K / wpb;
   a.lds = K / 32;
   a.accum = k0 > 0;
   a.nslices = (int)((kn + 127) / 128);
-  return (fmt == 0) ? launch_by_m<false>(a, stream) : launch_by_m<true>(a, stream);
+  switch (fmt) {
+    case 0: return launch_by_m<kFmtFp8>(a, stream);
+    case 1: return launch_by_m<kFmtFp4>(a, stream);
+    case 6: return launch_by_m<kElemInt4>(a, stream);
+    default: return launch_by_m<kElemInt2>(a, stream);
+  }
 }
 
 }  // namespace mxg

@@ -33,6 +33,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtBf8 = 1;
 constexpr int kFmtFp4 = 4;
+// Integer element formats (not MFMA formats: remapped onto E4M3 / E2M1
+// operand codes, see int4x8_to_e4m3 / int2x16_to_e2m1).
+constexpr int kElemInt4 = 8;
+constexpr int kElemInt2 = 9;
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row.  Fragment reads
 // have 16 consecutive lanes read 16 consecutive rows at the same logical
@@ -70,6 +74,54 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
   const int in = id - group * per_group;
   tm = first_m + in % gsz;
   tn = in / gsz;
+}
+
+// ---- integer weights: lossless remap onto scaled-MFMA operand codes -------
+//
+// Two's complement INT4 values -8..7 are exact E4M3 values and INT2 values
+// -2..1 are exact E2M1 values, so an integer operand is fed to the scaled
+// fp8 / fp4 MFMA by replacing every code with the float code of the same
+// value (the UE8M0 block scales are unchanged): the products and therefore
+// the results are those of the integer operand.  The lookups run on four
+// bytes at a time with v_perm_b32, whose selector bytes 0-3 pick bytes of
+// its second source and 4-7 bytes of its first.
+
+// Byte-wise lookup of four 4-bit indices (one per byte, 0..15) in the table
+// t0 (entries 0-3), t1 (4-7), t2 (8-11), t3 (12-15).
+__device__ __forceinline__ uint32_t lookup16(uint32_t idx, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
+  const uint32_t lo3 = idx & 0x07070707u;
+  const uint32_t a = __builtin_amdgcn_perm(t1, t0, lo3);
+  const uint32_t b = __builtin_amdgcn_perm(t3, t2, lo3);
+  const uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;  // 0xFF in the bytes whose index is >= 8
+  return (b & m) | (a & ~m);
+}
+
+// Eight INT4 codes (element i in bits 4i .. 4i+3) -> the E4M3 codes of
+// elements 0-3 (lo) and 4-7 (hi), one per byte.
+__device__ __forceinline__ void int4x8_to_e4m3(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  // E4M3 codes of 0..7 and of -8..-1 (indices 8..15)
+  constexpr uint32_t T0 = 0x44403800u, T1 = 0x4E4C4A48u, T2 = 0xCACCCED0u, T3 = 0xB8C0C4C8u;
+  const uint32_t ev = lookup16(x & 0x0F0F0F0Fu, T0, T1, T2, T3);         // elements 0, 2, 4, 6
+  const uint32_t od = lookup16((x >> 4) & 0x0F0F0F0Fu, T0, T1, T2, T3);  // elements 1, 3, 5, 7
+  lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+  hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+}
+
+// Sixteen INT2 codes (element i in bits 2i .. 2i+1) -> the E2M1 codes of
+// elements 0-7 (lo) and 8-15 (hi), two per byte, even element in the low
+// nibble.  One table entry maps a pair of INT2 codes (4 bits) to the byte
+// of their two E2M1 codes.
+__device__ __forceinline__ void int2x16_to_e2m1(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  // E2M1 code of each INT2 value: 0 -> 0x0, 1 -> 0x2 (1.0), -2 -> 0xC, -1 -> 0xA
+  // entry p = c0 + 4 c1 holds code(c0) | code(c1) << 4
+  constexpr uint32_t T0 = 0x0A0C0200u, T1 = 0x2A2C2220u, T2 = 0xCACCC2C0u, T3 = 0xAAACA2A0u;
+  // spread the four pairs of each 16-bit half to the bytes of a word
+  const uint32_t l = (x & 0xFFu) | ((x << 8) & 0xFF0000u);
+  const uint32_t h = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u);
+  const uint32_t li = (l & 0x000F000Fu) | ((l << 4) & 0x0F000F00u);
+  const uint32_t hi_i = (h & 0x000F000Fu) | ((h << 4) & 0x0F000F00u);
+  lo = lookup16(li, T0, T1, T2, T3);
+  hi = lookup16(hi_i, T0, T1, T2, T3);
 }
 
 // The format ids must be compile-time constants for the builtin.

@@ -13,11 +13,11 @@ hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, vo
                            hipStream_t stream);
 
 // fmt: 0 = E4M3 x E4M3, 1 = E4M3 x E2M1, 2 = E2M1 x E2M1, 3 = E5M2 x E5M2,
-// 4 = E4M3 x E5M2, 5 = E5M2 x E4M3 (A x B).  The MX launchers write
+// 4 = E4M3 x E5M2, 5 = E5M2 x E4M3, 6 = E4M3 x INT4, 7 = E4M3 x INT2 (A x B).  The MX launchers write
 // C through the epilogue `e` (output pointer, bias, activation, output type).
 hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream);
-// Split-K skinny kernel (M <= kSkinnyMaxM, fmt 0 or 1) over the k range
+// Split-K skinny kernel (M <= kSkinnyMaxM, fmt 0, 1, 6 or 7) over the k range
 // [k0, k0 + kn) of a product whose rows hold K elements (kn < 0: to K).  With
 // k0 > 0, C is fp32 and already holds the sum over k < k0, which is added.
 hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,

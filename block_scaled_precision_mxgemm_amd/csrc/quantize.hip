@@ -1,5 +1,5 @@
-// quantize.hip - fp32 rows -> E4M3 or E2M1 codes with one UE8M0 scale per 32
-// consecutive K elements.
+// quantize.hip - fp32 rows -> E4M3, E5M2, E2M1, INT4 or INT2 codes with one
+// UE8M0 scale per 32 consecutive K elements.
 //
 // Rule (one block of 32): amax = max |x|; e = floor(log2 amax) - emax with
 // emax = 8 (E4M3, largest finite 448 = 1.75 * 2^8), 15 (E5M2, 57344 =
@@ -11,7 +11,11 @@
 // way inside a block, although a plain E5M2 cast overflows to infinity).  A block holding a NaN or
 // an infinity gets scale byte 255 (NaN) and zero codes.  One E8M0 scale per 32
 // elements along the reduction axis: WWDC26 session 330 summary, section
-// "Scale Factor 付き量子化 tensor を作成する".
+// "Scale Factor 付き量子化 tensor を作成する".  The integer formats (two's
+// complement INT4 -8..7, INT2 -2..1: the 4-bit and 2-bit integer tensor
+// types of the same summary, section "量子化データ型のネイティブサポート")
+// take emax = 2 and 0 (the largest power of two of the range) and are
+// rounded to the nearest integer, ties to even, saturated to the range.
 //
 // All arithmetic is integer work on the fp32 bit patterns, so the result does
 // not depend on the denormal or rounding mode of the float units.
@@ -94,13 +98,28 @@ __device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
   return encode_mag<1, 0, 0x7u>(bits, e) | ((bits >> 31) << 3);
 }
 
+// Two's complement integer code of x * 2^-e in BITS bits: a "format" whose
+// spacing is 1 everywhere (KMIN = MBITS, so every value takes the subnormal
+// branch of encode_mag) rounds |x * 2^-e| to the nearest integer, ties to
+// even; positive values saturate at 2^(BITS-1) - 1, negative ones at
+// -2^(BITS-1).
+template <int BITS>
+__device__ __forceinline__ uint32_t encode_int(uint32_t bits, int e) {
+  constexpr int MB = BITS - 1;                       // |x * 2^-e| < 2^(BITS-1) up to rounding
+  constexpr uint32_t kNeg = 1u << (BITS - 1);        // largest negative magnitude
+  const uint32_t q = encode_mag<MB, MB, kNeg>(bits, e);
+  const bool neg = (bits >> 31) != 0u;
+  const uint32_t mag = neg ? q : min(q, kNeg - 1u);
+  return (neg ? 0u - mag : mag) & ((1u << BITS) - 1u);
+}
+
 // One block of 32: lanes sub = 0..7 of the block hold its elements 4*sub ..
 // 4*sub+3 in x; writes the block's codes and (lane 0) its scale byte.
 template <int ELEM>
 __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int sub, uint8_t* __restrict__ Q,
                                                uint8_t* __restrict__ S) {
-  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : (ELEM == kFmtBf8) ? 15 : 2;
-  constexpr bool kByte = ELEM != kFmtFp4;  // one code per byte
+  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : (ELEM == kFmtBf8) ? 15 : (ELEM == kElemInt2) ? 0 : 2;
+  constexpr bool kByte = ELEM == kFmtFp8 || ELEM == kFmtBf8;  // one code per byte
   uint32_t amax = 0u;
 #pragma unroll
   for (int i = 0; i < 4; i++) amax = max(amax, (uint32_t)x[i] & 0x7fffffffu);
@@ -121,6 +140,8 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
     c[i] = bad ? 0u
                : (ELEM == kFmtFp8)   ? encode_e4m3((uint32_t)x[i], e)
                : (ELEM == kFmtBf8)   ? encode_e5m2((uint32_t)x[i], e)
+               : (ELEM == kElemInt4) ? encode_int<4>((uint32_t)x[i], e)
+               : (ELEM == kElemInt2) ? encode_int<2>((uint32_t)x[i], e)
                                      : encode_e2m1((uint32_t)x[i], e);
   }
   // The codes are written once and read by a later GEMM: non-temporal
@@ -130,6 +151,8 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
   if (kByte) {
     __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                                 reinterpret_cast<uint32_t*>(Q + off));
+  } else if (ELEM == kElemInt2) {
+    __builtin_nontemporal_store((uint8_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6)), Q + (off >> 2));
   } else {
     __builtin_nontemporal_store((uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12)),
                                 reinterpret_cast<uint16_t*>(Q + (off >> 1)));
@@ -177,6 +200,12 @@ hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, vo
                        total);
   else if (elem == kFmtBf8)
     hipLaunchKernelGGL(quantize_kernel<kFmtBf8>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
+                       total);
+  else if (elem == kElemInt4)
+    hipLaunchKernelGGL(quantize_kernel<kElemInt4>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
+                       total);
+  else if (elem == kElemInt2)
+    hipLaunchKernelGGL(quantize_kernel<kElemInt2>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
                        total);
   else
     hipLaunchKernelGGL(quantize_kernel<kFmtFp4>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,

@@ -35,7 +35,7 @@ class Workload:
     N: int
     K: int
     seed: int
-    elem_a: str  # "e4m3" | "e2m1" | "fp16"
+    elem_a: str  # "e4m3" | "e5m2" | "e2m1" | "int4" | "int2" | "fp16"
     elem_b: str
     recipe: str
     description: str
@@ -60,6 +60,10 @@ WORKLOADS = {
                  "MXFP8 GEMM 8192^3, N(0,1) operands"),
         Workload("mxfp8xbf8_8192", 8192, 8192, 8192, 6, "e4m3", "e5m2", "normal",
                  "MX GEMM 8192^3, E4M3 A x E5M2 B, the same N(0,1) sources"),
+        Workload("decode_int4_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "int4", "decode",
+                 "decode GEMM, MXFP8 activations x INT4 weights (UE8M0 per 32), the decode sources"),
+        Workload("decode_int2_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "int2", "decode",
+                 "decode GEMM, MXFP8 activations x INT2 weights (UE8M0 per 32), the decode sources"),
     ]
 }
 

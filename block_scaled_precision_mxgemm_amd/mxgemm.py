@@ -16,15 +16,20 @@ import torch
 E4M3 = 0
 E5M2 = 1
 E2M1 = 4
+INT4 = 8
+INT2 = 9
 FMT_FP8_FP8 = 0
 FMT_FP8_FP4 = 1
 FMT_FP4_FP4 = 2
 FMT_BF8_BF8 = 3
 FMT_FP8_BF8 = 4
 FMT_BF8_FP8 = 5
+FMT_FP8_INT4 = 6
+FMT_FP8_INT2 = 7
 
 _FMT_ELEMS = {FMT_FP8_FP8: (E4M3, E4M3), FMT_FP8_FP4: (E4M3, E2M1), FMT_FP4_FP4: (E2M1, E2M1),
-              FMT_BF8_BF8: (E5M2, E5M2), FMT_FP8_BF8: (E4M3, E5M2), FMT_BF8_FP8: (E5M2, E4M3)}
+              FMT_BF8_BF8: (E5M2, E5M2), FMT_FP8_BF8: (E4M3, E5M2), FMT_BF8_FP8: (E5M2, E4M3),
+              FMT_FP8_INT4: (E4M3, INT4), FMT_FP8_INT2: (E4M3, INT2)}
 
 # output types and activations of the fused epilogue (MXG_OUT_*, MXG_ACT_*)
 OUT_F32 = 0
@@ -104,7 +109,11 @@ def _dev_u8(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def _row_bytes(K: int, elem: int) -> int:
-    return K // 2 if elem == E2M1 else K
+    if elem in (E2M1, INT4):
+        return K // 2
+    if elem == INT2:
+        return K // 4
+    return K
 
 
 def mxgemm_device_supported() -> bool:

@@ -54,7 +54,7 @@ def test_validation_codes(lib):
     assert _run(lib, *ok, 16, 16, 48, 0, None) == 1                         # K % 32 != 0
     assert _run(lib, *ok, 0, 16, 64, 0, None) == 1                          # M = 0
     assert _run(lib, *ok, 16, -1, 64, 0, None) == 1                         # N < 0
-    assert _run(lib, *ok, 16, 16, 64, 7, None) == 1                         # unknown fmt
+    assert _run(lib, *ok, 16, 16, 64, 8, None) == 1                         # unknown fmt
     assert _run(lib, 0x1001, A, A, A, A, 16, 16, 64, 0, None) == 2          # misaligned A
     assert _run(lib, A, A, A, A, 0x1008, 16, 16, 64, 0, None) == 2          # misaligned C
     assert b"aligned" in lib.mxgemm_status_string(2)

@@ -113,19 +113,24 @@ def test_decode_kernel_first_wait_counts_the_issued_loads():
     before the first copy, so that however the compiler merges those loads
     they are never among the counted ones.  Between the first copy and the
     first wait the compiler must issue exactly the counted global loads, or
-    the wait lets a stage's copies still be in flight.  With E2M1 weights and
-    K / 1024 odd the kernel has two wave kinds (WK = KW + 1 for waves 0-3,
-    KW - 1 for waves 4-7) behind one branch on the wave index; the prologue
-    of each kind starts at an assembly comment that names WK and MB."""
+    the wait lets a stage's copies still be in flight.  With two weight
+    operands per stage (E2M1, INT4) and K / 1024 odd the kernel has two wave
+    kinds (WK = KW + 1 for waves 0-3, KW - 1 for waves 4-7) behind one branch
+    on the wave index; the prologue of each kind starts at an assembly
+    comment that names WK and MB.  Every weight format (E4M3, E2M1, INT4,
+    INT2) is checked."""
     import re
     from block_scaled_precision_mxgemm_amd import build as B
     asm = H.compile_to_asm(os.path.join(ROOT, "block_scaled_precision_mxgemm_amd", "csrc", "gemm_decode.hip"),
                            B.FLAGS, B.HIPCC)
 
     seen = split = 0
-    for m in re.finditer(r"^(_ZN3mxg12_GLOBAL__N_113decode_kernelILb([01])ELi(\d+)ELi(\d+)ELi(\d+)EEEv\S*):", asm,
+    formats = set()
+    for m in re.finditer(r"^(_ZN3mxg12_GLOBAL__N_113decode_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEEv\S*):", asm,
                          re.M):
-        name, bf4, kw, mb = m.group(1), m.group(2) == "1", int(m.group(3)), int(m.group(4))
+        name, w, kw, mb = m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4))
+        formats.add(w)
+        two_per_stage = w in (4, 8)   # E2M1, INT4: 64-byte operands
         body = asm[m.end():asm.index(".Lfunc_end", m.end())]
         # the prologue of each wave kind starts at its marker comment
         wks = []
@@ -140,10 +145,10 @@ def test_decode_kernel_first_wait_counts_the_issued_loads():
             loads = re.findall(r"^\s*global_load_\w+", part[first_copy.start():first_wait.start()], re.M)
             assert len(loads) == mb * 2 * wk, (name, wk, len(loads), mb * 2 * wk)
             wks.append(wk)
-        if bf4 and kw % 2 == 1:
+        if two_per_stage and kw % 2 == 1:
             assert sorted(set(wks)) == [kw - 1, kw + 1], (name, wks)
             split += 1
         else:
             assert set(wks) == {kw}, (name, wks)
         seen += 1
-    assert seen >= 60 and split >= 12
+    assert seen >= 60 and split >= 12 and formats == {0, 4, 8, 9}
