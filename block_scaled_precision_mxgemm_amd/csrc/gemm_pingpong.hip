@@ -60,8 +60,9 @@ struct PPCfg {
   static constexpr int RB = BF4 ? 64 : 128;
   static constexpr int SZ_AH = 128 * RA;       // one A half, one stage
   static constexpr int SZ_B = 256 * RB;
-  static constexpr int SZ_SAH = SCALED ? 128 * 4 : 0;
-  static constexpr int SZ_SB = SCALED ? 256 * 4 : 0;
+  // scale buffers hold a group of 4 slices: 16 bytes per row
+  static constexpr int SZ_SAH = SCALED ? 128 * 16 : 0;
+  static constexpr int SZ_SB = SCALED ? 256 * 16 : 0;
   static constexpr int OFF_ATOP = 0;
   static constexpr int OFF_ABOT = OFF_ATOP + 2 * SZ_AH;
   static constexpr int OFF_B = OFF_ABOT + 2 * SZ_AH;
@@ -146,6 +147,19 @@ struct PPKernel {
     }
   }
 
+  // Scale bytes of a group of 4 slices: 16 per row (4 blocks per slice), 64
+  // rows per copy from row `row` of the tile, into lds (wave-uniform).  A
+  // copy of one slice's 4 bytes per row would touch one cache line per row
+  // for 256 bytes; taking 4 slices at once quarters the line requests (the
+  // per-slice scale copies cost about 14 % of a large GEMM's time,
+  // measured).  Past the end of K the 16 bytes run into the next row, or past
+  // the last row into the buffer's end (read as zeros); they are not used.
+  static __device__ __forceinline__ void copy_scale_group(__amdgpu_buffer_rsrc_t rs, uint32_t nb, int row, int G,
+                                                          uint8_t* lds, uint32_t off) {
+    const uint32_t soff = (uint32_t)row * nb + (uint32_t)(G * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, soff, 0, 0);
+  }
+
   template <int R>
   static __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row, int g) {
     v8i f;
@@ -206,16 +220,28 @@ struct PPKernel {
     // copies of slice t of each region (issued by the 4 waves of the calling group)
     auto copy_atop = [&](int t) {
       copy_rows<T::RA, 128>(rs_a, lda, 0, t, smem + T::OFF_ATOP + (t & 1) * T::SZ_AH, sw, oa);
-      if (T::SCALED) copy_scales<128>(rs_sa, nb, 0, t, smem + T::OFF_SATOP + (t & 1) * T::SZ_SAH, sw, os);
     };
     auto copy_abot = [&](int t) {
       copy_rows<T::RA, 128>(rs_a, lda, 128, t, smem + T::OFF_ABOT + (t & 1) * T::SZ_AH, sw, oa);
-      if (T::SCALED) copy_scales<128>(rs_sa, nb, 128, t, smem + T::OFF_SABOT + (t & 1) * T::SZ_SAH, sw, os);
     };
     auto copy_b = [&](int t) {
       copy_rows<T::RB, 256>(rs_b, ldb, 0, t, smem + T::OFF_B + (t & 1) * T::SZ_B, sw, ob);
-      if (T::SCALED) copy_scales<256>(rs_sb, nb, 0, t, smem + T::OFF_SB + (t & 1) * T::SZ_SB, sw, os);
     };
+    // Scale group G (slices 4G .. 4G + 3) into buffer G & 1 of each region,
+    // one copy of 64 rows per wave of the calling group: A_top rows 0-127
+    // (waves 0, 1) and A_bot rows 128-255 (waves 2, 3), or B rows 64 sw...
+    // Group G + 1 is copied in the load phase of slice 4G + 1 (A by group 1,
+    // B by group 0), after the last reads of group G - 1 from that buffer
+    // (slice 4G - 1) and well before its first reads (slice 4G + 4).
+    auto copy_sa_group = [&](int G) {
+      const int half = sw >> 1, q = sw & 1;
+      copy_scale_group(rs_sa, nb, half * 128 + q * 64, G,
+                       smem + (half ? T::OFF_SABOT : T::OFF_SATOP) + (G & 1) * T::SZ_SAH + q * 1024, os);
+    };
+    auto copy_sb_group = [&](int G) {
+      copy_scale_group(rs_sb, nb, sw * 64, G, smem + T::OFF_SB + (G & 1) * T::SZ_SB + sw * 1024, os);
+    };
+    const int ng = (S + 3) >> 2;
 
     // The workgroup is persistent: it takes tiles blockIdx.x, + gridDim.x, ...
     // (the grid is at most one workgroup per CU), so there is no dispatch gap
@@ -227,10 +253,12 @@ struct PPKernel {
     // steady state (B(0), A_top(0), A_top(1), A_bot(0)), issued by both groups
     if (grp == 0) {
       copy_b(0);
+      if (T::SCALED) copy_sb_group(0);
     } else {
       copy_atop(0);
       if (S > 1) copy_atop(1);
       copy_abot(0);
+      if (T::SCALED) copy_sa_group(0);
     }
     vm_wait_all();
     phase_barrier();
@@ -263,13 +291,15 @@ struct PPKernel {
 #pragma unroll
         for (int j = 0; j < 4; j++) bf[j] = read_frag<T::RB>(lb, sw * 64 + j * 16 + r, lg);
         if (T::SCALED) {
-          const uint8_t* lsa = smem + (grp ? T::OFF_SABOT : T::OFF_SATOP) + st * T::SZ_SAH;
-          const uint8_t* lsb = smem + T::OFF_SB + st * T::SZ_SB;
+          // slice s: group buffer (s >> 2) & 1, bytes 4 (s & 3) + lg of each row
+          const int sg = (s >> 2) & 1, sk = (s & 3) * 4 + lg;
+          const uint8_t* lsa = smem + (grp ? T::OFF_SABOT : T::OFF_SATOP) + sg * T::SZ_SAH;
+          const uint8_t* lsb = smem + T::OFF_SB + sg * T::SZ_SB;
           uint32_t x[8], y[4];
 #pragma unroll
-          for (int i = 0; i < 8; i++) x[i] = lsa[(i * 16 + r) * 4 + lg];
+          for (int i = 0; i < 8; i++) x[i] = lsa[(i * 16 + r) * 16 + sk];
 #pragma unroll
-          for (int j = 0; j < 4; j++) y[j] = lsb[(sw * 64 + j * 16 + r) * 4 + lg];
+          for (int j = 0; j < 4; j++) y[j] = lsb[(sw * 64 + j * 16 + r) * 16 + sk];
           sa[0] = (int)(x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24));
           sa[1] = (int)(x[4] | (x[5] << 8) | (x[6] << 16) | (x[7] << 24));
           sb = (int)(y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24));
@@ -279,6 +309,12 @@ struct PPKernel {
         } else {
           if (s + 2 < S) copy_atop(s + 2);
           if (s + 1 < S) copy_abot(s + 1);
+        }
+        if (T::SCALED && (s & 3) == 1 && (s >> 2) + 1 < ng) {
+          if (grp == 0)
+            copy_sb_group((s >> 2) + 1);
+          else
+            copy_sa_group((s >> 2) + 1);
         }
       }
       if constexpr (T::SCALED) {
@@ -381,6 +417,10 @@ struct PPKernel {
       copy_atop(0);
       if (S > 1) copy_atop(1);
       copy_abot(0);
+      if (T::SCALED) {
+        copy_sb_group(0);
+        copy_sa_group(0);
+      }
       vm_wait_all();
     }
     phase_barrier();

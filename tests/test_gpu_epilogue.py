@@ -107,7 +107,9 @@ def test_epilogue_gelu_against_oracle(out_type):
 
 
 # (workload recipe, M, N, K, fmt): the ping-pong kernel (>= 256 full tiles,
-# fp8 and fp4 x fp4), the 128 x 128 split-K ping-pong (full 128-tiles), the
+# fp8 and fp4 x fp4; with 272 tiles, a second tile per workgroup; K = 1152
+# ends with a partial scale group), the 128 x 128 split-K ping-pong (full
+# 128-tiles), the
 # 128 x 128 tiled kernel (ragged), a ragged shape with
 # >= 256 tiles (plain fp32 takes the 256 x 256 tiled kernel, a general
 # epilogue the 128 x 128 one), the decode kernel (1, 3 row blocks; two
@@ -116,6 +118,7 @@ def test_epilogue_gelu_against_oracle(out_type):
 # K = 4608 split between the decode and split-K kernels) and the split-K
 # skinny kernel.
 CASES = [("mxfp8_8192", 4096, 4096, 256, 0, 20000), ("mxfp8_2048", 4096, 4352, 256, 2, 20000),
+         ("mxfp8_2048", 4096, 4352, 1024, 4, 20000), ("mxfp8_2048", 4096, 4352, 1152, 0, 20000),
          ("mxfp8_2048", 512, 640, 384, 0, None), ("mxfp8_2048", 512, 640, 384, 4, None),
          ("mxfp8_2048", 300, 257, 512, 0, None), ("prefill_8192x14336x4096", 520, 530, 1056, 1, None),
          ("mxfp8_2048", 4100, 4100, 128, 0, 20000), ("decode_16x28672x8192", 16, 1000, 2048, 1, None),

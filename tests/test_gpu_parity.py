@@ -42,6 +42,9 @@ MODEL_CASES = {
     ("pp128", (2304, 2176, 512, 5)),
     ("nan", (4096, 4096, 256, 0)), ("nan", (128, 384, 256, 0)), ("nan", (200, 40, 256, 0)),
     ("nan", (128, 384, 256, 3)), ("inf", (37, 45, 96, 3)),
+    # 25 of 17.8 M outputs at up to 1.34 x the strict bound, 0.035 x the
+    # model bound
+    ("persistent", (4096, 4352, 768, 0)),
 }
 
 
@@ -204,16 +207,18 @@ def test_mx_gemm_large_tiles_full():
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5])
-def test_mx_gemm_persistent_two_tiles_full(fmt):
+@pytest.mark.parametrize("fmt,K", [(0, 1024), (1, 1024), (2, 1024), (3, 1024), (4, 1024), (5, 1024), (0, 1152),
+                                   (5, 1408), (3, 1280), (0, 768)])
+def test_mx_gemm_persistent_two_tiles_full(fmt, K):
     """More 256 x 256 tiles (16 x 17 = 272) than the grid's one workgroup per
     CU, so some workgroups run a second tile after the tile transition (next
-    tile's copies issued during the last compute phase, C staged through LDS);
-    block scales vary.  Checked in full."""
-    say("mx persistent two tiles", fmt)
-    M, N, K = 4096, 4352, 1024
+    tile's copies issued during the last slices, C staged through LDS); block
+    scales vary.  The scales come in groups of 4 slices (K = 512); K = 768,
+    1152, 1280 and 1408 end with a partial group.  Checked in full."""
+    say("mx persistent two tiles", fmt, K)
+    M, N = 4096, 4352
     a32, b32 = mx_sources("mxfp8_2048", M, N, K, seed=101 + fmt)
-    r, _ = mx_case(a32, b32, fmt)
+    r, _ = mx_case(a32, b32, fmt, model=_model("persistent", M, N, K, fmt))
     assert r["ok"], r
 
 
