@@ -134,19 +134,6 @@ struct PPKernel {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + q * 1024), 16, off, soff, 0, 0);
     }
   }
-  // Scale bytes of one slice: 4 per row (one per 32-element block), 64 rows
-  // per dword copy; ROWS / 64 copies (2 or 4) taken by waves 0.. of the group.
-  template <int ROWS>
-  static __device__ __forceinline__ void copy_scales(__amdgpu_buffer_rsrc_t rs, uint32_t nb, int row0, int slice,
-                                                     uint8_t* lds, int sw, uint32_t off) {
-    constexpr int NQ = ROWS / 64;
-    static_assert(NQ <= 4, "one scale copy per wave at most");
-    if (sw < NQ) {
-      const uint32_t soff = (uint32_t)(row0 + sw * 64) * nb + (uint32_t)(slice * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + sw * 256), 4, off, soff, 0, 0);
-    }
-  }
-
   // Scale bytes of a group of 4 slices: 16 per row (4 blocks per slice), 64
   // rows per copy from row `row` of the tile, into lds (wave-uniform).  A
   // copy of one slice's 4 bytes per row would touch one cache line per row
@@ -451,9 +438,10 @@ template <class T>
 struct PP128Kernel {
   using P = PPKernel<T>;
   static constexpr int SZ_A = 128 * T::RA, SZ_B = 128 * T::RB;
-  static constexpr int SZ_S = T::SCALED ? 128 * 4 : 0;  // scale rows of one operand, one slice
-  static constexpr int SZ_STAGE = SZ_A + SZ_B + 2 * SZ_S;
-  static constexpr int SZ_GROUP = 2 * SZ_STAGE;
+  static constexpr int SZ_STAGE = SZ_A + SZ_B;
+  // one scale buffer: a group of 4 slices, 16 bytes per row, A then B
+  static constexpr int SZ_SG = T::SCALED ? 2 * 128 * 16 : 0;
+  static constexpr int SZ_GROUP = 2 * SZ_STAGE + 2 * SZ_SG;
   static constexpr int SZ_RED = 4 * 16 * 64 * 16;  // group 1's partials: 4 waves x 16 fragments x 64 lanes
   static constexpr int LDS = 2 * SZ_GROUP > SZ_RED ? 2 * SZ_GROUP : SZ_RED;
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
@@ -499,12 +487,21 @@ struct PP128Kernel {
       uint8_t* st = gbase + (i & 1) * SZ_STAGE;
       P::template copy_rows<T::RA, 128>(rs_a, lda, 0, k, st, sw, oa);
       P::template copy_rows<T::RB, 128>(rs_b, ldb, 0, k, st + SZ_A, sw, ob);
-      if (T::SCALED) {
-        P::template copy_scales<128>(rs_sa, nb, 0, k, st + SZ_A + SZ_B, sw, os);
-        P::template copy_scales<128>(rs_sb, nb, 0, k, st + SZ_A + SZ_B + SZ_S, sw, os);
-      }
     };
-    if (Sg > 0) copy_iter(0);
+    // Scale group G (slices 4G .. 4G + 3, this group's iterations 2G and
+    // 2G + 1) into the group's buffer G & 1: one copy of 64 rows x 16 bytes
+    // per wave (A rows for waves 0, 1, B rows for waves 2, 3).  Group G + 1
+    // is copied in iteration 2G, after the last use of the buffer (group
+    // G - 1, iteration 2G - 1) and two iterations before its first use.
+    auto copy_sgroup = [&](int G) {
+      const int op = sw >> 1, q = sw & 1;
+      P::copy_scale_group(op ? rs_sb : rs_sa, nb, q * 64, G,
+                          gbase + 2 * SZ_STAGE + (G & 1) * SZ_SG + op * 2048 + q * 1024, os);
+    };
+    if (Sg > 0) {
+      copy_iter(0);
+      if (T::SCALED) copy_sgroup(0);
+    }
     vm_wait_all();
     phase_barrier();
 
@@ -534,17 +531,20 @@ struct PP128Kernel {
 #pragma unroll
       for (int f = 0; f < 4; f++) bf[f] = P::template read_frag<T::RB>(st + SZ_A, wc + 16 * f + r, lg);
       if (T::SCALED) {
-        const uint8_t* lsa = st + SZ_A + SZ_B;
-        const uint8_t* lsb = lsa + SZ_S;
+        // slice 2i + grp: buffer (i >> 1) & 1, bytes 4 ((2i + grp) & 3) + lg of each row
+        const uint8_t* lsa = gbase + 2 * SZ_STAGE + ((i >> 1) & 1) * SZ_SG;
+        const uint8_t* lsb = lsa + 2048;
+        const int sk = (2 * (i & 1) + grp) * 4 + lg;
         uint32_t x[4], y[4];
 #pragma unroll
-        for (int f = 0; f < 4; f++) x[f] = lsa[(wr + 16 * f + r) * 4 + lg];
+        for (int f = 0; f < 4; f++) x[f] = lsa[(wr + 16 * f + r) * 16 + sk];
 #pragma unroll
-        for (int f = 0; f < 4; f++) y[f] = lsb[(wc + 16 * f + r) * 4 + lg];
+        for (int f = 0; f < 4; f++) y[f] = lsb[(wc + 16 * f + r) * 16 + sk];
         sa = (int)(x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24));
         sb = (int)(y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24));
       }
       if (i + 1 < Sg) copy_iter(i + 1);
+      if (T::SCALED && (i & 1) == 0 && i + 2 < Sg) copy_sgroup((i >> 1) + 1);
       if constexpr (T::SCALED) {
         // as in the 256 x 256 kernel: the packed scales are operands of the
         // barrier, and s_nop covers the VALU-write -> MFMA-read wait states
