@@ -33,6 +33,8 @@ import numpy as np
 
 E4M3 = 0
 E5M2 = 1
+E2M3 = 2
+E3M2 = 3
 E2M1 = 4
 INT4 = 8
 INT2 = 9
@@ -71,6 +73,10 @@ def _load():
     lib.mxref_e5m2_value.restype = ctypes.c_double
     lib.mxref_e2m1_value.argtypes = [ctypes.c_uint8]
     lib.mxref_e2m1_value.restype = ctypes.c_double
+    lib.mxref_e2m3_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_e2m3_value.restype = ctypes.c_double
+    lib.mxref_e3m2_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_e3m2_value.restype = ctypes.c_double
     lib.mxref_int4_value.argtypes = [ctypes.c_uint8]
     lib.mxref_int4_value.restype = ctypes.c_double
     lib.mxref_int2_value.argtypes = [ctypes.c_uint8]
@@ -140,6 +146,18 @@ def e2m1_table() -> np.ndarray:
     return np.array([lib.mxref_e2m1_value(c) for c in range(16)], dtype=np.float64)
 
 
+def e2m3_table() -> np.ndarray:
+    """float64[64]: value of every E2M3 (FP6) code."""
+    lib = _load()
+    return np.array([lib.mxref_e2m3_value(c) for c in range(64)], dtype=np.float64)
+
+
+def e3m2_table() -> np.ndarray:
+    """float64[64]: value of every E3M2 (FP6) code."""
+    lib = _load()
+    return np.array([lib.mxref_e3m2_value(c) for c in range(64)], dtype=np.float64)
+
+
 def int4_table() -> np.ndarray:
     """float64[16]: value of every two's complement INT4 code (-8..7)."""
     lib = _load()
@@ -164,11 +182,13 @@ def fp16_value(bits: int) -> float:
 
 def row_bytes(K: int, elem: int) -> int:
     """Bytes per operand row: K for E4M3 and E5M2, K/2 for packed E2M1 and
-    INT4, K/4 for packed INT2."""
+    INT4, K/4 for packed INT2, 3K/4 for packed E2M3 and E3M2."""
     if elem in (E2M1, INT4):
         return K // 2
     if elem == INT2:
         return K // 4
+    if elem in (E2M3, E3M2):
+        return K // 4 * 3
     return K
 
 
@@ -178,7 +198,8 @@ def quantize(x: np.ndarray, elem: int):
     """Quantize fp32 rows (K contiguous) to (codes uint8, scales uint8).
 
     codes: rows x K (E4M3, E5M2), rows x K/2 (E2M1, INT4: even k in the low
-    nibble) or rows x K/4 (INT2: k in bits 2 (k mod 4)); scales: rows x K/32
+    nibble), rows x K/4 (INT2: k in bits 2 (k mod 4)) or rows x 3K/4 (E2M3,
+    E3M2: k in bits 6k .. 6k+5 of the row, little-endian); scales: rows x K/32
     UE8M0 bytes.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -187,7 +208,7 @@ def quantize(x: np.ndarray, elem: int):
     s = np.zeros((rows, K // 32), dtype=np.uint8)
     rc = _load().mxref_quantize(_ptr(x), rows, K, elem, _ptr(q), _ptr(s))
     if rc != 0:
-        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E5M2/E2M1/INT4/INT2)")
+        raise ValueError("oracle quantize: bad arguments (K %% 32 must be 0, elem E4M3/E5M2/E2M3/E3M2/E2M1/INT4/INT2)")
     return q, s
 
 

@@ -45,6 +45,14 @@
  *     exponent of the largest power of two the range holds (2 for INT4, 0
  *     for INT2), as emax does for the float formats; elements are rounded to
  *     nearest, ties to even, and saturated to the range (+7 / -8, +1 / -2).
+ *   - FP6 elements ("FP6" is the 6-bit float the scaled matrix unit takes
+ *     beside E5M2, the other "E5M2 (and FP6)" operand; the pages name no FP6
+ *     layout, so the OCP Microscaling definitions are taken, as for E2M1):
+ *     E2M3 = sign, 2 exponent bits (bias 1), 3 mantissa bits, largest 7.5,
+ *     emax 2; E3M2 = sign, 3 exponent bits (bias 3), 2 mantissa bits,
+ *     largest 28, emax 4; exponent field 0 is subnormal; no NaN, no
+ *     infinity.  Codes are packed little-endian, element k of a row at bits
+ *     6k .. 6k+5 of the row's bytes (four elements in three bytes).
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +63,8 @@
 
 #define MXREF_E4M3 0
 #define MXREF_E5M2 1
+#define MXREF_E2M3 2
+#define MXREF_E3M2 3
 #define MXREF_E2M1 4
 #define MXREF_INT4 8
 #define MXREF_INT2 9
@@ -62,7 +72,8 @@
 static int known_elem(int elem)
 {
     return elem == MXREF_E4M3 || elem == MXREF_E5M2 || elem == MXREF_E2M1 ||
-           elem == MXREF_INT4 || elem == MXREF_INT2;
+           elem == MXREF_INT4 || elem == MXREF_INT2 || elem == MXREF_E2M3 ||
+           elem == MXREF_E3M2;
 }
 
 /* Bytes of one operand row of K elements. */
@@ -72,7 +83,35 @@ static int64_t row_bytes(int elem, int64_t K)
         return K / 2;
     if (elem == MXREF_INT2)
         return K / 4;
+    if (elem == MXREF_E2M3 || elem == MXREF_E3M2)
+        return K / 4 * 3;
     return K;
+}
+
+static int is_fp6(int elem)
+{
+    return elem == MXREF_E2M3 || elem == MXREF_E3M2;
+}
+
+/* 6-bit code of element k of a packed row (bits 6k .. 6k+5). */
+static unsigned get6(const uint8_t *row, int64_t k)
+{
+    int64_t bit = 6 * k;
+    unsigned v = row[bit >> 3];
+    if ((bit & 7) > 2) /* the code runs into the next byte */
+        v |= (unsigned)row[(bit >> 3) + 1] << 8;
+    return (v >> (bit & 7)) & 63u;
+}
+
+/* Store the 6-bit code c as element k of a packed row. */
+static void put6(uint8_t *row, int64_t k, unsigned c)
+{
+    int64_t bit = 6 * k;
+    int sh = (int)(bit & 7);
+    unsigned mask = 63u << sh, v = (c & 63u) << sh;
+    row[bit >> 3] = (uint8_t)((row[bit >> 3] & ~mask) | (v & 0xffu));
+    if (sh > 2)
+        row[(bit >> 3) + 1] = (uint8_t)((row[(bit >> 3) + 1] & ~(mask >> 8)) | (v >> 8));
 }
 
 /* ---------------------------------------------------------------- decode */
@@ -115,6 +154,24 @@ double mxref_e2m1_value(uint8_t nibble)
 {
     int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
     double v = (e == 0) ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
+    return s ? -v : v;
+}
+
+/* OCP E2M3 6-bit code -> value: sign, 2 exponent bits (bias 1), 3 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-3); no NaN, no infinity. */
+double mxref_e2m3_value(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 3) & 3, m = code & 7;
+    double v = (e == 0) ? ldexp((double)m, -3) : ldexp(1.0 + m / 8.0, e - 1);
+    return s ? -v : v;
+}
+
+/* OCP E3M2 6-bit code -> value: sign, 3 exponent bits (bias 3), 2 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-4); no NaN, no infinity. */
+double mxref_e3m2_value(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 2) & 7, m = code & 3;
+    double v = (e == 0) ? ldexp((double)m, -4) : ldexp(1.0 + m / 4.0, e - 3);
     return s ? -v : v;
 }
 
@@ -231,6 +288,50 @@ static uint8_t encode_e2m1(double v)
     return (uint8_t)(code | (neg << 3));
 }
 
+/* Round |v| to the E2M3 grid (ties to even), saturate at 7.5, encode. */
+static uint8_t encode_e2m3(double v)
+{
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v), quantum, r;
+    uint8_t code;
+    /* normal binades [1, ...) carry 3 fraction bits; below 1 the spacing is
+     * the subnormal step 2^-3 */
+    quantum = (a >= 1.0) ? ldexp(1.0, floor_log2(a) - 3) : 0.125;
+    r = nearbyint(a / quantum) * quantum;
+    if (r > 7.5)
+        r = 7.5;
+    if (r < 1.0) {
+        code = (uint8_t)(r * 8.0); /* subnormal: m = r / 2^-3, 0..7 */
+    } else {
+        int e = floor_log2(r);
+        int m = (int)((r / ldexp(1.0, e) - 1.0) * 8.0);
+        code = (uint8_t)(((e + 1) << 3) | m);
+    }
+    return (uint8_t)(code | (neg << 5));
+}
+
+/* Round |v| to the E3M2 grid (ties to even), saturate at 28, encode. */
+static uint8_t encode_e3m2(double v)
+{
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v), quantum, r;
+    uint8_t code;
+    /* normal binades [2^-2, ...) carry 2 fraction bits; below 2^-2 the
+     * spacing is the subnormal step 2^-4 */
+    quantum = (a >= 0.25) ? ldexp(1.0, floor_log2(a) - 2) : 0.0625;
+    r = nearbyint(a / quantum) * quantum;
+    if (r > 28.0)
+        r = 28.0;
+    if (r < 0.25) {
+        code = (uint8_t)(r * 16.0); /* subnormal: m = r / 2^-4, 0..3 */
+    } else {
+        int e = floor_log2(r);
+        int m = (int)((r / ldexp(1.0, e) - 1.0) * 4.0);
+        code = (uint8_t)(((e + 3) << 2) | m);
+    }
+    return (uint8_t)(code | (neg << 5));
+}
+
 /* Round v to the nearest integer (ties to even), saturate to [qmin, qmax],
  * and return its two's complement code in `bits` bits. */
 static uint8_t encode_int(double v, int qmin, int qmax, int bits)
@@ -247,7 +348,8 @@ static uint8_t encode_int(double v, int qmin, int qmax, int bits)
 
 /* Quantize X[rows][K] (fp32, K contiguous) to codes Q and scales S.
  *   E4M3, E5M2: Q is rows x K bytes.   E2M1, INT4: Q is rows x K/2 bytes, two
- *   per byte.   INT2: Q is rows x K/4 bytes, four per byte.
+ *   per byte.   INT2: Q is rows x K/4 bytes, four per byte.   E2M3, E3M2: Q
+ *   is rows x 3K/4 bytes, 6-bit codes packed little-endian.
  *   S is rows x K/32 UE8M0 bytes.
  * Returns 0, or -1 on a bad argument (K not a multiple of 32, unknown elem). */
 int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
@@ -267,6 +369,10 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
         emax = 2; /* 4 <= 7 < 8 */
     else if (elem == MXREF_INT2)
         emax = 0; /* 1 */
+    else if (elem == MXREF_E2M3)
+        emax = 2; /* 7.5 = 1.875 * 2^2 */
+    else if (elem == MXREF_E3M2)
+        emax = 4; /* 28 = 1.75 * 2^4 */
     else
         return -1;
 
@@ -289,6 +395,8 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
                     int64_t k = b * 32 + i;
                     if (elem == MXREF_E4M3 || elem == MXREF_E5M2)
                         q[r * K + k] = 0;
+                    else if (is_fp6(elem))
+                        put6(q + r * row_bytes(elem, K), k, 0);
                     else if (elem == MXREF_INT2)
                         q[r * (K / 4) + k / 4] &= (uint8_t)~(3u << (2 * (k & 3)));
                     else
@@ -309,6 +417,9 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
                     q[r * K + k] = encode_e4m3(v);
                 } else if (elem == MXREF_E5M2) {
                     q[r * K + k] = encode_e5m2(v);
+                } else if (is_fp6(elem)) {
+                    put6(q + r * row_bytes(elem, K), k,
+                         elem == MXREF_E2M3 ? encode_e2m3(v) : encode_e3m2(v));
                 } else if (elem == MXREF_INT2) {
                     uint8_t c = encode_int(v, -2, 1, 2);
                     uint8_t *p = q + r * (K / 4) + k / 4;
@@ -331,6 +442,7 @@ int mxref_quantize(const float *x, int64_t rows, int64_t K, int elem,
 /* ------------------------------------------------------------------ GEMM */
 
 static double tab_e4m3[256], tab_e5m2[256], tab_e2m1[16], tab_int4[16], tab_int2[4], tab_ue8m0[256];
+static double tab_e2m3[64], tab_e3m2[64];
 static int tabs_ready = 0;
 
 static void make_tables(void)
@@ -348,6 +460,10 @@ static void make_tables(void)
         tab_int4[i] = mxref_int4_value((uint8_t)i);
     for (i = 0; i < 4; i++)
         tab_int2[i] = mxref_int2_value((uint8_t)i);
+    for (i = 0; i < 64; i++) {
+        tab_e2m3[i] = mxref_e2m3_value((uint8_t)i);
+        tab_e3m2[i] = mxref_e3m2_value((uint8_t)i);
+    }
     for (i = 0; i < 256; i++)
         tab_ue8m0[i] = mxref_ue8m0_value((uint8_t)i);
     tabs_ready = 1;
@@ -364,6 +480,10 @@ static double element(const uint8_t *row, int elem, int64_t k)
         return tab_int4[(row[k >> 1] >> ((k & 1) * 4)) & 15];
     if (elem == MXREF_INT2)
         return tab_int2[(row[k >> 2] >> ((k & 3) * 2)) & 3];
+    if (elem == MXREF_E2M3)
+        return tab_e2m3[get6(row, k)];
+    if (elem == MXREF_E3M2)
+        return tab_e3m2[get6(row, k)];
     return tab_e2m1[(row[k >> 1] >> ((k & 1) * 4)) & 15];
 }
 
