@@ -459,7 +459,8 @@ def mx_operands(name, dev):
     ta = torch.from_numpy(a32).to(dev)
     tb = torch.from_numpy(b32).to(dev)
     del a32, b32
-    elem = {"e4m3": mx.E4M3, "e5m2": mx.E5M2, "e2m1": mx.E2M1, "int4": mx.INT4, "int2": mx.INT2}
+    elem = {"e4m3": mx.E4M3, "e5m2": mx.E5M2, "e2m1": mx.E2M1, "int4": mx.INT4, "int2": mx.INT2,
+            "e2m3": mx.E2M3, "e3m2": mx.E3M2}
     qa, sa = mx.mxgemm_quantize(ta, elem[w.elem_a])
     qb, sb = mx.mxgemm_quantize(tb, elem[w.elem_b])
     torch.cuda.synchronize()
@@ -477,10 +478,11 @@ def bench_decode(dev, name="decode_16x28672x8192"):
 
     w = mxin.WORKLOADS[name]
     elem, fmt, kname = {"e2m1": (mx.E2M1, mx.FMT_FP8_FP4, "fp4"), "int4": (mx.INT4, mx.FMT_FP8_INT4, "int4"),
-                        "int2": (mx.INT2, mx.FMT_FP8_INT2, "int2")}[w.elem_b]
+                        "int2": (mx.INT2, mx.FMT_FP8_INT2, "int2"), "e2m3": (mx.E2M3, mx.FMT_FP8_FP6, "e2m3"),
+                        "e3m2": (mx.E3M2, mx.FMT_FP8_BF6, "e3m2")}[w.elem_b]
     a32, _ = mxin.mx_sources(w, N=1)
     qa, sa = mx.mxgemm_quantize(torch.from_numpy(a32).to(dev), mx.E4M3)
-    wb = w.N * w.K // (2 if elem != mx.INT2 else 4)
+    wb = w.N * w.K * {mx.INT2: 1, mx.E2M3: 3, mx.E3M2: 3}.get(elem, 2) // 4   # weight bytes
     copies = max(5, int(math.ceil(600e6 / (wb + w.N * w.K // 32))))   # > 2x the 256 MB MALL in total
     weights = []
     for b32 in mxin.decode_weight_copies(w, copies):
@@ -500,7 +502,9 @@ def bench_decode(dev, name="decode_16x28672x8192"):
     eager = time_windows(step)
     warm = time_windows(lambda i=0: mx.mxgemm_run(qa, sa, weights[0][0], weights[0][1], fmt, out=c))
     rec = timed_entry(cold, nbytes=nbytes)
-    rec.update({"kernel": "decode_kernel<fp8 x %s, K=8192> (LDS-staged weight stream)" % kname,
+    kernel = ("skinny_kernel<fp8 x %s> (split-K, weights read once as FP6 MFMA operands)" % kname
+              if elem in (mx.E2M3, mx.E3M2) else "decode_kernel<fp8 x %s, K=8192> (LDS-staged weight stream)" % kname)
+    rec.update({"kernel": kernel,
                 "us": rec["ms"] * 1e3, "us_best": rec["ms_min"] * 1e3, "algorithmic_bytes": nbytes,
                 "weight_copies_rotated": copies,
                 "eager_us": eager["ms_median"] * 1e3, "eager_GB/s": nbytes / (eager["ms_median"] * 1e-3) / 1e9,
@@ -520,7 +524,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["all", "headline", "decode", "int", "fp16", "prefill", "small", "ceiling"],
+    ap.add_argument("--only", choices=["all", "headline", "decode", "int", "fp6", "fp16", "prefill", "small",
+                                       "ceiling"],
                     default="all", help="run a subset (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for each of the two sampled large configurations")
@@ -694,6 +699,9 @@ def main():
         extra["decode_16x28672x8192"] = bench_decode(dev)
     if only in ("all", "decode", "int"):
         for name in ("decode_int4_16x28672x8192", "decode_int2_16x28672x8192"):
+            extra[name] = bench_decode(dev, name)
+    if only in ("all", "decode", "fp6"):
+        for name in ("decode_e2m3_16x28672x8192", "decode_e3m2_16x28672x8192"):
             extra[name] = bench_decode(dev, name)
 
     cpu = None

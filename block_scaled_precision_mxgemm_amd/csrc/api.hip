@@ -36,7 +36,7 @@ int validate_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* 
                 int64_t N, int64_t K, int fmt) {
   if (!A || !SA || !B || !SB || !C) return MXG_EINVAL;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
-  if (fmt < MXG_FMT_FP8_FP8 || fmt > MXG_FMT_FP8_INT2) return MXG_EINVAL;
+  if (fmt < MXG_FMT_FP8_FP8 || fmt > MXG_FMT_FP8_BF6) return MXG_EINVAL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXG_EALIGN;
   return MXG_OK;
 }
@@ -48,18 +48,23 @@ int validate_epi(const float* bias, int act, int out_type) {
   return MXG_OK;
 }
 
-bool int_weights(int fmt) { return fmt == MXG_FMT_FP8_INT4 || fmt == MXG_FMT_FP8_INT2; }
+// integer weights (remapped in registers to MFMA operand codes) and FP6
+// weights (MFMA operands as stored): the split-K kernel takes them for every M
+bool remapped_weights(int fmt) {
+  return fmt == MXG_FMT_FP8_INT4 || fmt == MXG_FMT_FP8_INT2 || fmt == MXG_FMT_FP8_FP6 || fmt == MXG_FMT_FP8_BF6;
+}
 
 // Kernel choice for an MX product (arguments validated): the weight-streaming
-// decode kernel, the split-K skinny kernel (both for E4M3 activations against
-// E4M3, E2M1, INT4 or INT2 weights), or the tiled / ping-pong kernels (every
-// float format pair).  Integer weights with more than 64 rows of activations
-// run the split-K kernel once per 64 rows (B is read once per 64 rows: a
-// correct path for such shapes, not a tuned one).
+// decode kernel (E4M3 activations against E4M3, E2M1, INT4 or INT2 weights),
+// the split-K skinny kernel (the same, and FP6 weights), or the tiled /
+// ping-pong kernels (every 8- and 4-bit float format pair).  Integer and FP6
+// weights with more than 64 rows of activations run the split-K kernel once
+// per 64 rows (B is read once per 64 rows: a correct path for such shapes,
+// not a tuned one).
 int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
            int64_t N, int64_t K, int fmt, hipStream_t st) {
   if (mxg::decode_ok(M, K, fmt, SA, SB, e)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
-  if (int_weights(fmt) && M > mxg::kSkinnyMaxM) {
+  if (remapped_weights(fmt) && M > mxg::kSkinnyMaxM) {
     const int64_t eb = mxg::epi_elem_bytes(e.out);
     for (int64_t m0 = 0; m0 < M; m0 += mxg::kSkinnyMaxM) {
       mxg::Epi ec = e;
@@ -72,7 +77,7 @@ int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, c
     return MXG_OK;
   }
   if (M <= mxg::kSkinnyMaxM &&
-      (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4 || int_weights(fmt))) {
+      (fmt == MXG_FMT_FP8_FP8 || fmt == MXG_FMT_FP8_FP4 || remapped_weights(fmt))) {
     // K not a multiple of 1024, up to 16 rows, fp32 C: the decode kernel
     // takes the largest multiple of 1024 below K, the split-K kernel adds the
     // rest (with more rows the split-K kernel alone measured faster at
@@ -95,6 +100,8 @@ static_assert(MXG_ACT_NONE == mxg::kActNone && MXG_ACT_GELU == mxg::kActGelu, "a
 static_assert(MXG_ELEM_E4M3 == mxg::kFmtFp8 && MXG_ELEM_E5M2 == mxg::kFmtBf8 && MXG_ELEM_E2M1 == mxg::kFmtFp4,
               "element ids are the MFMA format ids");
 static_assert(MXG_ELEM_INT4 == mxg::kElemInt4 && MXG_ELEM_INT2 == mxg::kElemInt2, "integer element ids");
+static_assert(MXG_ELEM_E2M3 == mxg::kFmtFp6 && MXG_ELEM_E3M2 == mxg::kFmtBf6, "FP6 element ids");
+static_assert(MXG_FMT_FP8_FP6 == 8 && MXG_FMT_FP8_BF6 == 9, "FP6 pair ids the split-K launch switches on");
 
 }  // namespace
 
@@ -128,7 +135,7 @@ int mxgemm_quantize(const float* X, int64_t rows, int64_t K, int elem, void* Q, 
   if (!X || !Q || !S) return MXG_EINVAL;
   if (!dim_ok(rows) || !dim_ok(K) || (K % 32) != 0) return MXG_EINVAL;
   if (elem != MXG_ELEM_E4M3 && elem != MXG_ELEM_E5M2 && elem != MXG_ELEM_E2M1 && elem != MXG_ELEM_INT4 &&
-      elem != MXG_ELEM_INT2)
+      elem != MXG_ELEM_INT2 && elem != MXG_ELEM_E2M3 && elem != MXG_ELEM_E3M2)
     return MXG_EINVAL;
   if (!aligned16(X) || !aligned16(Q)) return MXG_EALIGN;
   const int d = check_device();

@@ -40,11 +40,14 @@ struct SkArgs {
   int nslices;       // ceil(K / 128)
 };
 
-// WF: weight format (kFmtFp8, kFmtFp4, kElemInt4 or kElemInt2; the integer
-// codes are remapped in registers to E4M3 / E2M1 MFMA operands)
+// WF: weight format (kFmtFp8, kFmtFp4, kElemInt4, kElemInt2, kFmtFp6 or
+// kFmtBf6; the integer codes are remapped in registers to E4M3 / E2M1 MFMA
+// operands, the FP6 codes are MFMA operands as stored)
 template <int MT, int NF, int WF, int U, int W>
 struct Skinny {
-  static constexpr int BFMT = (WF == kFmtFp8 || WF == kElemInt4) ? kFmtFp8 : kFmtFp4;  // MFMA format of B
+  static constexpr bool FP6 = WF == kFmtFp6 || WF == kFmtBf6;
+  // MFMA format of B
+  static constexpr int BFMT = FP6 ? WF : (WF == kFmtFp8 || WF == kElemInt4) ? kFmtFp8 : kFmtFp4;
   struct Group {
     v8i a[U][MT];
     v8i b[U][NF];
@@ -86,6 +89,18 @@ struct Skinny {
     int2x16_to_e2m1((uint32_t)c[1], e[2], e[3]);
     return v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], 0, 0, 0, 0};
   }
+  // FP6 operand bytes of one lane: k = 32g .. 32g+31, 24 bytes (6 registers;
+  // element i of the lane at bits 6i .. 6i+5, as the rows store them)
+  static __device__ __forceinline__ v8i load_fp6(const uint8_t* row, int k0, int g, int K) {
+    v2i a = {0, 0}, b = {0, 0}, c = {0, 0};
+    const uint8_t* p = row + (k0 >> 2) * 3 + 24 * g;
+    if (k0 + 32 * g < K) {
+      a = *reinterpret_cast<const v2i*>(p);
+      b = *reinterpret_cast<const v2i*>(p + 8);
+      c = *reinterpret_cast<const v2i*>(p + 16);
+    }
+    return v8i{a[0], a[1], b[0], b[1], c[0], c[1], 0, 0};
+  }
   static __device__ __forceinline__ int load_scale(const uint8_t* srow, int blk, int nb) {
     return (blk < nb) ? (int)srow[blk] : 127;
   }
@@ -103,10 +118,13 @@ struct Skinny {
         const int n = min(n0 + j * 16 + r, a.N - 1);
         const uint8_t* brow = a.B + (int64_t)n * a.ldb;
         if (live) {
-          G.b[u][j] = WF == kFmtFp4     ? load_fp4(brow, k0, g, a.K)
-                      : WF == kElemInt4 ? load_int4(brow, k0, g, a.K)
-                      : WF == kElemInt2 ? load_int2(brow, k0, g, a.K)
-                                        : load_fp8(brow, k0, g, a.K);
+          if constexpr (FP6)
+            G.b[u][j] = load_fp6(brow, k0, g, a.K);
+          else
+            G.b[u][j] = WF == kFmtFp4     ? load_fp4(brow, k0, g, a.K)
+                        : WF == kElemInt4 ? load_int4(brow, k0, g, a.K)
+                        : WF == kElemInt2 ? load_int2(brow, k0, g, a.K)
+                                          : load_fp8(brow, k0, g, a.K);
           G.sb[u][j] = load_scale(a.SB + (int64_t)n * a.lds, sl * 4 + g, nb);
         } else {
           G.b[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -240,15 +258,16 @@ hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, con
   SkArgs a{};
   a.A = (const uint8_t*)A + k0;  // E4M3 activations: one byte per element
   a.SA = SA + k0 / 32;
-  const int64_t wpb = fmt == 0 ? 1 : fmt == 7 ? 4 : 2;  // weight elements per byte
-  a.B = (const uint8_t*)B + k0 / wpb;
+  // weight bytes per 4 elements: 4 (E4M3), 2 (E2M1, INT4), 1 (INT2), 3 (FP6)
+  const int64_t b4 = fmt == 0 ? 4 : fmt == 7 ? 1 : (fmt == 8 || fmt == 9) ? 3 : 2;
+  a.B = (const uint8_t*)B + k0 / 4 * b4;
   a.SB = SB + k0 / 32;
   a.e = e;
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)kn;
   a.lda = K;
-  a.ldb = K / wpb;
+  a.ldb = K / 4 * b4;
   a.lds = K / 32;
   a.accum = k0 > 0;
   a.nslices = (int)((kn + 127) / 128);
@@ -256,6 +275,8 @@ hipError_t launch_mx_skinny(const void* A, const uint8_t* SA, const void* B, con
     case 0: return launch_by_m<kFmtFp8>(a, stream);
     case 1: return launch_by_m<kFmtFp4>(a, stream);
     case 6: return launch_by_m<kElemInt4>(a, stream);
+    case 8: return launch_by_m<kFmtFp6>(a, stream);
+    case 9: return launch_by_m<kFmtBf6>(a, stream);
     default: return launch_by_m<kElemInt2>(a, stream);
   }
 }

@@ -33,6 +33,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtBf8 = 1;
 constexpr int kFmtFp4 = 4;
+// FP6 element formats (E2M3 and E3M2: the format ids the scaled MFMA gives
+// them).  An FP6 operand is 6 registers per lane: 32 codes of 6 bits,
+// element i of the lane at bits 6i .. 6i+5.
+constexpr int kFmtFp6 = 2;
+constexpr int kFmtBf6 = 3;
 // Integer element formats (not MFMA formats: remapped onto E4M3 / E2M1
 // operand codes, see int4x8_to_e4m3 / int2x16_to_e2m1).
 constexpr int kElemInt4 = 8;

@@ -1,5 +1,5 @@
-// quantize.hip - fp32 rows -> E4M3, E5M2, E2M1, INT4 or INT2 codes with one
-// UE8M0 scale per 32 consecutive K elements.
+// quantize.hip - fp32 rows -> E4M3, E5M2, E2M1, E2M3, E3M2, INT4 or INT2
+// codes with one UE8M0 scale per 32 consecutive K elements.
 //
 // Rule (one block of 32): amax = max |x|; e = floor(log2 amax) - emax with
 // emax = 8 (E4M3, largest finite 448 = 1.75 * 2^8), 15 (E5M2, 57344 =
@@ -16,6 +16,10 @@
 // types of the same summary, section "量子化データ型のネイティブサポート")
 // take emax = 2 and 0 (the largest power of two of the range) and are
 // rounded to the nearest integer, ties to even, saturated to the range.
+// The FP6 formats (the 6-bit float operands of the scaled matrix unit; the
+// pages give no layout, so the OCP Microscaling definitions are taken) take
+// emax = 2 (E2M3, 7.5 = 1.875 * 2^2) and 4 (E3M2, 28 = 1.75 * 2^4), and are
+// packed little-endian, element k at bits 6k .. 6k+5 of its row.
 //
 // All arithmetic is integer work on the fp32 bit patterns, so the result does
 // not depend on the denormal or rounding mode of the float units.
@@ -98,6 +102,15 @@ __device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
   return encode_mag<1, 0, 0x7u>(bits, e) | ((bits >> 31) << 3);
 }
 
+// FP6: E2M3 (bias 1, 3 mantissa bits, largest 7.5 = 0x1F) and E3M2 (bias 3,
+// 2 mantissa bits, largest 28 = 0x1F), sign in bit 5.
+__device__ __forceinline__ uint32_t encode_e2m3(uint32_t bits, int e) {
+  return encode_mag<3, 0, 0x1Fu>(bits, e) | ((bits >> 31) << 5);
+}
+__device__ __forceinline__ uint32_t encode_e3m2(uint32_t bits, int e) {
+  return encode_mag<2, -2, 0x1Fu>(bits, e) | ((bits >> 31) << 5);
+}
+
 // Two's complement integer code of x * 2^-e in BITS bits: a "format" whose
 // spacing is 1 everywhere (KMIN = MBITS, so every value takes the subnormal
 // branch of encode_mag) rounds |x * 2^-e| to the nearest integer, ties to
@@ -118,7 +131,11 @@ __device__ __forceinline__ uint32_t encode_int(uint32_t bits, int e) {
 template <int ELEM>
 __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int sub, uint8_t* __restrict__ Q,
                                                uint8_t* __restrict__ S) {
-  constexpr int kEmax = (ELEM == kFmtFp8) ? 8 : (ELEM == kFmtBf8) ? 15 : (ELEM == kElemInt2) ? 0 : 2;
+  constexpr int kEmax = (ELEM == kFmtFp8)   ? 8
+                        : (ELEM == kFmtBf8) ? 15
+                        : (ELEM == kElemInt2) ? 0
+                        : (ELEM == kFmtBf6)   ? 4
+                                              : 2;  // E2M1, INT4, E2M3
   constexpr bool kByte = ELEM == kFmtFp8 || ELEM == kFmtBf8;  // one code per byte
   uint32_t amax = 0u;
 #pragma unroll
@@ -142,6 +159,8 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
                : (ELEM == kFmtBf8)   ? encode_e5m2((uint32_t)x[i], e)
                : (ELEM == kElemInt4) ? encode_int<4>((uint32_t)x[i], e)
                : (ELEM == kElemInt2) ? encode_int<2>((uint32_t)x[i], e)
+               : (ELEM == kFmtFp6)   ? encode_e2m3((uint32_t)x[i], e)
+               : (ELEM == kFmtBf6)   ? encode_e3m2((uint32_t)x[i], e)
                                      : encode_e2m1((uint32_t)x[i], e);
   }
   // The codes are written once and read by a later GEMM: non-temporal
@@ -153,6 +172,13 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
                                 reinterpret_cast<uint32_t*>(Q + off));
   } else if (ELEM == kElemInt2) {
     __builtin_nontemporal_store((uint8_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6)), Q + (off >> 2));
+  } else if (ELEM == kFmtFp6 || ELEM == kFmtBf6) {
+    // four 6-bit codes = 3 bytes at byte 3/4 of the element index
+    const uint32_t v = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18);
+    uint8_t* q = Q + (off >> 2) * 3;
+    __builtin_nontemporal_store((uint8_t)v, q);
+    __builtin_nontemporal_store((uint8_t)(v >> 8), q + 1);
+    __builtin_nontemporal_store((uint8_t)(v >> 16), q + 2);
   } else {
     __builtin_nontemporal_store((uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12)),
                                 reinterpret_cast<uint16_t*>(Q + (off >> 1)));
@@ -206,6 +232,12 @@ hipError_t launch_quantize(const float* X, int64_t rows, int64_t K, int elem, vo
                        total);
   else if (elem == kElemInt2)
     hipLaunchKernelGGL(quantize_kernel<kElemInt2>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
+                       total);
+  else if (elem == kFmtFp6)
+    hipLaunchKernelGGL(quantize_kernel<kFmtFp6>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
+                       total);
+  else if (elem == kFmtBf6)
+    hipLaunchKernelGGL(quantize_kernel<kFmtBf6>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,
                        total);
   else
     hipLaunchKernelGGL(quantize_kernel<kFmtFp4>, dim3((unsigned)grid), dim3(256), 0, stream, X, (uint8_t*)Q, S,

@@ -35,7 +35,7 @@ class Workload:
     N: int
     K: int
     seed: int
-    elem_a: str  # "e4m3" | "e5m2" | "e2m1" | "int4" | "int2" | "fp16"
+    elem_a: str  # "e4m3" | "e5m2" | "e2m1" | "e2m3" | "e3m2" | "int4" | "int2" | "fp16"
     elem_b: str
     recipe: str
     description: str
@@ -64,6 +64,10 @@ WORKLOADS = {
                  "decode GEMM, MXFP8 activations x INT4 weights (UE8M0 per 32), the decode sources"),
         Workload("decode_int2_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "int2", "decode",
                  "decode GEMM, MXFP8 activations x INT2 weights (UE8M0 per 32), the decode sources"),
+        Workload("decode_e2m3_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "e2m3", "decode",
+                 "decode GEMM, MXFP8 activations x FP6 E2M3 weights (UE8M0 per 32), the decode sources"),
+        Workload("decode_e3m2_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "e3m2", "decode",
+                 "decode GEMM, MXFP8 activations x FP6 E3M2 weights (UE8M0 per 32), the decode sources"),
     ]
 }
 

@@ -15,6 +15,8 @@ import torch
 
 E4M3 = 0
 E5M2 = 1
+E2M3 = 2
+E3M2 = 3
 E2M1 = 4
 INT4 = 8
 INT2 = 9
@@ -26,10 +28,13 @@ FMT_FP8_BF8 = 4
 FMT_BF8_FP8 = 5
 FMT_FP8_INT4 = 6
 FMT_FP8_INT2 = 7
+FMT_FP8_FP6 = 8
+FMT_FP8_BF6 = 9
 
 _FMT_ELEMS = {FMT_FP8_FP8: (E4M3, E4M3), FMT_FP8_FP4: (E4M3, E2M1), FMT_FP4_FP4: (E2M1, E2M1),
               FMT_BF8_BF8: (E5M2, E5M2), FMT_FP8_BF8: (E4M3, E5M2), FMT_BF8_FP8: (E5M2, E4M3),
-              FMT_FP8_INT4: (E4M3, INT4), FMT_FP8_INT2: (E4M3, INT2)}
+              FMT_FP8_INT4: (E4M3, INT4), FMT_FP8_INT2: (E4M3, INT2), FMT_FP8_FP6: (E4M3, E2M3),
+              FMT_FP8_BF6: (E4M3, E3M2)}
 
 # output types and activations of the fused epilogue (MXG_OUT_*, MXG_ACT_*)
 OUT_F32 = 0
@@ -113,6 +118,8 @@ def _row_bytes(K: int, elem: int) -> int:
         return K // 2
     if elem == INT2:
         return K // 4
+    if elem in (E2M3, E3M2):
+        return K // 4 * 3
     return K
 
 

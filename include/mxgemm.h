@@ -60,9 +60,16 @@ extern "C" {
  * section "量子化データ型のネイティブサポート", with the block-wise scale of its
  * section "2-bit 量子化の限界圧縮を探る".  INT4 codes are packed two per byte
  * (even K index in the low nibble), INT2 codes four per byte (K index k in
- * bits 2 (k mod 4)). */
+ * bits 2 (k mod 4)).  E2M3 / E3M2 are the FP6 operands of the scaled matrix
+ * unit, taken with the OCP Microscaling definitions (the pages name the type
+ * but no layout): E2M3 sign, 2 exponent bits (bias 1), 3 mantissa bits,
+ * largest 7.5; E3M2 sign, 3 exponent bits (bias 3), 2 mantissa bits, largest
+ * 28; no NaN or infinity codes; packed little-endian, element k at bits
+ * 6k .. 6k+5 of its row (3 bytes per 4 elements). */
 #define MXG_ELEM_E4M3 0
 #define MXG_ELEM_E5M2 1
+#define MXG_ELEM_E2M3 2
+#define MXG_ELEM_E3M2 3
 #define MXG_ELEM_E2M1 4
 #define MXG_ELEM_INT4 8
 #define MXG_ELEM_INT2 9
@@ -76,6 +83,8 @@ extern "C" {
 #define MXG_FMT_BF8_FP8 5   /* E5M2 x E4M3 */
 #define MXG_FMT_FP8_INT4 6  /* E4M3 activations x INT4 weights */
 #define MXG_FMT_FP8_INT2 7  /* E4M3 activations x INT2 weights */
+#define MXG_FMT_FP8_FP6 8   /* E4M3 activations x E2M3 (FP6) weights */
+#define MXG_FMT_FP8_BF6 9   /* E4M3 activations x E3M2 (FP6) weights */
 
 /* Largest accepted M, N (rows) and K. */
 #define MXG_MAX_DIM (1 << 20)
@@ -93,13 +102,14 @@ extern "C" {
  * For every row r and every block b of 32 consecutive elements along K:
  *   amax = max |X[r][32b .. 32b+31]|;
  *   e    = floor(log2(amax)) - emax  (emax = 8 for E4M3, 15 for E5M2, 2 for
- *          E2M1 and INT4, 0 for INT2: the exponent of the largest power of
- *          two in the element range),
+ *          E2M1, E2M3 and INT4, 4 for E3M2, 0 for INT2: the exponent of the
+ *          largest power of two in the element range),
  *          clamped to [-127, 127]; e = -127 when amax = 0;
  *   S[r][b] = e + 127;
  *   Q[r][k] = round-to-nearest-even(X[r][k] * 2^-e), saturated to +-448
- *             (E4M3), +-57344 (E5M2), +-6 (E2M1), -8..7 (INT4) or -2..1
- *             (INT2); float codes keep the sign (-0 -> 0x80 / 0x8).
+ *             (E4M3), +-57344 (E5M2), +-6 (E2M1), +-7.5 (E2M3), +-28 (E3M2),
+ *             -8..7 (INT4) or -2..1 (INT2); float codes keep the sign
+ *             (-0 -> 0x80 / 0x20 / 0x8).
  * A block holding a NaN or an infinity gets S = 255 (NaN) and zero codes.
  * E4M3 saturating rather than overflowing follows "Resumo Técnico: RIGEL",
  * section 3 (saturation); one E8M0 scale per 32 elements follows the WWDC26
@@ -109,8 +119,9 @@ extern "C" {
  *   X     device, rows x K fp32, row-major, 16-byte aligned (read only)
  *   rows  >= 1;  K >= 32, K % 32 == 0
  *   elem  MXG_ELEM_E4M3 or MXG_ELEM_E5M2 (Q: rows x K bytes), MXG_ELEM_E2M1 or
- *         MXG_ELEM_INT4 (Q: rows x K/2 bytes, even k in the low nibble) or
- *         MXG_ELEM_INT2 (Q: rows x K/4 bytes); Q 16-byte aligned (written)
+ *         MXG_ELEM_INT4 (Q: rows x K/2 bytes, even k in the low nibble),
+ *         MXG_ELEM_INT2 (Q: rows x K/4 bytes), MXG_ELEM_E2M3 or
+ *         MXG_ELEM_E3M2 (Q: rows x 3K/4 bytes); Q 16-byte aligned (written)
  *   S     device, rows x K/32 bytes (written)
  * Returns MXG_OK or an error status.  The output is bit-for-bit deterministic.
  */
@@ -122,7 +133,8 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  *
  *   A, scaleA  device; A is M x K codes (E4M3 / E5M2: M*K bytes; E2M1: M*K/2
  *              bytes), scaleA is M x K/32 UE8M0 bytes
- *   (B: N x K codes of its element format: INT4 N*K/2 bytes, INT2 N*K/4)
+ *   (B: N x K codes of its element format: INT4 N*K/2 bytes, INT2 N*K/4,
+ *    FP6 3N*K/4)
  *   B, scaleB  device; B is N x K codes, scaleB is N x K/32 bytes
  *   C          device, M x N fp32 row-major, 16-byte aligned; overwritten
  *   M, N       >= 1 (any value; edges are masked); K >= 32, K % 32 == 0
@@ -133,7 +145,9 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * E4M3 / E2M1 codes of the same values (exact: -8..7 and -2..1 are values of
  * those formats), remapped in registers; they take the decode kernel (INT2:
  * K a multiple of 4096) and the split-K kernel, once per 64 rows of A when
- * M > 64.
+ * M > 64.  FP6 weights (MXG_FMT_FP8_FP6 / _BF6) are MFMA operands as stored
+ * (the instruction's E2M3 / E3M2 modes: a lane's 32 codes are its 24 bytes of
+ * a row), on the split-K kernel for every M (once per 64 rows of A).
  * Decode shapes with E4M3 activations and E4M3 or E2M1 weights take
  * weight-streaming kernels: for M <= 64 and K a multiple of 1024 from 2048,
  * one that reads B once per launch (fp32 C: all rows per launch, K in chunks

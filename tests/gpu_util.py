@@ -14,7 +14,8 @@ DEV = "cuda:0"
 
 FMT_ELEMS = {0: (oracle.E4M3, oracle.E4M3), 1: (oracle.E4M3, oracle.E2M1), 2: (oracle.E2M1, oracle.E2M1),
              3: (oracle.E5M2, oracle.E5M2), 4: (oracle.E4M3, oracle.E5M2), 5: (oracle.E5M2, oracle.E4M3),
-             6: (oracle.E4M3, oracle.INT4), 7: (oracle.E4M3, oracle.INT2)}
+             6: (oracle.E4M3, oracle.INT4), 7: (oracle.E4M3, oracle.INT2), 8: (oracle.E4M3, oracle.E2M3),
+             9: (oracle.E4M3, oracle.E3M2)}
 
 # Error model of one scaled-MFMA instruction (v_mfma_scale_f32_16x16x128_
 # f8f6f4): the products of one 128-element step are added in one operation

@@ -54,7 +54,7 @@ def test_validation_codes(lib):
     assert _run(lib, *ok, 16, 16, 48, 0, None) == 1                         # K % 32 != 0
     assert _run(lib, *ok, 0, 16, 64, 0, None) == 1                          # M = 0
     assert _run(lib, *ok, 16, -1, 64, 0, None) == 1                         # N < 0
-    assert _run(lib, *ok, 16, 16, 64, 8, None) == 1                         # unknown fmt
+    assert _run(lib, *ok, 16, 16, 64, 10, None) == 1                        # unknown fmt
     assert _run(lib, 0x1001, A, A, A, A, 16, 16, 64, 0, None) == 2          # misaligned A
     assert _run(lib, A, A, A, A, 0x1008, 16, 16, 64, 0, None) == 2          # misaligned C
     assert b"aligned" in lib.mxgemm_status_string(2)
@@ -62,7 +62,7 @@ def test_validation_codes(lib):
     q.restype = ctypes.c_int
     q.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p]
-    assert q(A, 4, 64, 3, A, A, None) == 1                                  # unknown element
+    assert q(A, 4, 64, 5, A, A, None) == 1                                  # unknown element
     assert q(A, 4, 40, 0, A, A, None) == 1                                  # K % 32 != 0
     assert q(0x1004, 4, 64, 0, A, A, None) == 2                             # misaligned X
     f = lib.fp16gemm_run

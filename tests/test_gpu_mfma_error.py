@@ -9,7 +9,8 @@ quantizer): a dominant product beside many small ones at gaps of 0 to 40
 binades, cancelling pairs of large products, random codes over the whole
 element range at unit and at varying block scales,
 for every operand-format pair.  The model the parity gate uses is asserted on
-all of them:
+all of them (the FP6 formats are checked against the oracle's pinned value
+tables):
 
     |result - exact| <= MFMA_STEP_KAPPA * max_k |a_k b_k| + 2^-24 |exact|
 
@@ -47,7 +48,16 @@ def _device():
 
 
 def _table(elem):
+    if elem == oracle.E2M3:
+        return oracle.e2m3_table()
+    if elem == oracle.E3M2:
+        return oracle.e3m2_table()
     return {oracle.E4M3: E4, oracle.E5M2: E5, oracle.E2M1: E2}[elem]
+
+
+def _neg(elem):
+    """The sign bit of an element code."""
+    return {oracle.E2M1: 0x8, oracle.E2M3: 0x20, oracle.E3M2: 0x20}.get(elem, 0x80)
 
 
 def _finite_codes(elem):
@@ -74,7 +84,12 @@ def _smallest(elem):
 
 def _pack(vals_codes, elem):
     """rows x K element codes -> the operand's byte plane (E2M1: two per
-    byte, even k in the low nibble)."""
+    byte, even k in the low nibble; FP6: 6 bits each, element k at bits
+    6k .. 6k+5 of the row, little-endian)."""
+    if elem in (oracle.E2M3, oracle.E3M2):
+        c = vals_codes.astype(np.uint8)
+        bits = ((c[:, :, None] >> np.arange(6)) & 1).reshape(c.shape[0], -1)
+        return np.ascontiguousarray(np.packbits(bits.astype(np.uint8), axis=1, bitorder="little"))
     if elem != oracle.E2M1:
         return np.ascontiguousarray(vals_codes.astype(np.uint8))
     c = vals_codes.astype(np.uint8)
@@ -93,7 +108,7 @@ def _operands(elem, rows, rng, families):
         fam = families[r % len(families)]
         if fam == "ones":
             codes[r] = one
-            codes[r, rng.random(K) < 0.5] |= 0x80 if elem != oracle.E2M1 else 0x8
+            codes[r, rng.random(K) < 0.5] |= _neg(elem)
         elif fam == "dominant":
             # one large element, the rest small, at block-scale gaps of
             # 0 .. 40 binades
@@ -101,7 +116,7 @@ def _operands(elem, rows, rng, families):
             small = fin[(np.abs(_table(elem)[fin]) > 0) & (np.abs(_table(elem)[fin]) <= 2 * tiny + 1e-30)]
             codes[r] = rng.choice(small, size=K)
             k = int(rng.integers(0, 32))
-            neg = (0x80 if elem != oracle.E2M1 else 0x8) if rng.random() < 0.5 else 0
+            neg = _neg(elem) if rng.random() < 0.5 else 0
             codes[r, k] = _code_of(elem, big) | neg
             scales[r, 0] = 127 + gap
             scales[r, 1:] = 127 - gap
@@ -109,7 +124,7 @@ def _operands(elem, rows, rng, families):
             # +X and -X in one step beside small terms: the result is the small part
             small = fin[(np.abs(_table(elem)[fin]) > 0) & (np.abs(_table(elem)[fin]) <= 4 * tiny + 1e-30)]
             codes[r] = rng.choice(small, size=K)
-            neg = 0x80 if elem != oracle.E2M1 else 0x8
+            neg = _neg(elem)
             codes[r, 3] = _code_of(elem, big)
             codes[r, 40] = _code_of(elem, big) | neg
             gap = int(rng.integers(0, 16))
@@ -169,7 +184,7 @@ def _run_single_steps(fmt, seed, M=16, N=8192, fam_a=FAMILIES_A, fam_b=FAMILIES_
     return c, ref, ab, sm
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5, 8, 9])
 def test_single_instruction_error_model(fmt):
     c, ref, ab, sm = _run_single_steps(fmt, 1000 + fmt)
     assert np.isfinite(ref).all() and np.isfinite(c).all()
