@@ -21,8 +21,21 @@
 // emax = 2 (E2M3, 7.5 = 1.875 * 2^2) and 4 (E3M2, 28 = 1.75 * 2^4), and are
 // packed little-endian, element k at bits 6k .. 6k+5 of its row.
 //
-// All arithmetic is integer work on the fp32 bit patterns, so the result does
-// not depend on the denormal or rounding mode of the float units.
+// The block exponent is integer work on the fp32 bit patterns.  E4M3, E5M2
+// and E2M1 codes come from gfx950's conversion instructions (fp32 -> OCP
+// E4M3 / E5M2 pairs, fp32 -> E2M1 pairs) applied to x * 2^-e: the scaling is
+// exact (a power of two; a product small enough to lose bits as an fp32
+// subnormal lies far below half the format's smallest subnormal, so its code
+// is a signed zero either way), the value is first clamped to the largest
+// finite magnitude, which gives the saturation, and the conversion rounds to
+// nearest even in the default float mode of a kernel (round to nearest,
+// fp32 subnormals kept).  The integer and FP6 codes are computed in integer
+// arithmetic (encode_mag below).  Both routes are bit-exact against the
+// float64 reference on every E4M3 tie, every mantissa at the exponents where
+// the rounding regime changes, and blocks of subnormals.  The integer route
+// for E4M3 ran the 8192 x 8192 quantization at 66 us; the conversions bring it
+// to the memory stream (the encode, ~25 VALU instructions per element, had
+// been the limit).
 //
 // Work mapping: 8 lanes per block, 4 elements (one 16-byte load) per lane; a
 // wave covers 8 consecutive blocks = 1 KiB of input with fully coalesced loads
@@ -35,6 +48,12 @@
 
 namespace mxg {
 namespace {
+
+// DPP lane patterns (gfx9 encodings): quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], and row_half_mirror (lane i of each 8 takes lane 7 - i).
+constexpr int kDppSwap1 = 0xB1;
+constexpr int kDppSwap2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
 
 // |x| = s * 2^(ex - 23) with s < 2^24; s = 0 for zero.
 struct Mag {
@@ -87,21 +106,6 @@ __device__ __forceinline__ uint32_t encode_mag(uint32_t bits, int e) {
   return min(code, MAXCODE);
 }
 
-// E4M3 (bias 7, 3 mantissa bits, no infinity, largest finite 448 = 0x7E) and
-// E2M1 (bias 1, 1 mantissa bit, largest 6 = 0x7) codes of x * 2^-e.
-__device__ __forceinline__ uint32_t encode_e4m3(uint32_t bits, int e) {
-  return encode_mag<3, -6, 0x7Eu>(bits, e) | ((bits >> 31) << 7);
-}
-
-// E5M2 (bias 15, 2 mantissa bits, largest finite 57344 = 0x7B).
-__device__ __forceinline__ uint32_t encode_e5m2(uint32_t bits, int e) {
-  return encode_mag<2, -14, 0x7Bu>(bits, e) | ((bits >> 31) << 7);
-}
-
-__device__ __forceinline__ uint32_t encode_e2m1(uint32_t bits, int e) {
-  return encode_mag<1, 0, 0x7u>(bits, e) | ((bits >> 31) << 3);
-}
-
 // FP6: E2M3 (bias 1, 3 mantissa bits, largest 7.5 = 0x1F) and E3M2 (bias 3,
 // 2 mantissa bits, largest 28 = 0x1F), sign in bit 5.
 __device__ __forceinline__ uint32_t encode_e2m3(uint32_t bits, int e) {
@@ -136,14 +140,15 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
                         : (ELEM == kElemInt2) ? 0
                         : (ELEM == kFmtBf6)   ? 4
                                               : 2;  // E2M1, INT4, E2M3
-  constexpr bool kByte = ELEM == kFmtFp8 || ELEM == kFmtBf8;  // one code per byte
   uint32_t amax = 0u;
 #pragma unroll
   for (int i = 0; i < 4; i++) amax = max(amax, (uint32_t)x[i] & 0x7fffffffu);
-  // the 8 lanes of a block are consecutive lanes of one wave
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
+  // the 8 lanes of a block are consecutive lanes of one wave, half a DPP
+  // row: swap neighbours, swap pairs, then mirror the two quads (register
+  // moves, where a lane shuffle would go through the LDS crossbar)
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, kDppSwap1, 0xF, 0xF, false));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, kDppSwap2, 0xF, 0xF, false));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, kDppHalfMirror, 0xF, 0xF, false));
   const bool bad = amax >= 0x7f800000u;  // infinity or NaN present
   int e = -127;
   if (amax != 0u) {
@@ -151,26 +156,45 @@ __device__ __forceinline__ void quantize_block(const v4i& x, int64_t blk, int su
     e = floor_log2_u(m.s) + m.ex - 23 - kEmax;
     e = min(max(e, -127), 127);
   }
+  const int64_t off = blk * 32 + sub * 4;  // element index
+  if constexpr (ELEM == kFmtFp8 || ELEM == kFmtBf8 || ELEM == kFmtFp4) {
+    constexpr float kMax = ELEM == kFmtFp8 ? 448.f : ELEM == kFmtBf8 ? 57344.f : 6.f;
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = __builtin_amdgcn_fmed3f(ldexpf(__int_as_float(x[i]), -e), -kMax, kMax);
+    // the codes are written once and read by a later GEMM: non-temporal
+    // stores keep them from displacing the input stream in the caches
+    if constexpr (ELEM == kFmtFp4) {
+      uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, y[2], y[3], 1.0f, 1);
+      __builtin_nontemporal_store((uint16_t)(bad ? 0u : v), reinterpret_cast<uint16_t*>(Q + (off >> 1)));
+    } else {
+      int v;
+      if constexpr (ELEM == kFmtFp8) {
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
+      } else {
+        v = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], v, true);
+      }
+      __builtin_nontemporal_store(bad ? 0u : (uint32_t)v, reinterpret_cast<uint32_t*>(Q + off));
+    }
+    if (sub == 0) S[blk] = bad ? (uint8_t)255 : (uint8_t)(e + 127);
+    return;
+  }
   uint32_t c[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     c[i] = bad ? 0u
-               : (ELEM == kFmtFp8)   ? encode_e4m3((uint32_t)x[i], e)
-               : (ELEM == kFmtBf8)   ? encode_e5m2((uint32_t)x[i], e)
                : (ELEM == kElemInt4) ? encode_int<4>((uint32_t)x[i], e)
                : (ELEM == kElemInt2) ? encode_int<2>((uint32_t)x[i], e)
                : (ELEM == kFmtFp6)   ? encode_e2m3((uint32_t)x[i], e)
-               : (ELEM == kFmtBf6)   ? encode_e3m2((uint32_t)x[i], e)
-                                     : encode_e2m1((uint32_t)x[i], e);
+                                     : encode_e3m2((uint32_t)x[i], e);
   }
   // The codes are written once and read by a later GEMM: non-temporal
   // stores keep them from displacing the input stream in the caches (E4M3
   // 8192 x 8192: 80 against 89-93 us, measured)
-  const int64_t off = blk * 32 + sub * 4;  // element index
-  if (kByte) {
-    __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                reinterpret_cast<uint32_t*>(Q + off));
-  } else if (ELEM == kElemInt2) {
+  if (ELEM == kElemInt2) {
     __builtin_nontemporal_store((uint8_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6)), Q + (off >> 2));
   } else if (ELEM == kFmtFp6 || ELEM == kFmtBf6) {
     // four 6-bit codes = 3 bytes at byte 3/4 of the element index
