@@ -443,7 +443,8 @@ struct PP128Kernel {
   static constexpr int SZ_SG = T::SCALED ? 2 * 128 * 16 : 0;
   static constexpr int SZ_GROUP = 2 * SZ_STAGE + 2 * SZ_SG;
   static constexpr int SZ_RED = 4 * 16 * 64 * 16;  // group 1's partials: 4 waves x 16 fragments x 64 lanes
-  static constexpr int LDS = 2 * SZ_GROUP > SZ_RED ? 2 * SZ_GROUP : SZ_RED;
+  static constexpr int SZ_CST = 4 * 4096;  // epilogue staging of group 0, after the partials
+  static constexpr int LDS = 2 * SZ_GROUP > SZ_RED + SZ_CST ? 2 * SZ_GROUP : SZ_RED + SZ_CST;
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
 
   template <int... I>
@@ -587,14 +588,26 @@ struct PP128Kernel {
     phase_barrier();
     if (grp == 1) return;
     // Lane (lg, r) of fragment (i, j) holds C[m][n .. n+3] with m = 16 i + r
-    // of the sub-tile's rows and n = 16 j + 4 lg of its columns.
+    // of the sub-tile's rows and n = 16 j + 4 lg of its columns.  Each 16 x
+    // 64 block (one i) goes through 4 KiB of this wave's LDS (16-byte chunks
+    // XOR-swizzled by row) and comes back row-contiguous, so that every store
+    // writes 256 bytes to each of 4 rows (whole cache lines) instead of 64
+    // bytes to each of 16.
+    uint8_t* cst = smem + SZ_RED + sw * 4096;
+    int le = lane;
+    asm volatile("" : "+v"(le));
+    const int lr = le & 15, llg = le >> 4;  // the fragment layout's (r, lg)
+    const int rr = le >> 4, cc = le & 15;   // read-back: row-in-quad, 16-byte chunk
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int64_t m = m0 + wr + 16 * i + r;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const v4f v = acc[i][j] + red[(i * 4 + j) * 64];
-        epi_store4<true>(a.e, a.N, m, n0 + wc + 16 * j + 4 * lg, v, true);
+      for (int j = 0; j < 4; j++)
+        *reinterpret_cast<v4f*>(cst + lr * 256 + (((j * 4 + llg) ^ lr) << 4)) = acc[i][j] + red[(i * 4 + j) * 64];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int row = q * 4 + rr;
+        const v4f v = *reinterpret_cast<const v4f*>(cst + row * 256 + ((cc ^ row) << 4));
+        epi_store4<true>(a.e, a.N, m0 + wr + 16 * i + row, n0 + wc + 4 * cc, v, true);
       }
     }
   }
