@@ -49,15 +49,21 @@ namespace {
 
 enum PPKind { kPPMX = 0, kPPF16 = 1 };
 
-// FA_, FB_: MFMA format ids of A and B (kFmtFp8 E4M3, kFmtBf8 E5M2, kFmtFp4 E2M1)
-template <int KIND, int FA_, int FB_>
+// FA_, FB_: MFMA format ids of A and B (kFmtFp8 E4M3, kFmtBf8 E5M2, kFmtFp4 E2M1).
+// KSTEPS_: MFMA k-steps (128 k each) per slice; 2 only for E2M1 x E2M1, whose
+// 256-k slices have the 128-byte rows (and LDS layout) of an fp8 slice.
+template <int KIND, int FA_, int FB_, int KSTEPS_ = 1>
 struct PPCfg {
   static constexpr int FA = FA_, FB = FB_;
   static constexpr bool AF4 = FA == kFmtFp4, BF4 = FB == kFmtFp4;
   static constexpr bool SCALED = (KIND == kPPMX);
   static constexpr bool A_FP4 = AF4, B_FP4 = BF4;
-  static constexpr int RA = AF4 ? 64 : 128;   // bytes per A row per slice
-  static constexpr int RB = BF4 ? 64 : 128;
+  static constexpr int KSTEPS = KSTEPS_;
+  static_assert(KSTEPS == 1 || (KSTEPS == 2 && AF4 && BF4 && SCALED), "two k-steps per slice: E2M1 x E2M1 only");
+  static constexpr int RA = AF4 ? 64 * KSTEPS : 128;   // bytes per A row per slice
+  static constexpr int RB = BF4 ? 64 * KSTEPS : 128;
+  // scale groups: 16 bytes per row, i.e. 4 / KSTEPS slices
+  static constexpr int GS = 4 / KSTEPS;
   static constexpr int SZ_AH = 128 * RA;       // one A half, one stage
   static constexpr int SZ_B = 256 * RB;
   // scale buffers hold a group of 4 slices: 16 bytes per row
@@ -171,6 +177,21 @@ struct PPKernel {
     (mfma_scaled_acc_pk<FB, FA, I / 8, (I % 8) & 3>(acc[I % 8][I / 8], bf[I / 8], af[I % 8], sb, sa[(I % 8) >> 2]),
      ...);
   }
+  // E2M1 operand of k-step H of a 128-byte fragment row: bytes 16 lg .. of
+  // the step's 64 (H = 0: the fragment's first half, H = 1: its second)
+  template <int H>
+  static __device__ __forceinline__ v8i fp4_step(const v8i& f) {
+    return v8i{f[4 * H], f[4 * H + 1], f[4 * H + 2], f[4 * H + 3], 0, 0, 0, 0};
+  }
+  template <int H, int... I>
+  static __device__ __forceinline__ void compute_scaled_step(v4f (&acc)[8][4], const v8i (&af)[8], const v8i (&bf)[4],
+                                                             const int (&sa)[2], int sb,
+                                                             std::integer_sequence<int, I...>) {
+    constexpr int FB = T::FB, FA = T::FA;
+    (mfma_scaled_acc_pk<FB, FA, I / 8, (I % 8) & 3>(acc[I % 8][I / 8], fp4_step<H>(bf[I / 8]), fp4_step<H>(af[I % 8]),
+                                                    sb, sa[(I % 8) >> 2]),
+     ...);
+  }
 
   static __device__ __forceinline__ void run(const PPArgs& a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -228,7 +249,7 @@ struct PPKernel {
     auto copy_sb_group = [&](int G) {
       copy_scale_group(rs_sb, nb, sw * 64, G, smem + T::OFF_SB + (G & 1) * T::SZ_SB + sw * 1024, os);
     };
-    const int ng = (S + 3) >> 2;
+    const int ng = T::KSTEPS == 1 ? (S + 3) >> 2 : (S + 1) >> 1;  // scale groups
 
     // The workgroup is persistent: it takes tiles blockIdx.x, + gridDim.x, ...
     // (the grid is at most one workgroup per CU), so there is no dispatch gap
@@ -268,8 +289,10 @@ struct PPKernel {
       const int st = s & 1;
       v8i af[8], bf[4];
       // scale bytes packed four to a register: byte i&3 of sa[i>>2] belongs
-      // to A fragment i, byte j of sb to B fragment j
+      // to A fragment i, byte j of sb to B fragment j (k-step 1 of a two-step
+      // slice: sa1, sb1)
       int sa[2] = {0, 0}, sb = 0;
+      int sa1[2] = {0, 0}, sb1 = 0;
       {
         const uint8_t* la = smem + (grp ? T::OFF_ABOT : T::OFF_ATOP) + st * T::SZ_AH;
         const uint8_t* lb = smem + T::OFF_B + st * T::SZ_B;
@@ -277,11 +300,27 @@ struct PPKernel {
         for (int i = 0; i < 8; i++) af[i] = read_frag<T::RA>(la, i * 16 + r, lg);
 #pragma unroll
         for (int j = 0; j < 4; j++) bf[j] = read_frag<T::RB>(lb, sw * 64 + j * 16 + r, lg);
-        if (T::SCALED) {
+        if (T::SCALED && T::KSTEPS == 1) {
           // slice s: group buffer (s >> 2) & 1, bytes 4 (s & 3) + lg of each row
           const int sg = (s >> 2) & 1, sk = (s & 3) * 4 + lg;
           const uint8_t* lsa = smem + (grp ? T::OFF_SABOT : T::OFF_SATOP) + sg * T::SZ_SAH;
           const uint8_t* lsb = smem + T::OFF_SB + sg * T::SZ_SB;
+          uint32_t x[8], y[4];
+#pragma unroll
+          for (int i = 0; i < 8; i++) x[i] = lsa[(i * 16 + r) * 16 + sk];
+#pragma unroll
+          for (int j = 0; j < 4; j++) y[j] = lsb[(sw * 64 + j * 16 + r) * 16 + sk];
+          sa[0] = (int)(x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24));
+          sa[1] = (int)(x[4] | (x[5] << 8) | (x[6] << 16) | (x[7] << 24));
+          sb = (int)(y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24));
+        } else if (T::SCALED) {
+          // two k-steps: group buffer (s >> 1) & 1, bytes 8 (s & 1) + 4 h + lg
+          // of each row for step h;
+          const int sg = (s >> 1) & 1, sk = (s & 1) * 8 + lg;
+          const uint8_t* lsa = smem + (grp ? T::OFF_SABOT : T::OFF_SATOP) + sg * T::SZ_SAH;
+          const uint8_t* lsb = smem + T::OFF_SB + sg * T::SZ_SB;
+          // step 0 here; step 1 after this phase's copies (below), so that the
+          // two steps' byte temporaries are never live together
           uint32_t x[8], y[4];
 #pragma unroll
           for (int i = 0; i < 8; i++) x[i] = lsa[(i * 16 + r) * 16 + sk];
@@ -297,14 +336,43 @@ struct PPKernel {
           if (s + 2 < S) copy_atop(s + 2);
           if (s + 1 < S) copy_abot(s + 1);
         }
-        if (T::SCALED && (s & 3) == 1 && (s >> 2) + 1 < ng) {
+        if constexpr (T::KSTEPS == 1) {
+          if (T::SCALED && (s & 3) == 1 && (s >> 2) + 1 < ng) {
+            if (grp == 0)
+              copy_sb_group((s >> 2) + 1);
+            else
+              copy_sa_group((s >> 2) + 1);
+          }
+        } else if ((s & 1) == 0 && (s >> 1) + 1 < ng) {
+          // groups of 2 slices: group G + 1 in slice 2G, after the last reads
+          // of group G - 1 (slice 2G - 1) and two slices before its first
+          // reads (slice 2G + 2)
           if (grp == 0)
-            copy_sb_group((s >> 2) + 1);
+            copy_sb_group((s >> 1) + 1);
           else
-            copy_sa_group((s >> 2) + 1);
+            copy_sa_group((s >> 1) + 1);
+        }
+        if constexpr (T::SCALED && T::KSTEPS == 2) {
+          // the step-1 scale bytes: after the copies are issued and the step-0
+          // bytes are packed (the fence keeps the loads below it)
+          asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sb)::"memory");
+          const int sg = (s >> 1) & 1, sk = (s & 1) * 8 + 4 + lg;
+          const uint8_t* lsa = smem + (grp ? T::OFF_SABOT : T::OFF_SATOP) + sg * T::SZ_SAH;
+          const uint8_t* lsb = smem + T::OFF_SB + sg * T::SZ_SB;
+          uint32_t x[8], y[4];
+#pragma unroll
+          for (int i = 0; i < 8; i++) x[i] = lsa[(i * 16 + r) * 16 + sk];
+#pragma unroll
+          for (int j = 0; j < 4; j++) y[j] = lsb[(sw * 64 + j * 16 + r) * 16 + sk];
+          sa1[0] = (int)(x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24));
+          sa1[1] = (int)(x[4] | (x[5] << 8) | (x[6] << 16) | (x[7] << 24));
+          sb1 = (int)(y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24));
         }
       }
-      if constexpr (T::SCALED) {
+      if constexpr (T::SCALED && T::KSTEPS == 2) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_nop 4"
+                     : "+v"(sa[0]), "+v"(sa[1]), "+v"(sb), "+v"(sa1[0]), "+v"(sa1[1]), "+v"(sb1)::"memory");
+      } else if constexpr (T::SCALED) {
         // The barrier asm takes the packed scales as operands, so the packing
         // (VALU) stays in the load phase instead of being sunk into the
         // compute phase; the s_nop keeps the wait states an MFMA needs after
@@ -314,7 +382,10 @@ struct PPKernel {
       } else {
         phase_barrier();
       }
-      if constexpr (T::SCALED) {
+      if constexpr (T::SCALED && T::KSTEPS == 2) {
+        compute_scaled_step<0>(acc, af, bf, sa, sb, std::make_integer_sequence<int, 32>{});
+        compute_scaled_step<1>(acc, af, bf, sa1, sb1, std::make_integer_sequence<int, 32>{});
+      } else if constexpr (T::SCALED) {
         compute_scaled(acc, af, bf, sa, sb, std::make_integer_sequence<int, 32>{});
       } else {
 #pragma unroll
@@ -352,7 +423,13 @@ struct PPKernel {
       // index the compiler cannot see through, so they are not hoisted out of
       // the tile loop and kept live (in registers the K loop needs)
       int le = lane;
-      asm volatile("" : "+v"(le));
+      if constexpr (T::KSTEPS == 2) {
+        // recomputed rather than kept: holding the lane index across the
+        // two-step K loop would spill it
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+      } else {
+        asm volatile("" : "+v"(le));
+      }
       const int lr = le & 15, llg = le >> 4;     // the fragment layout's (r, lg)
       const int rr = le >> 4, cc = le & 15;      // read-back: row-in-quad, 16-byte chunk
       // every store of this lane covers columns nc .. nc+3: its bias is
@@ -671,7 +748,10 @@ hipError_t launch_mx_pingpong(const void* A, const uint8_t* SA, const void* B, c
   switch (fmt) {
     case 0: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtFp8>>(a, 128, stream);
     case 1: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtFp4>>(a, 128, stream);
-    case 2: return launch_pp<PPCfg<kPPMX, kFmtFp4, kFmtFp4>>(a, 128, stream);
+    case 2:
+      // 256-k slices (two MFMA k-steps per phase) where K allows
+      return (K % 256) == 0 ? launch_pp<PPCfg<kPPMX, kFmtFp4, kFmtFp4, 2>>(a, 256, stream)
+                            : launch_pp<PPCfg<kPPMX, kFmtFp4, kFmtFp4>>(a, 128, stream);
     case 3: return launch_pp<PPCfg<kPPMX, kFmtBf8, kFmtBf8>>(a, 128, stream);
     case 4: return launch_pp<PPCfg<kPPMX, kFmtFp8, kFmtBf8>>(a, 128, stream);
     default: return launch_pp<PPCfg<kPPMX, kFmtBf8, kFmtFp8>>(a, 128, stream);

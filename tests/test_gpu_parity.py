@@ -208,13 +208,16 @@ def test_mx_gemm_large_tiles_full():
 
 
 @pytest.mark.parametrize("fmt,K", [(0, 1024), (1, 1024), (2, 1024), (3, 1024), (4, 1024), (5, 1024), (0, 1152),
-                                   (5, 1408), (3, 1280), (0, 768)])
+                                   (5, 1408), (3, 1280), (0, 768), (2, 1152), (2, 1280), (2, 768), (2, 256)])
 def test_mx_gemm_persistent_two_tiles_full(fmt, K):
     """More 256 x 256 tiles (16 x 17 = 272) than the grid's one workgroup per
     CU, so some workgroups run a second tile after the tile transition (next
     tile's copies issued during the last slices, C staged through LDS); block
     scales vary.  The scales come in groups of 4 slices (K = 512); K = 768,
-    1152, 1280 and 1408 end with a partial group.  Checked in full."""
+    1152, 1280 and 1408 end with a partial group.  E2M1 x E2M1 (fmt 2) with
+    K % 256 == 0 runs 256-k slices (two MFMA k-steps each, scale groups of 2
+    slices: K = 1280 and 768 end with a partial group, K = 256 is one slice);
+    K = 1152 takes the 128-k slices.  Checked in full."""
     say("mx persistent two tiles", fmt, K)
     M, N = 4096, 4352
     a32, b32 = mx_sources("mxfp8_2048", M, N, K, seed=101 + fmt)
