@@ -520,7 +520,7 @@ struct PP128Kernel {
   static constexpr int SZ_SG = T::SCALED ? 2 * 128 * 16 : 0;
   static constexpr int SZ_GROUP = 2 * SZ_STAGE + 2 * SZ_SG;
   static constexpr int SZ_RED = 4 * 16 * 64 * 16;  // group 1's partials: 4 waves x 16 fragments x 64 lanes
-  static constexpr int SZ_CST = 4 * 4096;  // epilogue staging of group 0, after the partials
+  static constexpr int SZ_CST = 8 * 4096;  // epilogue staging, 4 KiB per wave, after the partials
   static constexpr int LDS = 2 * SZ_GROUP > SZ_RED + SZ_CST ? 2 * SZ_GROUP : SZ_RED + SZ_CST;
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a gfx950 CU");
 
@@ -654,32 +654,39 @@ struct PP128Kernel {
     for (; nbar < 2 * S0; nbar++) phase_barrier();
     mfma_drain(acc);
 
-    // every load phase and copy has completed: the stages are free
-    v4f* red = reinterpret_cast<v4f*>(smem) + sw * 16 * 64 + lane;
-    if (grp == 1) {
+    // every load phase and copy has completed: the stages are free.  The
+    // groups split the store: group 0 finishes row blocks i = 0, 1 of its
+    // sub-tile and group 1 blocks 2, 3, each after adding the other group's
+    // partial sums of those blocks, passed through LDS (8 KiB per wave); the
+    // sum is group 0's plus group 1's either way.
+    const int ikeep = 2 * grp;
+    v4f* give = reinterpret_cast<v4f*>(smem) + (grp * 4 + sw) * 8 * 64 + lane;
+    const v4f* take = reinterpret_cast<const v4f*>(smem) + ((1 - grp) * 4 + sw) * 8 * 64 + lane;
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) red[(i * 4 + j) * 64] = acc[i][j];
-    }
+      for (int j = 0; j < 4; j++) give[(i * 4 + j) * 64] = grp ? acc[i][j] : acc[2 + i][j];
     phase_barrier();
-    if (grp == 1) return;
     // Lane (lg, r) of fragment (i, j) holds C[m][n .. n+3] with m = 16 i + r
     // of the sub-tile's rows and n = 16 j + 4 lg of its columns.  Each 16 x
     // 64 block (one i) goes through 4 KiB of this wave's LDS (16-byte chunks
     // XOR-swizzled by row) and comes back row-contiguous, so that every store
     // writes 256 bytes to each of 4 rows (whole cache lines) instead of 64
     // bytes to each of 16.
-    uint8_t* cst = smem + SZ_RED + sw * 4096;
+    uint8_t* cst = smem + SZ_RED + wave * 4096;
     int le = lane;
     asm volatile("" : "+v"(le));
     const int lr = le & 15, llg = le >> 4;  // the fragment layout's (r, lg)
     const int rr = le >> 4, cc = le & 15;   // read-back: row-in-quad, 16-byte chunk
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int h = 0; h < 2; h++) {
+      const int i = ikeep + h;
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        *reinterpret_cast<v4f*>(cst + lr * 256 + (((j * 4 + llg) ^ lr) << 4)) = acc[i][j] + red[(i * 4 + j) * 64];
+      for (int j = 0; j < 4; j++) {
+        const v4f mine = grp ? acc[2 + h][j] : acc[h][j];
+        const v4f other = take[(h * 4 + j) * 64];
+        *reinterpret_cast<v4f*>(cst + lr * 256 + (((j * 4 + llg) ^ lr) << 4)) = grp ? other + mine : mine + other;
+      }
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int row = q * 4 + rr;
