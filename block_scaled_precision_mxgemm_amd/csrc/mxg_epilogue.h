@@ -53,11 +53,10 @@ __device__ __forceinline__ float gelu(float y) {
   return 0.5f * y * one_plus_erf;
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+// fp32 -> bf16 bits, round to nearest even (gfx950's conversion
+// instruction); NaN stays a NaN.
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // fp32 -> fp16 bits, round to nearest even (the hardware conversion).
