@@ -502,8 +502,7 @@ def bench_decode(dev, name="decode_16x28672x8192"):
     eager = time_windows(step)
     warm = time_windows(lambda i=0: mx.mxgemm_run(qa, sa, weights[0][0], weights[0][1], fmt, out=c))
     rec = timed_entry(cold, nbytes=nbytes)
-    kernel = ("skinny_kernel<fp8 x %s> (split-K, weights read once as FP6 MFMA operands)" % kname
-              if elem in (mx.E2M3, mx.E3M2) else "decode_kernel<fp8 x %s, K=8192> (LDS-staged weight stream)" % kname)
+    kernel = "decode_kernel<fp8 x %s, K=8192> (LDS-staged weight stream)" % kname
     rec.update({"kernel": kernel,
                 "us": rec["ms"] * 1e3, "us_best": rec["ms_min"] * 1e3, "algorithmic_bytes": nbytes,
                 "weight_copies_rotated": copies,

@@ -50,13 +50,14 @@ int validate_epi(const float* bias, int act, int out_type) {
 
 // integer weights (remapped in registers to MFMA operand codes) and FP6
 // weights (MFMA operands as stored): the split-K kernel takes them for every M
+// the decode kernel does not
 bool remapped_weights(int fmt) {
   return fmt == MXG_FMT_FP8_INT4 || fmt == MXG_FMT_FP8_INT2 || fmt == MXG_FMT_FP8_FP6 || fmt == MXG_FMT_FP8_BF6;
 }
 
 // Kernel choice for an MX product (arguments validated): the weight-streaming
-// decode kernel (E4M3 activations against E4M3, E2M1, INT4 or INT2 weights),
-// the split-K skinny kernel (the same, and FP6 weights), or the tiled /
+// decode kernel (E4M3 activations against E4M3, E2M1, E2M3, E3M2, INT4 or
+// INT2 weights), the split-K skinny kernel (the same), or the tiled /
 // ping-pong kernels (every 8- and 4-bit float format pair).  Integer and FP6
 // weights with more than 64 rows of activations run the split-K kernel once
 // per 64 rows (B is read once per 64 rows: a correct path for such shapes,

@@ -55,6 +55,12 @@ constexpr int kDecStagesDeep = 8;
 constexpr int kDeepMaxFrags = 1;
 constexpr int kBand = 128;                    // bytes of each weight row per stage and wave
 constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
+// FP6 weights: one 96-byte MFMA operand per row and stage, copied 12 bytes
+// per lane; the copy writes lane l at 16 l of LDS (the slot's last 4 bytes
+// are not written), so a stage keeps the 128-byte rows of the other formats
+// with 12-byte pieces in 16-byte slots, swizzled the same way
+constexpr bool is_fp6(int w) { return w == kFmtFp6 || w == kFmtBf6; }
+constexpr int band_bytes(int w) { return is_fp6(w) ? 96 : kBand; }  // global bytes of a row per stage
 // Reduced output blocks (16 x 16) a wave keeps in registers until its
 // copies are done.  A store issued inside the stream would sit among the copies in the
 // in-order vector-memory counter and make the next stage waits of that wave
@@ -83,10 +89,13 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0
 
 // Weight formats W: kFmtFp8 (E4M3, 128 bytes per 128-k MFMA operand),
 // kFmtFp4 (E2M1, 64 bytes), kElemInt4 (64 bytes, remapped in registers to
-// an E4M3 operand), kElemInt2 (32 bytes, remapped to an E2M1 operand).
-constexpr int op_bytes(int w) { return w == kFmtFp8 ? 128 : w == kElemInt2 ? 32 : 64; }
+// an E4M3 operand), kElemInt2 (32 bytes, remapped to an E2M1 operand),
+// kFmtFp6 / kFmtBf6 (E2M3 / E3M2, 96 bytes, MFMA operands as stored).
+constexpr int op_bytes(int w) { return w == kFmtFp8 ? 128 : is_fp6(w) ? 96 : w == kElemInt2 ? 32 : 64; }
 // MFMA operand format the weights are fed as
-constexpr int mfma_fmt(int w) { return (w == kFmtFp8 || w == kElemInt4) ? kFmtFp8 : kFmtFp4; }
+constexpr int mfma_fmt(int w) {
+  return is_fp6(w) ? w : (w == kFmtFp8 || w == kElemInt4) ? kFmtFp8 : kFmtFp4;
+}
 
 // K / 1024 = KW MFMAs (128 k each) per wave per fragment on average.  With
 // two MFMA operands per 128-byte stage (E2M1, INT4) and KW odd, waves 0-3
@@ -96,7 +105,7 @@ constexpr bool split_k(int w, int kw) { return op_bytes(w) == 64 && kw % 2 == 1;
 
 // LDS of one wave's ring and scale slots for WK MFMAs per fragment
 constexpr int ring_bytes(int w, int wk, int d) {
-  const int nq = wk / (128 / op_bytes(w));
+  const int nq = wk / (band_bytes(w) / op_bytes(w));
   const int nsi = (16 * wk + 63) / 64;
   const int nsl = (nq - 1 + d + nq - 1) / nq;
   return d * kStageBytes + nsl * nsi * 256;
@@ -111,7 +120,9 @@ struct Decode {
   static constexpr int D = D_;
   static constexpr int WK = KW + XK;                     // MFMAs per fragment of this wave
   static constexpr int OPB = op_bytes(W);                // bytes of a weight row per MFMA
-  static constexpr int MPS = 128 / OPB;                  // MFMAs per stage (128 bytes of a row)
+  static constexpr int BAND = band_bytes(W);             // global bytes of a weight row per stage
+  static constexpr int STAGE = kStageBytes;              // one stage in LDS: 16 rows of 128 bytes
+  static constexpr int MPS = BAND / OPB;                 // MFMAs per stage
   static constexpr int NQ = WK / MPS;                    // stages per fragment
   static constexpr int kBFmt = mfma_fmt(W);              // MFMA format of the weight operand
   static constexpr int SBW = 4 * WK;                     // scale bytes of a row per wave
@@ -134,7 +145,7 @@ struct Decode {
   static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8, NS4 = (SBW % 8) / 4;
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
   static_assert(NQ >= 1 && WK % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
-  static_assert(ring_bytes(W, WK, D) == D * kStageBytes + NSL * SZ_SC && SZ_WAVE >= ring_bytes(W, WK, D),
+  static_assert(ring_bytes(W, WK, D) == D * STAGE + NSL * SZ_SC && SZ_WAVE >= ring_bytes(W, WK, D),
                 "region layout");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
   static_assert(MB >= 1 && MB * WK <= 16, "A operands of all blocks in 128 VGPRs");
@@ -244,7 +255,7 @@ struct Decode {
     if (q == 0) {
       const auto rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)(a.SB + (int64_t)row0 * t.nb), 0, 16 * t.nb,
                                                           kRsrcWord3);
-      uint8_t* sc = t.wsm + D * kStageBytes + (fs % NSL) * SZ_SC;
+      uint8_t* sc = t.wsm + D * STAGE + (fs % NSL) * SZ_SC;
 #pragma unroll
       for (int i = 0; i < NSI; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(sc + i * 256), 4,
@@ -252,11 +263,11 @@ struct Decode {
                                                  (uint32_t)(4 * t.kb), 0, kStreamPolicy);
     }
     const auto rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)(a.B + (int64_t)row0 * t.rb), 0, 16 * t.rb, kRsrcWord3);
-    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * kStageBytes;
-    const uint32_t soff = (uint32_t)(t.kb * OPB + qv * kBand);
+    uint8_t* st = t.wsm + ((fs * NQ + q) & (D - 1)) * STAGE;
+    const uint32_t soff = (uint32_t)(t.kb * OPB + qv * BAND);
 #pragma unroll
     for (int h = 0; h < 2; h++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), is_fp6(W) ? 12 : 16,
                                                (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0,
                                                kStreamPolicy);
   }
@@ -334,8 +345,8 @@ struct Decode {
       wait_stage<0>();
     // stage s + D - 1, into the buffer read at stage s - 1
     issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ, FIRST);
-    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * kStageBytes;
-    const uint8_t* sc = t.wsm + D * kStageBytes + (f % NSL) * SZ_SC;
+    const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * STAGE;
+    const uint8_t* sc = t.wsm + D * STAGE + (f % NSL) * SZ_SC;
     const int g = t.g, r = t.r;
     const int sw = (r >> 1) & 7;
 #pragma unroll
@@ -351,6 +362,13 @@ struct Decode {
         const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + ((g ^ sw) << 4));
         const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else if constexpr (is_fp6(W)) {
+        // lane group g: k 32g .. 32g+31, the 24 bytes at 24g of the row's
+        // operand = pieces 2g and 2g + 1 (12 bytes each, in swizzled
+        // 16-byte slots)
+        const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + (((2 * g) ^ sw) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((2 * g + 1) ^ sw) << 4));
+        bv = v8i{lo[0], lo[1], lo[2], hi[0], hi[1], hi[2], 0, 0};
       } else if constexpr (W == kElemInt4) {
         const uint8_t* row = st + r * kBand;
         // the fp8 operand's k ranges, 8 bytes of INT4 codes each (bytes 8g
@@ -432,13 +450,17 @@ struct Decode {
     // has at least one: the grid is at most the fragment count)
     t.f_begin = (int)((int64_t)a.nfrags * blockIdx.x / gridDim.x);
     t.nf = (int)((int64_t)a.nfrags * (blockIdx.x + 1) / gridDim.x) - t.f_begin;
-    t.rb = (uint32_t)(a.ldk / (128 / OPB));
+    if constexpr (is_fp6(W))
+      t.rb = (uint32_t)((int64_t)a.ldk * OPB / 128);
+    else
+      t.rb = (uint32_t)(a.ldk / (128 / OPB));
     t.nb = (uint32_t)(a.ldk >> 5);
     // copy lane l: row l >> 3 (+8), physical chunk l & 7 holding logical chunk
     // (l & 7) ^ ((row >> 1) & 7)
     t.brow = t.lane >> 3;
 #pragma unroll
-    for (int h = 0; h < 2; h++) t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * 16);
+    for (int h = 0; h < 2; h++)
+      t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * (is_fp6(W) ? 12 : 16));
     // scale copy i, lane l: entry e = 64 i + l is row e / LPR, dword e % LPR
     // (entries past row 15 repeat row 15 into the slot's unused tail)
 #pragma unroll
@@ -515,7 +537,7 @@ hipError_t launch_dec_m(const DecArgs& a, int cus, hipStream_t stream) {
 // state of 14 or 16 MFMAs per wave no longer fits beside the A operands, and
 // with INT4 weights the remapped operands of 16 MFMAs per wave (the compiler
 // spills above 14).
-constexpr int max_kw(int w) { return w == kFmtFp8 ? 12 : w == kElemInt4 ? 14 : 16; }
+constexpr int max_kw(int w) { return (w == kFmtFp8 || is_fp6(w)) ? 12 : w == kElemInt4 ? 14 : 16; }
 // K / 1024 the kernel takes for a weight format: INT2 stages hold four MFMA
 // operands, so every wave's band must be whole stages without a split
 constexpr bool kw_ok(int w, int kw) { return kw >= 2 && kw <= max_kw(w) && (w != kElemInt2 || kw % 4 == 0); }
@@ -538,7 +560,8 @@ hipError_t launch_dec_k(const DecArgs& a, int cus, hipStream_t stream, std::inte
 
 // weight format of a (validated) format pair taken by the decode kernel
 int weight_format(int fmt) {
-  return fmt == 1 ? kFmtFp4 : fmt == 6 ? kElemInt4 : fmt == 7 ? kElemInt2 : kFmtFp8;
+  return fmt == 1 ? kFmtFp4 : fmt == 6 ? kElemInt4 : fmt == 7 ? kElemInt2 : fmt == 8 ? kFmtFp6 : fmt == 9 ? kFmtBf6
+                                                                                                     : kFmtFp8;
 }
 
 // Rows of A one launch covers: 64 for K <= 4096, 32 for K <= 8192, 16
@@ -555,7 +578,8 @@ int chunk_kw(int kw, int P, int i) { return kw / P + (i < kw % P ? 1 : 0); }
 
 }  // namespace
 bool decode_ok(int64_t M, int64_t K, int fmt, const uint8_t* SA, const uint8_t* SB, const Epi& e) {
-  if (!(M <= 64 && (fmt == 0 || fmt == 1 || fmt == 6 || fmt == 7) && (K % 1024) == 0 && K >= 2048 &&
+  if (!(M <= 64 && (fmt == 0 || fmt == 1 || fmt == 6 || fmt == 7 || fmt == 8 || fmt == 9) && (K % 1024) == 0 &&
+        K >= 2048 &&
         (((uintptr_t)SA | (uintptr_t)SB) & 3) == 0))
     return false;
   const int w = weight_format(fmt);
@@ -595,7 +619,7 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
   // (16-bit C: each launch takes all of K, which decode_ok keeps in range,
   // and launches of fewer rows stream B again)
   const int w = weight_format(fmt);
-  const int64_t wbytes = 128 / op_bytes(w);  // K elements per weight byte
+  const int64_t opb = op_bytes(w);  // weight bytes per 128 K elements
   for (int64_t m0 = 0; m0 < M && err == hipSuccess; m0 += step) {
     int64_t k0 = 0;
     for (int c = 0; c < P && err == hipSuccess; c++) {
@@ -603,7 +627,7 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
       DecArgs a{};
       a.A = (const uint8_t*)A + m0 * K + k0;  // E4M3 activations: one byte per element
       a.SA = SA + m0 * (K / 32) + k0 / 32;
-      a.B = (const uint8_t*)B + k0 / wbytes;
+      a.B = (const uint8_t*)B + k0 / 128 * opb;
       a.SB = SB + k0 / 32;
       a.e = c == P - 1 ? e : Epi{e.C, nullptr, kOutF32, kActNone};
       a.e.C = (uint8_t*)e.C + m0 * N * epi_elem_bytes(e.out);
@@ -617,6 +641,8 @@ hipError_t launch_mx_decode(const void* A, const uint8_t* SA, const void* B, con
       err = w == kFmtFp4     ? launch_dec_k<kFmtFp4>(a, cus, stream, kws)
             : w == kElemInt4 ? launch_dec_k<kElemInt4>(a, cus, stream, kws)
             : w == kElemInt2 ? launch_dec_k<kElemInt2>(a, cus, stream, kws)
+            : w == kFmtFp6   ? launch_dec_k<kFmtFp6>(a, cus, stream, kws)
+            : w == kFmtBf6   ? launch_dec_k<kFmtBf6>(a, cus, stream, kws)
                              : launch_dec_k<kFmtFp8>(a, cus, stream, kws);
       k0 += kc;
     }

@@ -147,12 +147,13 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * K a multiple of 4096) and the split-K kernel, once per 64 rows of A when
  * M > 64.  FP6 weights (MXG_FMT_FP8_FP6 / _BF6) are MFMA operands as stored
  * (the instruction's E2M3 / E3M2 modes: a lane's 32 codes are its 24 bytes of
- * a row), on the split-K kernel for every M (once per 64 rows of A).
- * Decode shapes with E4M3 activations and E4M3 or E2M1 weights take
+ * a row); they take the decode kernel and the split-K kernel, once per 64
+ * rows of A when M > 64.
+ * Decode shapes with E4M3 activations and E4M3, E2M1 or FP6 weights take
  * weight-streaming kernels: for M <= 64 and K a multiple of 1024 from 2048,
  * one that reads B once per launch (fp32 C: all rows per launch, K in chunks
- * of up to 16384 (E2M1 weights) or 12288 (E4M3 weights), fewer as M grows,
- * each chunk adding into C, K up to 131072; 16-bit C through
+ * of up to 16384 (E2M1 weights) or 12288 (E4M3 and FP6 weights), fewer as M
+ * grows, each chunk adding into C, K up to 131072; 16-bit C through
  * mxgemm_run_fused: all of K per launch, K up to 16384 / 12288, one launch per
  * 64, 32 or 16 rows for K <= 4096, <= 8192, above); for other small M
  * (M <= 64) a split-K kernel, which with fp32 C and M <= 16 only adds the

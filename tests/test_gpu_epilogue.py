@@ -115,8 +115,8 @@ def test_epilogue_gelu_against_oracle(out_type):
 # epilogue the 128 x 128 one), the decode kernel (1, 3 row blocks; two
 # K chunks at K = 8192 for 33 rows, 20480 and, with E4M3 weights, 14336,
 # where 16-bit outputs take two row launches or the split-K kernel instead;
-# K = 4608 split between the decode and split-K kernels) and the split-K
-# skinny kernel.
+# K = 4608 split between the decode and split-K kernels; E2M3 / E3M2 weights
+# on the same paths) and the split-K skinny kernel.
 CASES = [("mxfp8_8192", 4096, 4096, 256, 0, 20000), ("mxfp8_2048", 4096, 4352, 256, 2, 20000),
          ("mxfp8_2048", 4096, 4352, 1024, 4, 20000), ("mxfp8_2048", 4096, 4352, 1152, 0, 20000),
          ("mxfp8_2048", 512, 640, 384, 0, None), ("mxfp8_2048", 512, 640, 384, 4, None),
@@ -125,7 +125,9 @@ CASES = [("mxfp8_8192", 4096, 4096, 256, 0, 20000), ("mxfp8_2048", 4096, 4352, 2
          ("decode_16x28672x8192", 48, 1000, 4096, 0, None), ("decode_16x28672x8192", 33, 1001, 8192, 1, None),
          ("decode_16x28672x8192", 40, 512, 1536, 0, None), ("decode_16x28672x8192", 7, 1003, 1536, 1, None),
          ("decode_16x28672x8192", 17, 1001, 20480, 1, None), ("decode_16x28672x8192", 16, 600, 14336, 0, None),
-         ("decode_16x28672x8192", 13, 1001, 4608, 1, None)]
+         ("decode_16x28672x8192", 13, 1001, 4608, 1, None), ("decode_16x28672x8192", 16, 1000, 4096, 8, None),
+         ("decode_16x28672x8192", 33, 1001, 8192, 9, None), ("decode_16x28672x8192", 13, 1001, 4608, 8, None),
+         ("decode_16x28672x8192", 17, 600, 14336, 9, None)]
 
 EPILOGUES = [(True, oracle.ACT_GELU, oracle.OUT_BF16), (True, oracle.ACT_NONE, oracle.OUT_F16),
              (False, oracle.ACT_GELU, oracle.OUT_F32), (True, oracle.ACT_GELU, oracle.OUT_F16)]
@@ -176,7 +178,7 @@ def test_fused_gemm(name, M, N, K, fmt, npts):
     # kernel adds the rest; a 16-bit C takes the split-K kernel for all of K.
     blocks = (M + 15) // 16
     limit = (16 if fmt == 1 else 12) if blocks <= 1 else 8 if blocks <= 2 else 4
-    decode_rows = fmt in (0, 1) and M <= 64
+    decode_rows = fmt in (0, 1, 8, 9) and M <= 64
     chunked = decode_rows and ((K % 1024 == 0 and K >= 2048 and K // 1024 > limit) or
                                (M <= 16 and K % 1024 != 0 and K - K % 1024 >= 2048))
     for use_bias, act, out_type in EPILOGUES:

@@ -4,7 +4,8 @@ scale per 32 K elements) through the C ABI, against the CPU oracle.
 Quantizer: bit-exact, on normal data, on every fp32 mantissa at the
 exponents where FP6 rounding changes regime (subnormal, normal, saturating
 binades), and on special blocks.  GEMM (E4M3 activations x FP6 weights, fed
-to the scaled MFMA's FP6 modes as stored, on the split-K kernel): the strict
+to the scaled MFMA's FP6 modes as stored, on the decode and split-K
+kernels): the strict
 K-term bound per element, NaN positions
 identical; one and several row blocks, more than 64 rows (the split-K kernel
 once per 64 rows), K not a multiple of 128, ragged N, and the decode
@@ -78,9 +79,15 @@ def test_fp6_quantize_every_mantissa(elem):
 
 
 # (M, N, K): one row block (1, 13, 16 rows), two and four, more than 64 rows
-# (several split-K launches), K not a multiple of 128, ragged N
+# (several split-K launches), K not a multiple of 128, ragged N.  With K a
+# multiple of 1024 from 2048 and up to 64 rows the decode kernel takes the
+# product: besides the shapes above, K in several chunks adding into C
+# (16384 for one row block, 12288 with four: 3 chunks), K = 4160 (the
+# decode kernel for 4096, the split-K kernel adds the rest), N = 1 and
+# N < 16 (one ragged fragment)
 FP6_SHAPES = [(1, 300, 2048), (16, 1001, 4096), (13, 250, 8192), (32, 300, 4096), (40, 777, 8192), (64, 500, 4096),
-              (7, 1000, 1536), (33, 250, 96), (5, 28, 32), (64, 129, 256), (65, 300, 512), (200, 130, 1024)]
+              (7, 1000, 1536), (33, 250, 96), (5, 28, 32), (64, 129, 256), (65, 300, 512), (200, 130, 1024),
+              (2, 40, 16384), (64, 520, 12288), (9, 300, 4160), (1, 1, 2048), (3, 13, 3072)]
 
 # measured above the strict K-term bound (one or three 128-element steps of
 # the scaled MFMA, whose alignment term then exceeds K units: up to 6.2 x
