@@ -347,13 +347,16 @@ def test_accumulator_width_on_gpu():
 
 # NaN and infinity propagation on every kernel family: a NaN scale byte in a
 # row of A and a NaN code in a row of B (E4M3 0x7F) make that whole row /
-# column NaN; with E2M1 weights (no NaN code) a NaN scale byte of B does.
-# Shapes: 256 x 256 ping-pong (>= 256 full tiles), 128 x 128 split-K
-# ping-pong, 4-wave tiled (ragged), split-K skinny, decode (one launch, K
-# chunks adding into C, decode + split-K remainder).
+# column NaN; with E2M1, FP6 or integer weights (no NaN code) a NaN scale
+# byte of B does.  Shapes: 256 x 256 ping-pong (>= 256 full tiles), 128 x 128
+# split-K ping-pong, 4-wave tiled (ragged), split-K skinny, decode (one
+# launch, K chunks adding into C, decode + split-K remainder) with E4M3, E2M1,
+# E2M3, E3M2, INT4 and INT2 weights.
 NAN_CASES = [(4096, 4096, 256, 0, 30000), (128, 384, 256, 0, None), (200, 40, 256, 0, None), (8, 40, 256, 0, None),
              (8, 40, 2048, 0, None), (8, 40, 2048, 1, None), (40, 520, 8192, 1, None), (13, 40, 4608, 1, None),
-             (4096, 4096, 256, 2, 30000), (128, 384, 256, 3, None)]
+             (4096, 4096, 256, 2, 30000), (128, 384, 256, 3, None),
+             (8, 40, 2048, 8, None), (13, 40, 4608, 9, None), (40, 520, 16384, 8, None), (8, 40, 2048, 6, None),
+             (8, 40, 4096, 7, None)]
 
 
 @pytest.mark.parametrize("M,N,K,fmt,npts", NAN_CASES)
@@ -365,8 +368,8 @@ def test_nan_propagation(M, N, K, fmt, npts):
     qb, sb = gpu_quantize(b32, eb)
     ia, jb, jc = 3, 7, N - 1
     sa[ia, (K // 32) // 2] = 255            # NaN scale in A row 3
-    if eb == oracle.E2M1:
-        sb[jb, 1] = 255                     # NaN scale in B row 7 (E2M1 has no NaN code)
+    if eb in (oracle.E2M1, oracle.E2M3, oracle.E3M2, oracle.INT4, oracle.INT2):
+        sb[jb, 1] = 255                     # NaN scale in B row 7 (these elements have no NaN code)
     else:
         qb[jb, K // 2 + 1] = 0x7F           # NaN code in B row 7 (E4M3 / E5M2 alike)
     sb[jc, K // 32 - 1] = 255               # NaN scale in the last row of B (ragged edge)
