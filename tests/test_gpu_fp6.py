@@ -5,11 +5,10 @@ Quantizer: bit-exact, on normal data, on every fp32 mantissa at the
 exponents where FP6 rounding changes regime (subnormal, normal, saturating
 binades), and on special blocks.  GEMM (E4M3 activations x FP6 weights, fed
 to the scaled MFMA's FP6 modes as stored, on the decode and split-K
-kernels): the strict
-K-term bound per element, NaN positions
-identical; one and several row blocks, more than 64 rows (the split-K kernel
-once per 64 rows), K not a multiple of 128, ragged N, and the decode
-workload at full size.  Outputs start as NaN canaries and LDS is poisoned
+kernels): the strict K-term bound per element, NaN positions identical; one
+and several row blocks, more than 64 rows (the split-K kernel once per 64
+rows), K not a multiple of 128 or of 1024 (decode plus split-K remainder),
+K in chunks above 12288, ragged N, and the decode workload at full size.  Outputs start as NaN canaries and LDS is poisoned
 before every GEMM.
 """
 import numpy as np
