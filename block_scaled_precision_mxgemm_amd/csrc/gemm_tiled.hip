@@ -438,6 +438,8 @@ using MxMid44 = MxMid<kFmtFp4, kFmtFp4>;
 using F16Big = Cfg<kF16, 256, 256, 2, 2, kFmtFp8, kFmtFp8, false>;
 using F16Mid = Cfg<kF16, 128, 128, 2, 2, kFmtFp8, kFmtFp8, false>;
 using F16MidKN = Cfg<kF16, 128, 128, 2, 2, kFmtFp8, kFmtFp8, true>;
+// K x N right operand with fewer 128 x 128 tiles than CUs: 64 x 64 tiles
+using F16SmallKN = Cfg<kF16, 64, 64, 2, 2, kFmtFp8, kFmtFp8, true>;
 using DeqMid = Cfg<kDEQ, 128, 128, 2, 2, kFmtFp8, kFmtFp8, false>;
 
 template <int FA, int FB>
@@ -482,6 +484,11 @@ hipError_t launch_f16_tiled(const uint16_t* A, const uint16_t* B, float* C, int6
   a.lda = K * 2;
   if (!b_is_nk) {
     a.ldb = N * 2;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    if (((M + 127) / 128) * ((N + 127) / 128) < cus) return launch<F16SmallKN, 2>(a, stream);
     return launch<F16MidKN, 2>(a, stream);
   }
   a.ldb = K * 2;

@@ -476,6 +476,17 @@ def test_fp16_gemm_ragged(b_is_nk, M, N, K):
     assert r["ok"], r
 
 
+def test_fp16_gemm_kn_mid_tiles():
+    """K x N right operand with as many 128 x 128 tiles as a full chip (the
+    128 x 128 K x N kernel; fewer tiles take 64 x 64 ones); sampled."""
+    say("fp16 kn 128-tiles")
+    w = mxin.WORKLOADS["fp16_1024"]
+    a16, b16 = mxin.fp16_sources(w, False, 2048, 2048 - 8, 200, seed=5)
+    pts = mxin.sample_points(2048, 2048 - 8, 20000)
+    r = _fp16_case(a16, b16, False, points=pts)
+    assert r["ok"], r
+
+
 def test_fp16_gemm_large_tiles_nk():
     say("fp16 large tiles")
     w = mxin.WORKLOADS["mxfp8_2048"]
