@@ -60,7 +60,12 @@ constexpr int kStageBytes = 16 * kBand;       // one stage: 16 rows
 // are not written), so a stage keeps the 128-byte rows of the other formats
 // with 12-byte pieces in 16-byte slots, swizzled the same way
 constexpr bool is_fp6(int w) { return w == kFmtFp6 || w == kFmtBf6; }
-constexpr int band_bytes(int w) { return is_fp6(w) ? 96 : kBand; }  // global bytes of a row per stage
+// FP6 weights with K / 1024 a multiple of 4 instead stream whole 128-byte
+// lines per row and stage (16-byte copies, as for the other formats): a
+// wave's band is then 3 K / 4096 stages holding 4 operands per 3 stages, and
+// an operand may begin in the stage before the one that completes it
+constexpr bool fp6_line(int w, int kw) { return is_fp6(w) && kw % 4 == 0; }
+constexpr int band_bytes(int w, int kw) { return is_fp6(w) && !fp6_line(w, kw) ? 96 : kBand; }  // global bytes of a row per stage
 // Reduced output blocks (16 x 16) a wave keeps in registers until its
 // copies are done.  A store issued inside the stream would sit among the copies in the
 // in-order vector-memory counter and make the next stage waits of that wave
@@ -96,6 +101,10 @@ constexpr int op_bytes(int w) { return w == kFmtFp8 ? 128 : is_fp6(w) ? 96 : w =
 constexpr int mfma_fmt(int w) {
   return is_fp6(w) ? w : (w == kFmtFp8 || w == kElemInt4) ? kFmtFp8 : kFmtFp4;
 }
+// stages per fragment of a wave with wk MFMAs
+constexpr int stages_per_frag(int w, int wk) {
+  return fp6_line(w, wk) ? 3 * wk / 4 : wk / (band_bytes(w, wk) / op_bytes(w));
+}
 
 // K / 1024 = KW MFMAs (128 k each) per wave per fragment on average.  With
 // two MFMA operands per 128-byte stage (E2M1, INT4) and KW odd, waves 0-3
@@ -105,7 +114,7 @@ constexpr bool split_k(int w, int kw) { return op_bytes(w) == 64 && kw % 2 == 1;
 
 // LDS of one wave's ring and scale slots for WK MFMAs per fragment
 constexpr int ring_bytes(int w, int wk, int d) {
-  const int nq = wk / (band_bytes(w) / op_bytes(w));
+  const int nq = stages_per_frag(w, wk);
   const int nsi = (16 * wk + 63) / 64;
   const int nsl = (nq - 1 + d + nq - 1) / nq;
   return d * kStageBytes + nsl * nsi * 256;
@@ -120,10 +129,20 @@ struct Decode {
   static constexpr int D = D_;
   static constexpr int WK = KW + XK;                     // MFMAs per fragment of this wave
   static constexpr int OPB = op_bytes(W);                // bytes of a weight row per MFMA
-  static constexpr int BAND = band_bytes(W);             // global bytes of a weight row per stage
+  static constexpr bool LINE = fp6_line(W, WK);          // FP6 operands across 128-byte line stages
+  static constexpr int BAND = band_bytes(W, WK);         // global bytes of a weight row per stage
   static constexpr int STAGE = kStageBytes;              // one stage in LDS: 16 rows of 128 bytes
-  static constexpr int MPS = BAND / OPB;                 // MFMAs per stage
-  static constexpr int NQ = WK / MPS;                    // stages per fragment
+  static constexpr int MPS = LINE ? 1 : BAND / OPB;      // MFMAs per stage (accumulators)
+  static constexpr int NQ = stages_per_frag(W, WK);      // stages per fragment
+  static constexpr int CPB = is_fp6(W) && !LINE ? 12 : 16;  // bytes per lane of a weight copy
+  // stages between a copy's issue and the stage that reads it: D - 1, and
+  // D - 2 with line stages, whose straddling operands still read the
+  // previous stage (the buffer then refilled is two stages old)
+  static constexpr int AHEAD = LINE ? D - 2 : D - 1;
+  // MFMAs whose operands complete in stage q: ops_count(q) of them from
+  // ops_first(q) (line stages: operand u ends at byte 96 u + 95 of the band)
+  static constexpr int ops_first(int q) { return LINE ? 128 * q / 96 : q * MPS; }
+  static constexpr int ops_count(int q) { return LINE ? (128 * q + 32) / 96 + 1 - ops_first(q) : MPS; }
   static constexpr int kBFmt = mfma_fmt(W);              // MFMA format of the weight operand
   static constexpr int SBW = 4 * WK;                     // scale bytes of a row per wave
   static constexpr int LPR = SBW / 4;                    // scale copy lanes per row (4 bytes each)
@@ -144,7 +163,8 @@ struct Decode {
   // the stage waits never count them (the compiler may merge the small ones).
   static constexpr int NS16 = SBW / 16, NS8 = (SBW % 16) / 8, NS4 = (SBW % 8) / 4;
   static constexpr bool FITS = LDS <= 160 * 1024;  // the 160 KiB LDS of a gfx950 CU
-  static_assert(NQ >= 1 && WK % MPS == 0 && (D & (D - 1)) == 0, "whole stages per fragment");
+  static_assert(NQ >= 1 && (LINE ? WK % 4 == 0 && AHEAD >= 2 : WK % MPS == 0) && (D & (D - 1)) == 0,
+                "whole stages per fragment");
   static_assert(ring_bytes(W, WK, D) == D * STAGE + NSL * SZ_SC && SZ_WAVE >= ring_bytes(W, WK, D),
                 "region layout");
   static_assert(NSL * NQ >= NQ - 1 + D, "scale slot reuse");
@@ -209,16 +229,16 @@ struct Decode {
     v4f held[kHeld];      // reduced blocks u = w, w + 8, ... (u = MB f + mb), stored at the end
   };
 
-  // Vector-memory instructions of the A loads that one stage of the first
+  // Vector-memory instructions of the A loads that stage q of the first
   // fragment needs (lo and hi halves per MFMA), and those of stages q .. NQ-1.
-  static constexpr int la() { return MB * 2 * MPS; }
-  static constexpr int la_from(int q) { return q >= NQ ? 0 : la() + la_from(q + 1); }
+  static constexpr int la(int q) { return MB * 2 * ops_count(q); }
+  static constexpr int la_from(int q) { return q >= NQ ? 0 : la(q) + la_from(q + 1); }
   // Copies issued after stage s's copies and before its wait: the copies of
-  // stages s+1 .. s+D-2 (2 weight copies each, plus the scale copies at every
-  // fragment start) and, in the first fragment, the A loads of stages
+  // stages s+1 .. s+AHEAD-1 (2 weight copies each, plus the scale copies at
+  // every fragment start) and, in the first fragment, the A loads of stages
   // q .. NQ-1 issued by the prologue after stage q's copies.
   static constexpr int younger(int q, bool first) {
-    return 2 * (D - 2) + NSI * ((q + D - 2) / NQ) + (first && q <= D - 2 ? la_from(q) : 0);
+    return 2 * (AHEAD - 1) + NSI * ((q + AHEAD - 1) / NQ) + (first && q <= AHEAD - 1 ? la_from(q) : 0);
   }
 
   template <int N>
@@ -267,13 +287,13 @@ struct Decode {
     const uint32_t soff = (uint32_t)(t.kb * OPB + qv * BAND);
 #pragma unroll
     for (int h = 0; h < 2; h++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), is_fp6(W) ? 12 : 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(st + h * 8 * kBand), CPB,
                                                (uint32_t)min(t.brow + 8 * h, last) * t.rb + t.bch[h], soff, 0,
                                                kStreamPolicy);
   }
 
-  // A operands for stage q of this wave (rows clamped to M-1; rows >= M are
-  // computed and discarded): wave MFMA j = q * MPS + u covers k 128 (kb + j)
+  // A operands of the MFMAs of stage q of this wave (rows clamped to M-1;
+  // rows >= M are computed and discarded): wave MFMA j covers k 128 (kb + j)
   // .. +127.
   template <int Q>
   static __device__ __forceinline__ void load_a(State& t) {
@@ -283,7 +303,8 @@ struct Decode {
       const int m = min(16 * mb + t.r, a.M - 1);
       const uint8_t* row = a.A + (int64_t)m * a.ldk + (int64_t)t.kb * 128;
 #pragma unroll
-      for (int u = 0; u < MPS; u++) t.av[mb][Q * MPS + u] = load_fp8_op(row + (Q * MPS + u) * 128, t.g);
+      for (int u = 0; u < ops_count(Q); u++)
+        t.av[mb][ops_first(Q) + u] = load_fp8_op(row + (ops_first(Q) + u) * 128, t.g);
     }
   }
 
@@ -312,7 +333,7 @@ struct Decode {
   }
 
   // Prologue, in this issue order: the A scales, then stage p's copies and
-  // A(p), for p = 0 ..; stages up to D - 2, A up to NQ - 1.
+  // A(p), for p = 0 ..; stages up to AHEAD - 1, A up to NQ - 1.
   template <int... P>
   static __device__ __forceinline__ void prologue(State& t, std::integer_sequence<int, P...>) {
     // an assembly comment naming the counted loads, for the static check of
@@ -322,7 +343,7 @@ struct Decode {
     order_fence();
     (
         [&] {
-          if constexpr (P <= D - 2) issue(t, P / NQ, P % NQ, true);
+          if constexpr (P <= AHEAD - 1) issue(t, P / NQ, P % NQ, true);
           order_fence();
           if constexpr (P < NQ) load_a<P>(t);
           order_fence();
@@ -339,19 +360,19 @@ struct Decode {
     // the wait stricter).  Past the first fragment, when a younger stage lies
     // beyond the last one its copies were skipped, and the stage waits for
     // everything instead.
-    if (FIRST || (f * NQ + Q) + D - 2 < t.nf * NQ)
+    if (FIRST || (f * NQ + Q) + AHEAD - 1 < t.nf * NQ)
       wait_stage<younger(Q, FIRST)>();
     else
       wait_stage<0>();
-    // stage s + D - 1, into the buffer read at stage s - 1
-    issue(t, f + (Q + D - 1) / NQ, (Q + D - 1) % NQ, FIRST);
+    // stage s + AHEAD, into the buffer read last at stage s - 1
+    issue(t, f + (Q + AHEAD) / NQ, (Q + AHEAD) % NQ, FIRST);
     const uint8_t* st = t.wsm + ((f * NQ + Q) & (D - 1)) * STAGE;
     const uint8_t* sc = t.wsm + D * STAGE + (f % NSL) * SZ_SC;
     const int g = t.g, r = t.r;
     const int sw = (r >> 1) & 7;
 #pragma unroll
-    for (int u = 0; u < MPS; u++) {
-      const int j = Q * MPS + u;  // this wave's MFMA index inside the fragment
+    for (int u = 0; u < ops_count(Q); u++) {
+      const int j = ops_first(Q) + u;  // this wave's MFMA index inside the fragment
       v8i bv;
       if constexpr (W == kFmtFp4) {
         // lane group g: k 32g .. 32g+31 of operand u (16 bytes)
@@ -362,6 +383,23 @@ struct Decode {
         const v4i lo = *reinterpret_cast<const v4i*>(st + r * kBand + ((g ^ sw) << 4));
         const v4i hi = *reinterpret_cast<const v4i*>(st + r * kBand + (((4 + g) ^ sw) << 4));
         bv = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else if constexpr (LINE) {
+        // lane group g: k 32g .. 32g+31, the 24 bytes at 96 j + 24 g of this
+        // wave's band of the row, as three 8-byte pieces; a piece before
+        // byte 128 Q lies in the previous stage (at most one stage back: an
+        // operand is 96 bytes)
+        int w6[6];
+#pragma unroll
+        for (int i = 0; i < 3; i++) {
+          const int p = 96 * j + 24 * g + 8 * i - 128 * Q;  // -128 < p < 128
+          const int back = p < 0 ? 1 : 0;
+          const int o = p + 128 * back;
+          const uint8_t* sb_ = t.wsm + ((f * NQ + Q - back) & (D - 1)) * STAGE;
+          const v2i c = *reinterpret_cast<const v2i*>(sb_ + r * kBand + (((o >> 4) ^ sw) << 4) + (o & 8));
+          w6[2 * i] = c[0];
+          w6[2 * i + 1] = c[1];
+        }
+        bv = v8i{w6[0], w6[1], w6[2], w6[3], w6[4], w6[5], 0, 0};
       } else if constexpr (is_fp6(W)) {
         // lane group g: k 32g .. 32g+31, the 24 bytes at 24g of the row's
         // operand = pieces 2g and 2g + 1 (12 bytes each, in swizzled
@@ -394,8 +432,8 @@ struct Decode {
       const int sb = sc[r * SBW + 4 * j + g];
 #pragma unroll
       for (int mb = 0; mb < MB; mb++)
-        t.acc[mb][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bv, t.av[mb][j], t.acc[mb][u], kBFmt, kFmtFp8, 0, sb, 0,
+        t.acc[mb][LINE ? 0 : u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bv, t.av[mb][j], t.acc[mb][LINE ? 0 : u], kBFmt, kFmtFp8, 0, sb, 0,
             (int)__builtin_amdgcn_ubfe(t.sa[mb][j], 8 * g, 8));
     }
   }
@@ -460,7 +498,7 @@ struct Decode {
     t.brow = t.lane >> 3;
 #pragma unroll
     for (int h = 0; h < 2; h++)
-      t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * (is_fp6(W) ? 12 : 16));
+      t.bch[h] = (uint32_t)(((t.lane & 7) ^ (((t.brow + 8 * h) >> 1) & 7)) * CPB);
     // scale copy i, lane l: entry e = 64 i + l is row e / LPR, dword e % LPR
     // (entries past row 15 repeat row 15 into the slot's unused tail)
 #pragma unroll
@@ -470,7 +508,7 @@ struct Decode {
       t.scol[i] = (uint32_t)(4 * (e % LPR));
     }
 
-    prologue(t, std::make_integer_sequence<int, (D - 1 > NQ ? D - 1 : NQ)>{});
+    prologue(t, std::make_integer_sequence<int, (AHEAD > NQ ? AHEAD : NQ)>{});
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
