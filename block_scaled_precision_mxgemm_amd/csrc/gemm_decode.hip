@@ -1,8 +1,9 @@
 // gemm_decode.hip - MX GEMM for decode shapes with few activation rows (M <= 64)
 // against a large weight matrix B (N x K: E4M3, E2M1, E2M3, E3M2, INT4 or INT2
 // elements with UE8M0 block scales; K a multiple of 1024 from 2048; one
-// launch takes up to 12288 of it with 8- and 6-bit weights and 16384 with
-// 4-bit ones, longer K runs in chunks that add into an fp32 C).  The
+// launch takes up to 12288 of it with 8- and 6-bit weights, 14336 with INT4
+// and 16384 with E2M1 and INT2 ones, longer K runs in chunks that add into an
+// fp32 C).  The
 // product is bound by the bytes of B, which must stream from HBM exactly
 // once; the weight plane is what quantization shrinks ("Metal tensors で
 // カスタム機械学習オペレーションを最適化する", section "主要内容": inference
