@@ -97,8 +97,11 @@ __device__ __forceinline__ uint32_t lookup16(uint32_t idx, uint32_t t0, uint32_t
   const uint32_t lo3 = idx & 0x07070707u;
   const uint32_t a = __builtin_amdgcn_perm(t1, t0, lo3);
   const uint32_t b = __builtin_amdgcn_perm(t3, t2, lo3);
-  const uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;  // 0xFF in the bytes whose index is >= 8
-  return (b & m) | (a & ~m);
+  // byte i of the result: byte i of a (selector i) or, where the index is
+  // >= 8, byte i of b (selector i + 4); a third permute instead of a byte
+  // mask, whose multiply by 0xFF would be a quarter-rate integer multiply
+  const uint32_t sel = ((idx >> 1) & 0x04040404u) | 0x03020100u;
+  return __builtin_amdgcn_perm(b, a, sel);
 }
 
 // Eight INT4 codes (element i in bits 4i .. 4i+3) -> the E4M3 codes of
