@@ -47,6 +47,8 @@ constexpr int kDecWaves = 8;
 // per CU) keep HBM as busy as 7 do, and the shallower first burst of copies
 // brings each wave's first stage back sooner (16 x 28672 x 8192: 24.3 us at
 // depth 4 against 25.7 us at depth 8; fp8 weights 39.7 against 39.4 us).
+// Operands of 64 bytes or less and FP6 line stages keep 2 stages in flight
+// in this ring (Decode::AHEAD).
 constexpr int kDecStages = 4;
 // Ring depth when every workgroup owns at most one fragment (N <= 16 x CUs):
 // a wave's whole stream is then a few stages, all of which can be in flight
