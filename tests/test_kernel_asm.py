@@ -108,17 +108,23 @@ def test_kernel_source_is_hazard_free(src):
 def test_decode_kernel_first_wait_counts_the_issued_loads():
     """The decode kernel's stage waits count the vector-memory instructions
     issued after a stage's copies; in the first fragment these include the
-    A operand loads of the prologue, 2 WK per row block (the lo and hi
-    halves of each of the wave's WK MFMA operands).  The A scales are loaded
-    before the first copy, so that however the compiler merges those loads
-    they are never among the counted ones.  Between the first copy and the
-    first wait the compiler must issue exactly the counted global loads, or
-    the wait lets a stage's copies still be in flight.  With two weight
-    operands per stage (E2M1, INT4) and K / 1024 odd the kernel has two wave
-    kinds (WK = KW + 1 for waves 0-3, KW - 1 for waves 4-7) behind one branch
-    on the wave index; the prologue of each kind starts at an assembly
-    comment that names WK and MB.  Every weight format (E4M3, E2M1, INT4,
-    INT2, E2M3, E3M2) is checked."""
+    A operand loads (2 per row block and MFMA: the lo and hi halves of the
+    operand), each stage's issued right after that stage's copies, so the
+    prologue issues those of the stages it copies: the MFMAs whose operands
+    complete in the first AHEAD stages, AHEAD = D - 2 for operands of 64
+    bytes or less in a 4-stage ring and for FP6 line stages (K / 1024 a
+    multiple of 4: 4 operands of 96 bytes per 3 stages of 128), else D - 1.
+    The A scales are loaded before the first copy, so that however the
+    compiler merges those loads they are never among the counted ones.
+    Between the first copy and the first wait the compiler must issue
+    exactly the counted global loads, or the wait lets a stage's copies
+    still be in flight.  With two weight operands per stage (E2M1, INT4)
+    and K / 1024 odd the kernel has two wave kinds (WK = KW + 1 for waves
+    0-3, KW - 1 for waves 4-7) behind one branch on the wave index; the
+    prologue of each kind starts at an assembly comment that names WK, MB
+    and the count it issues, which must also be the count the rule above
+    gives.  Every weight format (E4M3, E2M1, INT4, INT2, E2M3, E3M2) is
+    checked."""
     import re
     from block_scaled_precision_mxgemm_amd import build as B
     asm = H.compile_to_asm(os.path.join(ROOT, "block_scaled_precision_mxgemm_amd", "csrc", "gemm_decode.hip"),
@@ -126,24 +132,37 @@ def test_decode_kernel_first_wait_counts_the_issued_loads():
 
     seen = split = 0
     formats = set()
+    op_bytes = {0: 128, 4: 64, 8: 64, 9: 32, 2: 96, 3: 96}   # E4M3, E2M1, INT4, INT2, E2M3, E3M2
+
+    def prologue_a_loads(w, wk, mb, d):
+        fp6_line = w in (2, 3) and wk % 4 == 0
+        ahead = d - 2 if (fp6_line or (op_bytes[w] <= 64 and d == 4)) else d - 1
+        if fp6_line:   # operand u completes in stage (96 u + 95) // 128
+            ops = sum(1 for u in range(wk) if (96 * u + 95) // 128 < ahead)
+        else:          # 128-byte stages of whole operands (96-byte stages for other FP6)
+            per_stage = max(1, 128 // op_bytes[w]) if w not in (2, 3) else 1
+            ops = min(wk, ahead * per_stage)
+        return 2 * mb * ops
+
     for m in re.finditer(r"^(_ZN3mxg12_GLOBAL__N_113decode_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEEv\S*):", asm,
                          re.M):
-        name, w, kw, mb = m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4))
+        name, w, kw, mb, d = m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4)), int(m.group(5))
         formats.add(w)
         two_per_stage = w in (4, 8)   # E2M1, INT4: 64-byte operands
         body = asm[m.end():asm.index(".Lfunc_end", m.end())]
         # the prologue of each wave kind starts at its marker comment
         wks = []
-        for p in re.finditer(r"; decode prologue wk=(\d+) mb=(\d+)", body):
-            wk = int(p.group(1))
+        for p in re.finditer(r"; decode prologue wk=(\d+) mb=(\d+) la=(\d+)", body):
+            wk, la = int(p.group(1)), int(p.group(3))
             assert int(p.group(2)) == mb, name
+            assert la == prologue_a_loads(w, wk, mb, d), (name, wk, la, prologue_a_loads(w, wk, mb, d))
             part = body[p.end():]
             first_wait = re.search(r"s_waitcnt vmcnt\(", part)
             first_copy = re.search(r"^\s*buffer_load_dwordx[34] .* lds", part, re.M)
             assert first_wait and first_copy and first_copy.start() < first_wait.start(), name
             assert re.search(r"^\s*global_load_\w+", part[:first_copy.start()], re.M), name   # the A scales
             loads = re.findall(r"^\s*global_load_\w+", part[first_copy.start():first_wait.start()], re.M)
-            assert len(loads) == mb * 2 * wk, (name, wk, len(loads), mb * 2 * wk)
+            assert len(loads) == la, (name, wk, len(loads), la)
             wks.append(wk)
         if two_per_stage and kw % 2 == 1:
             assert sorted(set(wks)) == [kw - 1, kw + 1], (name, wks)
