@@ -86,7 +86,10 @@ def test_fp6_quantize_every_mantissa(elem):
 # N < 16 (one ragged fragment)
 FP6_SHAPES = [(1, 300, 2048), (16, 1001, 4096), (13, 250, 8192), (32, 300, 4096), (40, 777, 8192), (64, 500, 4096),
               (7, 1000, 1536), (33, 250, 96), (5, 28, 32), (64, 129, 256), (65, 300, 512), (200, 130, 1024),
-              (2, 40, 16384), (64, 520, 12288), (9, 300, 4160), (1, 1, 2048), (3, 13, 3072)]
+              (2, 40, 16384), (64, 520, 12288), (9, 300, 4160), (1, 1, 2048), (3, 13, 3072),
+              # decode line stages: K / 1024 = 12 in one launch with the 4-stage
+              # ring (more fragments than CUs) and the 8-stage one, and 4
+              (5, 4500, 12288), (3, 1000, 12288), (8, 4200, 4096)]
 
 # measured above the strict K-term bound (one or three 128-element steps of
 # the scaled MFMA, whose alignment term then exceeds K units: up to 6.2 x
