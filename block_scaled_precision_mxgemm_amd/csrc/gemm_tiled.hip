@@ -39,6 +39,9 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int FA = FA_, FB = FB_;
   static constexpr bool AF4 = FA == kFmtFp4, BF4 = FB == kFmtFp4, BKN = BKN_;
+  // FP6 (E2M3 / E3M2) right operand: 96 bytes per row and 128-k slice,
+  // copied 12 bytes per lane into the 16-byte slots of 128-byte LDS rows
+  static constexpr bool B6 = FB == kFmtFp6 || FB == kFmtBf6;
   static constexpr bool SCALED = (KIND != kF16);
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
   static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
@@ -58,6 +61,7 @@ struct Cfg {
   static_assert(NQA % NW == 0 && NQB % NW == 0, "tile copies split evenly over the waves");
   static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
+  static_assert(!B6 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "FP6 weights: E4M3 x FP6 on 128 x 128 tiles");
 };
 
 struct Args {
@@ -96,6 +100,29 @@ struct Kernel {
       // zeroed before use
       const int cc = (col_byte + c * 16 + 16 <= ld) ? c : 0;
       copy16_to_lds(g + (int64_t)grow * ld + col_byte + cc * 16, lds + q * 1024);
+    }
+  }
+  // FP6 rows (K a multiple of 128, so every slice is whole): piece p (12
+  // bytes, k 16 p .. 16 p + 15 of the slice) of row r lands in the 16-byte
+  // slot p ^ swz8(r) of the 128-byte LDS row (a 12-byte copy writes lane l at
+  // 16 l; the slot's last 4 bytes stay unwritten)
+  template <int NQ>
+  static __device__ __forceinline__ void issue_rows6(const uint8_t* __restrict__ g, int64_t ld, int row0,
+                                                     int rows_valid, int64_t col_byte, uint8_t* lds, int wave,
+                                                     int lane) {
+    constexpr int kRsrcWord3 = 0x00020000;
+    const int nrows = min(rows_valid - row0, 128);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)row0 * ld), 0, (int)(nrows * ld),
+                                                      kRsrcWord3);
+#pragma unroll
+    for (int t = 0; t < NQ / T::NW; t++) {
+      const int q = wave + T::NW * t;
+      const int o = q * 1024 + lane * 16;
+      const int row = o / 128;
+      const int c = ((o % 128) >> 4) ^ swz8(row);
+      const int grow = min(row, nrows - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + q * 1024), 12,
+                                               (uint32_t)((int64_t)grow * ld + col_byte + c * 12), 0, 0, 0);
     }
   }
   // In a partial last slice, chunks past K were copied from in-bounds but
@@ -204,6 +231,22 @@ struct Kernel {
     return f;
   }
 
+  // FP6 operand of row `row`: lane group g holds k 32 g .. 32 g + 31, the
+  // pieces 2 g and 2 g + 1 (12 bytes each)
+  static __device__ __forceinline__ v8i read_frag6(const uint8_t* lds, int row, int g) {
+    const int s = swz8(row);
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + row * 128 + (((2 * g) ^ s) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + row * 128 + (((2 * g + 1) ^ s) << 4));
+    return v8i{lo[0], lo[1], lo[2], hi[0], hi[1], hi[2], 0, 0};
+  }
+  template <bool SIX>
+  static __device__ __forceinline__ v8i read_b(const uint8_t* lds, int row, int g) {
+    if constexpr (SIX)
+      return read_frag6(lds, row, g);
+    else
+      return read_frag<T::RB>(lds, row, g);
+  }
+
   // E4M3 byte pair -> two fp16 values times 2^(scale-127), rounded to fp16.
   static __device__ __forceinline__ uint32_t deq_pair(uint32_t two, uint32_t sbyte) {
     uint32_t out = 0;
@@ -266,6 +309,8 @@ struct Kernel {
       issue_rows<T::RA, T::NQA>(a.A, a.lda, m0, a.M, (int64_t)step * T::RA, base, wave, lane);
       if (T::BKN)
         load_kn(a, n0, step, tid, kn);
+      else if constexpr (T::B6)
+        issue_rows6<T::NQB>(a.B, a.ldb, n0, a.N, (int64_t)step * 96, base + T::SZA, wave, lane);
       else
         issue_rows<T::RB, T::NQB>(a.B, a.ldb, n0, a.N, (int64_t)step * T::RB, base + T::SZA, wave, lane);
       if (T::SCALED) {
@@ -277,7 +322,7 @@ struct Kernel {
       uint8_t* base = stage_ptr(st);
       if (step == a.nsteps - 1) {
         if (a.tail_a < T::RA) zero_tail<T::RA, T::NQA>(a.tail_a, base, wave, lane);
-        if (!T::BKN && a.tail_b < T::RB) zero_tail<T::RB, T::NQB>(a.tail_b, base + T::SZA, wave, lane);
+        if (!T::BKN && !T::B6 && a.tail_b < T::RB) zero_tail<T::RB, T::NQB>(a.tail_b, base + T::SZA, wave, lane);
       }
       if (T::BKN) commit_kn(kn, base + T::SZA, tid);
       if (T::SCALED) {
@@ -316,7 +361,7 @@ struct Kernel {
           af[i] = read_frag<T::RA>(la, row, g);
           sa[i] = lsa8[row * 4 + g];
         }
-        v8i bcur = read_frag<T::RB>(lb, wj * T::TN + r, g);
+        v8i bcur = read_b<T::B6>(lb, wj * T::TN + r, g);
         int sbcur = lsb8[(wj * T::TN + r) * 4 + g];
 #pragma unroll
         for (int j = 0; j < T::FN; j++) {
@@ -324,7 +369,7 @@ struct Kernel {
           int sbnext = sbcur;
           if (j + 1 < T::FN) {
             const int row = wj * T::TN + (j + 1) * 16 + r;
-            bnext = read_frag<T::RB>(lb, row, g);
+            bnext = read_b<T::B6>(lb, row, g);
             sbnext = lsb8[row * 4 + g];
           }
 #pragma unroll
@@ -457,10 +502,13 @@ bool use_big_tiles(int64_t M, int64_t N) {
 hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
   Args a = make_args(A, SA, B, SB, e, M, N, K);
-  const bool af4 = (fmt == 2), bf4 = (fmt == 1 || fmt == 2);
+  const bool af4 = (fmt == 2), bf4 = (fmt == 1 || fmt == 2), bf6 = (fmt == 8 || fmt == 9);
   a.lda = af4 ? K / 2 : K;
-  a.ldb = bf4 ? K / 2 : K;
+  a.ldb = bf4 ? K / 2 : bf6 ? K / 4 * 3 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
+  // E4M3 x FP6 (K a multiple of 128, checked by the caller): 128 x 128 tiles
+  if (fmt == 8) return launch<MxMid<kFmtFp8, kFmtFp6>, 2>(a, stream);
+  if (fmt == 9) return launch<MxMid<kFmtFp8, kFmtBf6>, 2>(a, stream);
   // the 256 x 256 tiled kernels store plain fp32 only (MxBig*::EPI_GENERAL)
   const bool big_pp = use_big_tiles(M, N);
   if (big_pp && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, e, M, N, K, fmt, stream);

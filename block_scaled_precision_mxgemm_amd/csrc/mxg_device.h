@@ -23,6 +23,7 @@ namespace mxg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));  // an FP6 MFMA operand (6 registers)
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -152,6 +153,13 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& c, const v8i& a, const v8i&
   if constexpr (FA == kFmtFp8 && FB == kFmtFp8) {
     asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
         : "+a"(c) : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+  } else if constexpr ((FA == kFmtFp6 || FA == kFmtBf6) && FB == kFmtFp8) {
+    // an FP6 first operand takes 6 registers (32 six-bit codes per lane);
+    // the compiler gathers them with VALU moves just before this MFMA and
+    // inserts no wait states for an inline MFMA's operands: the s_nop does
+    const v6i a6 = {a[0], a[1], a[2], a[3], a[4], a[5]};
+    asm("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:%5"
+        : "+a"(c) : "v"(a6), "v"(b), "v"(scale_a), "v"(scale_b), "i"(FA));
   } else if constexpr (FA != kFmtFp4 && FB != kFmtFp4) {
     // 8-register operands with an E5M2 side: the format ids go in cbsz / blgp
     asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:%5 blgp:%6"

@@ -147,8 +147,9 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * K a multiple of 4096) and the split-K kernel, once per 64 rows of A when
  * M > 64.  FP6 weights (MXG_FMT_FP8_FP6 / _BF6) are MFMA operands as stored
  * (the instruction's E2M3 / E3M2 modes: a lane's 32 codes are its 24 bytes of
- * a row); they take the decode kernel and the split-K kernel, once per 64
- * rows of A when M > 64.
+ * a row); they take the decode kernel and the split-K kernel, and with
+ * M > 64 the 4-wave tiled kernel when K % 128 == 0, else the split-K kernel
+ * once per 64 rows of A.
  * Decode shapes with E4M3 activations and E4M3, E2M1 or FP6 weights take
  * weight-streaming kernels: for M <= 64 and K a multiple of 1024 from 2048,
  * one that reads B once per launch (fp32 C: all rows per launch, K in chunks

@@ -4,12 +4,13 @@ scale per 32 K elements) through the C ABI, against the CPU oracle.
 Quantizer: bit-exact, on normal data, on every fp32 mantissa at the
 exponents where FP6 rounding changes regime (subnormal, normal, saturating
 binades), and on special blocks.  GEMM (E4M3 activations x FP6 weights, fed
-to the scaled MFMA's FP6 modes as stored, on the decode and split-K
+to the scaled MFMA's FP6 modes as stored, on the decode, split-K and tiled
 kernels): the strict K-term bound per element, NaN positions identical; one
-and several row blocks, more than 64 rows (the split-K kernel once per 64
-rows), K not a multiple of 128 or of 1024 (decode plus split-K remainder),
-K in chunks above 12288, ragged N, and the decode workload at full size.  Outputs start as NaN canaries and LDS is poisoned
-before every GEMM.
+and several row blocks, more than 64 rows (the tiled kernel when K is a
+multiple of 128, else the split-K kernel once per 64 rows), K not a multiple
+of 128 or of 1024 (decode plus split-K remainder), K in chunks above 12288,
+ragged N, and the decode workload at full size.  Outputs start as NaN
+canaries and LDS is poisoned before every GEMM.
 """
 import numpy as np
 import pytest
@@ -89,7 +90,10 @@ FP6_SHAPES = [(1, 300, 2048), (16, 1001, 4096), (13, 250, 8192), (32, 300, 4096)
               (2, 40, 16384), (64, 520, 12288), (9, 300, 4160), (1, 1, 2048), (3, 13, 3072),
               # decode line stages: K / 1024 = 12 in one launch with the 4-stage
               # ring (more fragments than CUs) and the 8-stage one, and 4
-              (5, 4500, 12288), (3, 1000, 12288), (8, 4200, 4096)]
+              (5, 4500, 12288), (3, 1000, 12288), (8, 4200, 4096),
+              # more than 64 rows: the tiled kernel (K a multiple of 128; full
+              # and ragged 128-tiles), and K = 2080 on the split-K kernel
+              (256, 384, 2048), (130, 300, 1024), (300, 777, 4096), (100, 200, 2080)]
 
 # measured above the strict K-term bound (one or three 128-element steps of
 # the scaled MFMA, whose alignment term then exceeds K units: up to 6.2 x
