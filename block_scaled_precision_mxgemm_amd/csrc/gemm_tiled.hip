@@ -42,11 +42,15 @@ struct Cfg {
   // FP6 (E2M3 / E3M2) right operand: 96 bytes per row and 128-k slice,
   // copied 12 bytes per lane into the 16-byte slots of 128-byte LDS rows
   static constexpr bool B6 = FB == kFmtFp6 || FB == kFmtBf6;
+  // INT4 right operand: 64 bytes per row and slice (as E2M1), remapped in
+  // registers to the E4M3 codes of the same values for an E4M3 MFMA operand
+  static constexpr bool BI4 = FB == kElemInt4;
+  static constexpr int FBM = BI4 ? kFmtFp8 : FB;     // MFMA format of the right operand
   static constexpr bool SCALED = (KIND != kF16);
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
   static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
   static constexpr int RA = AF4 ? 64 : 128;          // LDS bytes per A row per slice
-  static constexpr int RB = BF4 ? 64 : 128;
+  static constexpr int RB = (BF4 || BI4) ? 64 : 128;
   static constexpr int KSLICE = (KIND == kF16) ? 64 : 128;  // K elements per slice
   static constexpr int SZA = BM * RA, SZB = BN * RB;
   static constexpr int SZSA = SCALED ? BM * 4 : 0, SZSB = SCALED ? BN * 4 : 0;
@@ -62,6 +66,7 @@ struct Cfg {
   static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
   static_assert(!B6 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "FP6 weights: E4M3 x FP6 on 128 x 128 tiles");
+  static_assert(!BI4 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "INT4 weights: E4M3 x INT4 on 128 x 128 tiles");
 };
 
 struct Args {
@@ -239,10 +244,27 @@ struct Kernel {
     const v4i hi = *reinterpret_cast<const v4i*>(lds + row * 128 + (((2 * g + 1) ^ s) << 4));
     return v8i{lo[0], lo[1], lo[2], hi[0], hi[1], hi[2], 0, 0};
   }
+  // INT4 operand of row `row` remapped to E4M3 codes: the fp8 operand's k
+  // ranges 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15 are the 8 code
+  // bytes at 8 g and 32 + 8 g of the 64-byte row (16-byte chunks swizzled by
+  // swz4)
+  static __device__ __forceinline__ v8i read_frag_int4(const uint8_t* lds, int row, int g) {
+    const int s = swz4(row);
+    const v2i lo = *reinterpret_cast<const v2i*>(lds + row * 64 + (((g >> 1) ^ s) << 4) + 8 * (g & 1));
+    const v2i hi = *reinterpret_cast<const v2i*>(lds + row * 64 + (((2 + (g >> 1)) ^ s) << 4) + 8 * (g & 1));
+    uint32_t e[8];
+    int4x8_to_e4m3((uint32_t)lo[0], e[0], e[1]);
+    int4x8_to_e4m3((uint32_t)lo[1], e[2], e[3]);
+    int4x8_to_e4m3((uint32_t)hi[0], e[4], e[5]);
+    int4x8_to_e4m3((uint32_t)hi[1], e[6], e[7]);
+    return v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], (int)e[4], (int)e[5], (int)e[6], (int)e[7]};
+  }
   template <bool SIX>
   static __device__ __forceinline__ v8i read_b(const uint8_t* lds, int row, int g) {
     if constexpr (SIX)
       return read_frag6(lds, row, g);
+    else if constexpr (T::BI4)
+      return read_frag_int4(lds, row, g);
     else
       return read_frag<T::RB>(lds, row, g);
   }
@@ -374,8 +396,10 @@ struct Kernel {
           }
 #pragma unroll
           for (int i = 0; i < T::FM; i++)
-            mfma_scaled_acc<T::FB, T::FA>(acc[i][j], bcur, af[i], sbcur,
-                                                                                    sa[i]);
+            if constexpr (T::BI4)
+              mfma_scaled_acc_after_valu(acc[i][j], bcur, af[i], sbcur, sa[i]);
+            else
+              mfma_scaled_acc<T::FBM, T::FA>(acc[i][j], bcur, af[i], sbcur, sa[i]);
           bcur = bnext;
           sbcur = sbnext;
         }
@@ -450,7 +474,7 @@ hipError_t launch(const Args& a0, hipStream_t stream) {
   const int rem = a.K - (a.nsteps - 1) * T::KSLICE;  // K elements in the last slice
   auto bytes = [&](bool f4, bool f16, int elems) { return f16 ? elems * 2 : (f4 ? elems / 2 : elems); };
   a.tail_a = bytes(T::AF4, !T::SCALED, rem);
-  a.tail_b = bytes(T::BF4, !T::SCALED, rem);
+  a.tail_b = bytes(T::BF4 || T::BI4, !T::SCALED, rem);
   const int64_t nt = (int64_t)a.tiles_m * a.tiles_n;
   hipLaunchKernelGGL((tiled_kernel<T, WPE>), dim3((unsigned)nt), dim3(T::NTHR), 0, stream, a);
   return hipGetLastError();
@@ -502,13 +526,15 @@ bool use_big_tiles(int64_t M, int64_t N) {
 hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const Epi& e,
                            int64_t M, int64_t N, int64_t K, int fmt, hipStream_t stream) {
   Args a = make_args(A, SA, B, SB, e, M, N, K);
-  const bool af4 = (fmt == 2), bf4 = (fmt == 1 || fmt == 2), bf6 = (fmt == 8 || fmt == 9);
+  const bool af4 = (fmt == 2), bf4 = (fmt == 1 || fmt == 2 || fmt == 6), bf6 = (fmt == 8 || fmt == 9);
   a.lda = af4 ? K / 2 : K;
   a.ldb = bf4 ? K / 2 : bf6 ? K / 4 * 3 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
   // E4M3 x FP6 (K a multiple of 128, checked by the caller): 128 x 128 tiles
   if (fmt == 8) return launch<MxMid<kFmtFp8, kFmtFp6>, 2>(a, stream);
   if (fmt == 9) return launch<MxMid<kFmtFp8, kFmtBf6>, 2>(a, stream);
+  // E4M3 x INT4 (codes remapped to E4M3 in registers): 128 x 128 tiles
+  if (fmt == 6) return launch<MxMid<kFmtFp8, kElemInt4>, 2>(a, stream);
   // the 256 x 256 tiled kernels store plain fp32 only (MxBig*::EPI_GENERAL)
   const bool big_pp = use_big_tiles(M, N);
   if (big_pp && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, e, M, N, K, fmt, stream);

@@ -181,6 +181,16 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& c, const v8i& a, const v8i&
   }
 }
 
+// E4M3 x E4M3 scaled MFMA (accumulator tied as above) whose operand a VALU
+// instruction may have written just before (codes remapped in registers):
+// the compiler inserts no wait states for an inline MFMA's operands, so the
+// s_nop supplies them.
+__device__ __forceinline__ void mfma_scaled_acc_after_valu(v4f& c, const v8i& a, const v8i& b, int scale_a,
+                                                           int scale_b) {
+  asm("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+      : "+a"(c) : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+}
+
 // Scaled MFMA taking its scales from byte BA of scale_a and byte BB of
 // scale_b (the op_sel / op_sel_hi pair selects the byte), so that the scales
 // of four fragments share one VGPR.  Accumulator tied as above; volatile, so
