@@ -49,8 +49,8 @@ int validate_epi(const float* bias, int act, int out_type) {
 }
 
 // integer weights (remapped in registers to MFMA operand codes) and FP6
-// weights (MFMA operands as stored): the split-K kernel takes them for every M
-// the decode kernel does not
+// weights (MFMA operands as stored): the split-K kernel takes them for every
+// M the decode and tiled kernels do not
 bool remapped_weights(int fmt) {
   return fmt == MXG_FMT_FP8_INT4 || fmt == MXG_FMT_FP8_INT2 || fmt == MXG_FMT_FP8_FP6 || fmt == MXG_FMT_FP8_BF6;
 }
