@@ -58,11 +58,11 @@ bool remapped_weights(int fmt) {
 // Kernel choice for an MX product (arguments validated): the weight-streaming
 // decode kernel (E4M3 activations against E4M3, E2M1, E2M3, E3M2, INT4 or
 // INT2 weights), the split-K skinny kernel (the same), or the tiled /
-// ping-pong kernels (every 8- and 4-bit float format pair; INT4 weights, and
-// FP6 weights when K is a multiple of 128, on the tiled kernel).  INT2
-// weights, and FP6 weights with other K, with more than 64 rows of
-// activations run the split-K kernel once per 64 rows (B is read once per 64
-// rows: a correct path for such shapes, not a tuned one).
+// ping-pong kernels (every 8- and 4-bit float format pair; integer weights,
+// and FP6 weights when K is a multiple of 128, on the tiled kernel).  FP6
+// weights with other K and more than 64 rows of activations run the split-K
+// kernel once per 64 rows (B is read once per 64 rows: a correct path for
+// such shapes, not a tuned one).
 int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, const mxg::Epi& e, int64_t M,
            int64_t N, int64_t K, int fmt, hipStream_t st) {
   if (mxg::decode_ok(M, K, fmt, SA, SB, e)) return to_status(mxg::launch_mx_decode(A, SA, B, SB, e, M, N, K, fmt, st));
@@ -70,9 +70,9 @@ int run_mx(const void* A, const uint8_t* SA, const void* B, const uint8_t* SB, c
   // (the byte offsets of 128 weight rows stay below 2^31)
   if ((fmt == MXG_FMT_FP8_FP6 || fmt == MXG_FMT_FP8_BF6) && M > mxg::kSkinnyMaxM && K % 128 == 0 && K < (1 << 24))
     return to_status(mxg::launch_mx_tiled(A, SA, B, SB, e, M, N, K, fmt, st));
-  // INT4 weights with more rows: the tiled kernel (any K; a partial last
-  // slice is zero-padded, and INT4 code 0 is the value 0)
-  if (fmt == MXG_FMT_FP8_INT4 && M > mxg::kSkinnyMaxM)
+  // integer weights with more rows: the tiled kernel (any K; in a partial
+  // last slice the codes past K are finite and meet zeroed activations)
+  if ((fmt == MXG_FMT_FP8_INT4 || fmt == MXG_FMT_FP8_INT2) && M > mxg::kSkinnyMaxM)
     return to_status(mxg::launch_mx_tiled(A, SA, B, SB, e, M, N, K, fmt, st));
   if (remapped_weights(fmt) && M > mxg::kSkinnyMaxM) {
     const int64_t eb = mxg::epi_elem_bytes(e.out);

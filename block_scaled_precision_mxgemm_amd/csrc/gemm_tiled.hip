@@ -45,12 +45,14 @@ struct Cfg {
   // INT4 right operand: 64 bytes per row and slice (as E2M1), remapped in
   // registers to the E4M3 codes of the same values for an E4M3 MFMA operand
   static constexpr bool BI4 = FB == kElemInt4;
-  static constexpr int FBM = BI4 ? kFmtFp8 : FB;     // MFMA format of the right operand
+  // INT2 right operand: 32 bytes per row and slice, remapped to E2M1 codes
+  static constexpr bool BI2 = FB == kElemInt2;
+  static constexpr int FBM = BI4 ? kFmtFp8 : BI2 ? kFmtFp4 : FB;  // MFMA format of the right operand
   static constexpr bool SCALED = (KIND != kF16);
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
   static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
   static constexpr int RA = AF4 ? 64 : 128;          // LDS bytes per A row per slice
-  static constexpr int RB = (BF4 || BI4) ? 64 : 128;
+  static constexpr int RB = BI2 ? 32 : (BF4 || BI4) ? 64 : 128;
   static constexpr int KSLICE = (KIND == kF16) ? 64 : 128;  // K elements per slice
   static constexpr int SZA = BM * RA, SZB = BN * RB;
   static constexpr int SZSA = SCALED ? BM * 4 : 0, SZSB = SCALED ? BN * 4 : 0;
@@ -66,7 +68,8 @@ struct Cfg {
   static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
   static_assert(!B6 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "FP6 weights: E4M3 x FP6 on 128 x 128 tiles");
-  static_assert(!BI4 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "INT4 weights: E4M3 x INT4 on 128 x 128 tiles");
+  static_assert(!(BI4 || BI2) || (KIND == kMX && FA == kFmtFp8 && BM == 128),
+                "integer weights: E4M3 x INT4 / INT2 on 128 x 128 tiles");
 };
 
 struct Args {
@@ -98,7 +101,7 @@ struct Kernel {
       const int o = q * 1024 + lane * 16;
       const int row = o / R;
       const int pch = (o % R) >> 4;
-      const int c = pch ^ (R == 128 ? swz8(row) : swz4(row));
+      const int c = pch ^ (R == 128 ? swz8(row) : R == 64 ? swz4(row) : 0);  // 32-byte rows: 2 chunks, none
       const int grow = min(row0 + row, rows_valid - 1);
       // a chunk reaching past the end of the row (partial last slice) reads
       // the slice's first chunk instead, which is always in bounds; it is
@@ -140,7 +143,7 @@ struct Kernel {
       const int o = q * 1024 + lane * 16;
       const int row = o / R;
       const int pch = (o % R) >> 4;
-      const int c = pch ^ (R == 128 ? swz8(row) : swz4(row));
+      const int c = pch ^ (R == 128 ? swz8(row) : R == 64 ? swz4(row) : 0);  // 32-byte rows: 2 chunks, none
       if (c * 16 >= valid_bytes) *reinterpret_cast<v4i*>(lds + o) = v4i{0, 0, 0, 0};
     }
   }
@@ -259,12 +262,23 @@ struct Kernel {
     int4x8_to_e4m3((uint32_t)hi[1], e[6], e[7]);
     return v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], (int)e[4], (int)e[5], (int)e[6], (int)e[7]};
   }
+  // INT2 operand of row `row` remapped to E2M1 codes: the fp4 operand's k
+  // range 32 g .. 32 g + 31 is the 8 code bytes at 8 g of the 32-byte row
+  static __device__ __forceinline__ v8i read_frag_int2(const uint8_t* lds, int row, int g) {
+    const v2i c = *reinterpret_cast<const v2i*>(lds + row * 32 + 8 * g);
+    uint32_t e[4];
+    int2x16_to_e2m1((uint32_t)c[0], e[0], e[1]);
+    int2x16_to_e2m1((uint32_t)c[1], e[2], e[3]);
+    return v8i{(int)e[0], (int)e[1], (int)e[2], (int)e[3], 0, 0, 0, 0};
+  }
   template <bool SIX>
   static __device__ __forceinline__ v8i read_b(const uint8_t* lds, int row, int g) {
     if constexpr (SIX)
       return read_frag6(lds, row, g);
     else if constexpr (T::BI4)
       return read_frag_int4(lds, row, g);
+    else if constexpr (T::BI2)
+      return read_frag_int2(lds, row, g);
     else
       return read_frag<T::RB>(lds, row, g);
   }
@@ -398,6 +412,8 @@ struct Kernel {
           for (int i = 0; i < T::FM; i++)
             if constexpr (T::BI4)
               mfma_scaled_acc_after_valu(acc[i][j], bcur, af[i], sbcur, sa[i]);
+            else if constexpr (T::BI2)
+              mfma_scaled_acc_fp4a_after_valu(acc[i][j], bcur, af[i], sbcur, sa[i]);
             else
               mfma_scaled_acc<T::FBM, T::FA>(acc[i][j], bcur, af[i], sbcur, sa[i]);
           bcur = bnext;
@@ -474,7 +490,7 @@ hipError_t launch(const Args& a0, hipStream_t stream) {
   const int rem = a.K - (a.nsteps - 1) * T::KSLICE;  // K elements in the last slice
   auto bytes = [&](bool f4, bool f16, int elems) { return f16 ? elems * 2 : (f4 ? elems / 2 : elems); };
   a.tail_a = bytes(T::AF4, !T::SCALED, rem);
-  a.tail_b = bytes(T::BF4 || T::BI4, !T::SCALED, rem);
+  a.tail_b = T::BI2 ? rem / 4 : bytes(T::BF4 || T::BI4, !T::SCALED, rem);
   const int64_t nt = (int64_t)a.tiles_m * a.tiles_n;
   hipLaunchKernelGGL((tiled_kernel<T, WPE>), dim3((unsigned)nt), dim3(T::NTHR), 0, stream, a);
   return hipGetLastError();
@@ -528,13 +544,15 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
   Args a = make_args(A, SA, B, SB, e, M, N, K);
   const bool af4 = (fmt == 2), bf4 = (fmt == 1 || fmt == 2 || fmt == 6), bf6 = (fmt == 8 || fmt == 9);
   a.lda = af4 ? K / 2 : K;
-  a.ldb = bf4 ? K / 2 : bf6 ? K / 4 * 3 : K;
+  a.ldb = bf4 ? K / 2 : bf6 ? K / 4 * 3 : fmt == 7 ? K / 4 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
   // E4M3 x FP6 (K a multiple of 128, checked by the caller): 128 x 128 tiles
   if (fmt == 8) return launch<MxMid<kFmtFp8, kFmtFp6>, 2>(a, stream);
   if (fmt == 9) return launch<MxMid<kFmtFp8, kFmtBf6>, 2>(a, stream);
   // E4M3 x INT4 (codes remapped to E4M3 in registers): 128 x 128 tiles
   if (fmt == 6) return launch<MxMid<kFmtFp8, kElemInt4>, 2>(a, stream);
+  // E4M3 x INT2 (codes remapped to E2M1 in registers): 128 x 128 tiles
+  if (fmt == 7) return launch<MxMid<kFmtFp8, kElemInt2>, 2>(a, stream);
   // the 256 x 256 tiled kernels store plain fp32 only (MxBig*::EPI_GENERAL)
   const bool big_pp = use_big_tiles(M, N);
   if (big_pp && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, e, M, N, K, fmt, stream);

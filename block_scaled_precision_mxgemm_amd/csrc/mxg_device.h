@@ -191,6 +191,15 @@ __device__ __forceinline__ void mfma_scaled_acc_after_valu(v4f& c, const v8i& a,
       : "+a"(c) : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
 }
 
+// The same for an E2M1 first operand (remapped codes) against an E4M3
+// second one.
+__device__ __forceinline__ void mfma_scaled_acc_fp4a_after_valu(v4f& c, const v8i& a, const v8i& b, int scale_a,
+                                                                int scale_b) {
+  const v4i a4 = {a[0], a[1], a[2], a[3]};
+  asm("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4"
+      : "+a"(c) : "v"(a4), "v"(b), "v"(scale_a), "v"(scale_b));
+}
+
 // Scaled MFMA taking its scales from byte BA of scale_a and byte BB of
 // scale_b (the op_sel / op_sel_hi pair selects the byte), so that the scales
 // of four fragments share one VGPR.  Accumulator tied as above; volatile, so

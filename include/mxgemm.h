@@ -144,9 +144,8 @@ int mxgemm_quantize(const float *X, int64_t rows, int64_t K, int elem,
  * Integer weights (MXG_FMT_FP8_INT4 / _INT2) are fed to that MFMA as the
  * E4M3 / E2M1 codes of the same values (exact: -8..7 and -2..1 are values of
  * those formats), remapped in registers; they take the decode kernel (INT2:
- * K a multiple of 4096) and the split-K kernel; with M > 64, INT4 weights
- * take the 4-wave tiled kernel and INT2 weights the split-K kernel once per
- * 64 rows of A.  FP6 weights (MXG_FMT_FP8_FP6 / _BF6) are MFMA operands as stored
+ * K a multiple of 4096) and the split-K kernel, and with M > 64 the 4-wave
+ * tiled kernel.  FP6 weights (MXG_FMT_FP8_FP6 / _BF6) are MFMA operands as stored
  * (the instruction's E2M3 / E3M2 modes: a lane's 32 codes are its 24 bytes of
  * a row); they take the decode kernel and the split-K kernel, and with
  * M > 64 the 4-wave tiled kernel when K % 128 == 0, else the split-K kernel

@@ -128,7 +128,8 @@ CASES = [("mxfp8_8192", 4096, 4096, 256, 0, 20000), ("mxfp8_2048", 4096, 4352, 2
          ("decode_16x28672x8192", 13, 1001, 4608, 1, None), ("decode_16x28672x8192", 16, 1000, 4096, 8, None),
          ("decode_16x28672x8192", 33, 1001, 8192, 9, None), ("decode_16x28672x8192", 13, 1001, 4608, 8, None),
          ("decode_16x28672x8192", 17, 600, 14336, 9, None), ("decode_16x28672x8192", 200, 300, 1024, 8, None),
-         ("decode_16x28672x8192", 130, 257, 2048, 9, None), ("decode_16x28672x8192", 150, 260, 1056, 6, None)]
+         ("decode_16x28672x8192", 130, 257, 2048, 9, None), ("decode_16x28672x8192", 150, 260, 1056, 6, None),
+         ("decode_16x28672x8192", 140, 270, 2080, 7, None)]
 
 EPILOGUES = [(True, oracle.ACT_GELU, oracle.OUT_BF16), (True, oracle.ACT_NONE, oracle.OUT_F16),
              (False, oracle.ACT_GELU, oracle.OUT_F32), (True, oracle.ACT_GELU, oracle.OUT_F16)]

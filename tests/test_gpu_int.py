@@ -69,9 +69,8 @@ def test_int_quantize_every_mantissa(elem):
 # (M, N, K): decode kernel one launch (K 2048 .. 8192 and, for INT4, 14336 =
 # the per-launch maximum), odd K / 1024 (uneven wave split for INT4), two and
 # four row blocks, K chunks adding into C, decode + split-K remainder, the
-# split-K kernel (K not a multiple of 1024, short K), more than 64 rows (INT4:
-# the tiled kernel, full and ragged tiles, a partial last slice; INT2: the
-# split-K kernel once per 64 rows)
+# split-K kernel (K not a multiple of 1024, short K), more than 64 rows (the
+# tiled kernel: full and ragged tiles, a partial last slice)
 INT_SHAPES = [(1, 300, 2048), (16, 1001, 4096), (13, 250, 8192), (3, 64, 8192), (16, 1000, 3072), (9, 5000, 5120),
               (17, 1001, 8192), (32, 300, 4096), (40, 777, 8192), (64, 500, 4096), (16, 1000, 14336),
               (5, 300, 32768), (16, 700, 11008), (7, 1000, 1536), (33, 250, 96), (5, 28, 32), (64, 129, 256),
