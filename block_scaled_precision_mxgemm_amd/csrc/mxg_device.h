@@ -90,47 +90,57 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
 // value (the UE8M0 block scales are unchanged): the products and therefore
 // the results are those of the integer operand.  The lookups run on four
 // bytes at a time with v_perm_b32, whose selector bytes 0-3 pick bytes of
-// its second source and 4-7 bytes of its first.
+// its second source and 4-7 bytes of its first; selector values above 7 give
+// a constant byte instead: 8, 9, 10, 11 repeat bit 7 of source bytes 1, 3, 5
+// and 7 eight times, 12 gives 0x00 and 13-15 give 0xFF.
 
-// Byte-wise lookup of four 4-bit indices (one per byte, 0..15) in the table
-// t0 (entries 0-3), t1 (4-7), t2 (8-11), t3 (12-15).
-__device__ __forceinline__ uint32_t lookup16(uint32_t idx, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
-  const uint32_t lo3 = idx & 0x07070707u;
-  const uint32_t a = __builtin_amdgcn_perm(t1, t0, lo3);
-  const uint32_t b = __builtin_amdgcn_perm(t3, t2, lo3);
-  // byte i of the result: byte i of a (selector i) or, where the index is
-  // >= 8, byte i of b (selector i + 4); a third permute instead of a byte
-  // mask, whose multiply by 0xFF would be a quarter-rate integer multiply
-  const uint32_t sel = ((idx >> 1) & 0x04040404u) | 0x03020100u;
-  return __builtin_amdgcn_perm(b, a, sel);
+// Byte-wise lookup of four 4-bit indices (one per byte, 0..15) in a 16-entry
+// table held as two 8-byte halves that are XORed: the first half is indexed
+// with n, the second with n ^ 8.  For n < 8 the first permute returns a table
+// byte and the second one of the constant bytes above (n ^ 8 >= 8), and for
+// n >= 8 the other way round, so each half stores the wanted byte XOR the
+// constant byte that the other half returns for the same n.  That constant is
+// known for every n (selectors 8-11 read bit 7 of the other half's odd
+// bytes), and the halves can be filled one after the other with no circular
+// dependence: it costs two permutes and two XORs per four bytes, against
+// three permutes and a selector computation for a byte select.
+__device__ __forceinline__ uint32_t lookup16x(uint32_t idx, uint32_t lo0, uint32_t lo1, uint32_t hi0, uint32_t hi1) {
+  return __builtin_amdgcn_perm(lo1, lo0, idx) ^ __builtin_amdgcn_perm(hi1, hi0, idx ^ 0x08080808u);
+}
+
+// The nibbles 0-3 (lo) and 4-7 (hi) of x, one per byte (low nibble of each
+// byte; the high nibble is cleared).
+__device__ __forceinline__ void spread_nibbles(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  const uint32_t s = x >> 4;
+  lo = __builtin_amdgcn_perm(s, x, 0x05010400u) & 0x0F0F0F0Fu;
+  hi = __builtin_amdgcn_perm(s, x, 0x07030602u) & 0x0F0F0F0Fu;
 }
 
 // Eight INT4 codes (element i in bits 4i .. 4i+3) -> the E4M3 codes of
 // elements 0-3 (lo) and 4-7 (hi), one per byte.
 __device__ __forceinline__ void int4x8_to_e4m3(uint32_t x, uint32_t& lo, uint32_t& hi) {
-  // E4M3 codes of 0..7 and of -8..-1 (indices 8..15)
-  constexpr uint32_t T0 = 0x44403800u, T1 = 0x4E4C4A48u, T2 = 0xCACCCED0u, T3 = 0xB8C0C4C8u;
-  const uint32_t ev = lookup16(x & 0x0F0F0F0Fu, T0, T1, T2, T3);         // elements 0, 2, 4, 6
-  const uint32_t od = lookup16((x >> 4) & 0x0F0F0F0Fu, T0, T1, T2, T3);  // elements 1, 3, 5, 7
-  lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);
-  hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+  // E4M3 codes of 0..7 (n = 0..7) and of -8..-1 (n = 8..15):
+  //   00 38 40 44 48 4A 4C 4E  D0 CE CC CA C8 C4 C0 B8
+  // stored as described at lookup16x (bytes in index order, low byte first)
+  constexpr uint32_t L0 = 0x444038FFu, L1 = 0xB1B3B548u, H0 = 0x3533CED0u, H1 = 0x473F3BC8u;
+  uint32_t a, b;
+  spread_nibbles(x, a, b);
+  lo = lookup16x(a, L0, L1, H0, H1);
+  hi = lookup16x(b, L0, L1, H0, H1);
 }
 
 // Sixteen INT2 codes (element i in bits 2i .. 2i+1) -> the E2M1 codes of
 // elements 0-7 (lo) and 8-15 (hi), two per byte, even element in the low
-// nibble.  One table entry maps a pair of INT2 codes (4 bits) to the byte
-// of their two E2M1 codes.
+// nibble.  A nibble of x holds a pair of INT2 codes p = c0 + 4 c1, and its
+// table entry is the byte of their two E2M1 codes, code(c0) | code(c1) << 4,
+// with code 0 -> 0x0, 1 -> 0x2 (1.0), -2 -> 0xC, -1 -> 0xA:
+//   00 02 0C 0A 20 22 2C 2A  C0 C2 CC CA A0 A2 AC AA
 __device__ __forceinline__ void int2x16_to_e2m1(uint32_t x, uint32_t& lo, uint32_t& hi) {
-  // E2M1 code of each INT2 value: 0 -> 0x0, 1 -> 0x2 (1.0), -2 -> 0xC, -1 -> 0xA
-  // entry p = c0 + 4 c1 holds code(c0) | code(c1) << 4
-  constexpr uint32_t T0 = 0x0A0C0200u, T1 = 0x2A2C2220u, T2 = 0xCACCC2C0u, T3 = 0xAAACA2A0u;
-  // spread the four pairs of each 16-bit half to the bytes of a word
-  const uint32_t l = (x & 0xFFu) | ((x << 8) & 0xFF0000u);
-  const uint32_t h = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u);
-  const uint32_t li = (l & 0x000F000Fu) | ((l << 4) & 0x0F000F00u);
-  const uint32_t hi_i = (h & 0x000F000Fu) | ((h << 4) & 0x0F000F00u);
-  lo = lookup16(li, T0, T1, T2, T3);
-  hi = lookup16(hi_i, T0, T1, T2, T3);
+  constexpr uint32_t L0 = 0x0A0C02FFu, L1 = 0xD5D3DD20u, H0 = 0x3533C2C0u, H1 = 0x55535DA0u;
+  uint32_t a, b;
+  spread_nibbles(x, a, b);
+  lo = lookup16x(a, L0, L1, H0, H1);
+  hi = lookup16x(b, L0, L1, H0, H1);
 }
 
 // The format ids must be compile-time constants for the builtin.
