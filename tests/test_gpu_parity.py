@@ -42,6 +42,9 @@ MODEL_CASES = {
     ("pp128", (2304, 2176, 512, 5)),
     ("nan", (4096, 4096, 256, 0)), ("nan", (128, 384, 256, 0)), ("nan", (200, 40, 256, 0)),
     ("nan", (128, 384, 256, 3)), ("inf", (37, 45, 96, 3)),
+    # K = 256 / 288 with FP6 and INT4 weights: up to 1.6 x the strict bound,
+    # 0.016 x the model bound (the E4M3 case of the same shape: 1.54 x)
+    ("nan", (200, 40, 256, 6)), ("nan", (200, 40, 256, 8)), ("nan", (130, 40, 288, 9)),
     # 25 of 17.8 M outputs at up to 1.34 x the strict bound, 0.035 x the
     # model bound
     ("persistent", (4096, 4352, 768, 0)),
@@ -351,12 +354,14 @@ def test_accumulator_width_on_gpu():
 # byte of B does.  Shapes: 256 x 256 ping-pong (>= 256 full tiles), 128 x 128
 # split-K ping-pong, 4-wave tiled (ragged), split-K skinny, decode (one
 # launch, K chunks adding into C, decode + split-K remainder) with E4M3, E2M1,
-# E2M3, E3M2, INT4 and INT2 weights.
+# E2M3, E3M2, INT4 and INT2 weights; FP6, INT4 and INT2 weights with more
+# than 64 rows (tiled kernel; FP6 with K % 128 != 0: split-K per 64 rows).
 NAN_CASES = [(4096, 4096, 256, 0, 30000), (128, 384, 256, 0, None), (200, 40, 256, 0, None), (8, 40, 256, 0, None),
              (8, 40, 2048, 0, None), (8, 40, 2048, 1, None), (40, 520, 8192, 1, None), (13, 40, 4608, 1, None),
              (4096, 4096, 256, 2, 30000), (128, 384, 256, 3, None),
              (8, 40, 2048, 8, None), (13, 40, 4608, 9, None), (40, 520, 16384, 8, None), (8, 40, 2048, 6, None),
-             (8, 40, 4096, 7, None)]
+             (8, 40, 4096, 7, None), (200, 40, 256, 6, None), (200, 40, 256, 7, None), (200, 40, 256, 8, None),
+             (130, 40, 288, 9, None)]
 
 
 @pytest.mark.parametrize("M,N,K,fmt,npts", NAN_CASES)
