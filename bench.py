@@ -707,7 +707,27 @@ def main():
         ceilings["fp4_e2m1"] = mfma_ceiling(mx, qa5, sa5, mx.FMT_FP4_FP4)
         extra["prefill_mxfp4_8192x14336x4096"]["ceiling_frac"] = (
             extra["prefill_mxfp4_8192x14336x4096"]["TFLOP/s"] / ceilings["fp4_e2m1"]["TFLOP/s"])
-        del qa5, sa5, qb5, sb5, c4
+        del qa5, sa5, qb5, sb5
+
+        # the same prefill GEMM with E4M3 activations and FP6 / INT4 / INT2
+        # weights (the 4-wave tiled kernel), against the fp8 peak: one MFMA
+        # operand is E4M3 (INT4 runs E4M3 x E4M3, INT2 E4M3 x E2M1 after the
+        # remap); the E4M3 x E2M1 MFMA ceiling is measured beside it
+        for name, fmt in (("prefill_e2m3_8192x14336x4096", mx.FMT_FP8_FP6),
+                          ("prefill_int4_8192x14336x4096", mx.FMT_FP8_INT4),
+                          ("prefill_int2_8192x14336x4096", mx.FMT_FP8_INT2)):
+            wq, ta, tb, qaq, saq, qbq, sbq = mx_operands(name, dev)
+            del ta, tb
+            rq = time_windows(lambda i=0: mx.mxgemm_run(qaq, saq, qbq, sbq, fmt, out=c4))
+            extra[name] = timed_entry(rq, flops=f4, peak=PEAK_FP8_TFLOPS)
+            log("%s: %.3f ms = %.0f TFLOP/s (%.1f%% of the fp8 peak)" % (
+                name, rq["ms_median"], extra[name]["TFLOP/s"], 100 * extra[name]["peak_frac"]))
+            if fmt == mx.FMT_FP8_INT2:
+                ceilings["fp8_e2m1"] = mfma_ceiling(mx, qaq, saq, mx.FMT_FP8_FP4)
+                log("MFMA ceiling E4M3 x E2M1: %.0f TFLOP/s" % ceilings["fp8_e2m1"]["TFLOP/s"])
+                extra[name]["ceiling_frac"] = extra[name]["TFLOP/s"] / ceilings["fp8_e2m1"]["TFLOP/s"]
+            del qaq, saq, qbq, sbq
+        del c4
         torch.cuda.empty_cache()
 
     if only in ("all", "decode"):

@@ -54,6 +54,12 @@ WORKLOADS = {
                  "LLM-prefill MXFP8 GEMM, 8192 tokens x 4096 -> 14336"),
         Workload("prefill_mxfp4_8192x14336x4096", 8192, 14336, 4096, 4, "e2m1", "e2m1", "prefill",
                  "LLM-prefill MXFP4 x MXFP4 GEMM (both operands E2M1), same sources"),
+        Workload("prefill_e2m3_8192x14336x4096", 8192, 14336, 4096, 4, "e4m3", "e2m3", "prefill",
+                 "LLM-prefill GEMM, MXFP8 activations x FP6 E2M3 weights, same sources"),
+        Workload("prefill_int4_8192x14336x4096", 8192, 14336, 4096, 4, "e4m3", "int4", "prefill",
+                 "LLM-prefill GEMM, MXFP8 activations x INT4 weights (UE8M0 per 32), same sources"),
+        Workload("prefill_int2_8192x14336x4096", 8192, 14336, 4096, 4, "e4m3", "int2", "prefill",
+                 "LLM-prefill GEMM, MXFP8 activations x INT2 weights (UE8M0 per 32), same sources"),
         Workload("decode_16x28672x8192", 16, 28672, 8192, 5, "e4m3", "e2m1", "decode",
                  "decode MXFP8 x MXFP4 GEMM, 16 tokens x 8192 -> 28672"),
         Workload("mxfp8_8192", 8192, 8192, 8192, 6, "e4m3", "e4m3", "normal",

@@ -26,7 +26,9 @@ def _device():
 
 MX_WORKLOADS = [("mxfp8_256", 0, None), ("mxfp8_2048", 0, 30000), ("prefill_8192x14336x4096", 0, 30000),
                 ("prefill_mxfp4_8192x14336x4096", 2, 30000), ("decode_16x28672x8192", 1, None),
-                ("mxfp8_8192", 0, 30000), ("mxfp8xbf8_8192", 4, 30000)]
+                ("mxfp8_8192", 0, 30000), ("mxfp8xbf8_8192", 4, 30000),
+                ("prefill_e2m3_8192x14336x4096", 8, 30000), ("prefill_int4_8192x14336x4096", 6, 30000),
+                ("prefill_int2_8192x14336x4096", 7, 30000)]
 
 
 @pytest.mark.parametrize("name,fmt,npts", MX_WORKLOADS)
