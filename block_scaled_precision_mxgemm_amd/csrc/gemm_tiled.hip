@@ -68,8 +68,8 @@ struct Cfg {
   static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
   static_assert(!B6 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "FP6 weights: E4M3 x FP6 on 128 x 128 tiles");
-  static_assert(!(BI4 || BI2) || (KIND == kMX && FA == kFmtFp8 && BM == 128),
-                "integer weights: E4M3 x INT4 / INT2 on 128 x 128 tiles");
+  static_assert(!(BI4 || BI2) || (KIND == kMX && FA == kFmtFp8 && (BM == 128 || BM == 256)),
+                "integer weights: E4M3 x INT4 / INT2 on 128 x 128 or 256 x 256 tiles");
 };
 
 struct Args {
@@ -520,7 +520,11 @@ using MxMid = Cfg<kMX, 128, 128, 2, 2, FA, FB, false>;
 // is read and remapped by one wave only, where 2 x 2 waves remap every one
 // twice (measured at 8192 x 14336 x 4096: INT4 0.778 -> 0.695 ms, INT2 0.626
 // -> 0.595 ms; FP6 weights, whose fragments are only gathered, gained
-// nothing and keep 2 x 2)
+// nothing and keep 2 x 2).  Outputs of at least 256 tiles of 256 x 256 with
+// a plain fp32 store take the 256 x 256 tiles (2 x 2 waves of 128 x 128:
+// each fragment is remapped by two waves but feeds 8 MFMAs in each, the
+// same remap work per MFMA with fewer LDS bytes per MFMA; INT4 0.685 ->
+// 0.665 ms, INT2 0.585 -> 0.556 ms)
 template <int FB>
 using MxIntMid = Cfg<kMX, 128, 128, 1, 4, kFmtFp8, FB, false>;
 using MxBig88 = MxBig<kFmtFp8, kFmtFp8>;
@@ -557,9 +561,10 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
   if (fmt == 8) return launch<MxMid<kFmtFp8, kFmtFp6>, 2>(a, stream);
   if (fmt == 9) return launch<MxMid<kFmtFp8, kFmtBf6>, 2>(a, stream);
   // E4M3 x INT4 (codes remapped to E4M3 in registers): 128 x 128 tiles
-  if (fmt == 6) return launch<MxIntMid<kElemInt4>, 2>(a, stream);
+  const bool big_int = use_big_tiles(M, N) && e.bias == nullptr && e.act == kActNone && e.out == kOutF32;
+  if (fmt == 6) return big_int ? launch<MxBig<kFmtFp8, kElemInt4>, 1>(a, stream) : launch<MxIntMid<kElemInt4>, 2>(a, stream);
   // E4M3 x INT2 (codes remapped to E2M1 in registers): 128 x 128 tiles
-  if (fmt == 7) return launch<MxIntMid<kElemInt2>, 2>(a, stream);
+  if (fmt == 7) return big_int ? launch<MxBig<kFmtFp8, kElemInt2>, 1>(a, stream) : launch<MxIntMid<kElemInt2>, 2>(a, stream);
   // the 256 x 256 tiled kernels store plain fp32 only (MxBig*::EPI_GENERAL)
   const bool big_pp = use_big_tiles(M, N);
   if (big_pp && pingpong_mx_ok(SA, SB, M, N, K)) return launch_mx_pingpong(A, SA, B, SB, e, M, N, K, fmt, stream);

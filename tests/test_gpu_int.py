@@ -94,6 +94,19 @@ def test_int_gemm(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", [6, 7])
+@pytest.mark.parametrize("M,N,K", [(4100, 4200, 384), (4096, 4352, 1056)])
+def test_int_gemm_large_tiles(fmt, M, N, K):
+    """Outputs with at least 256 tiles of 256 x 256 (the 256 x 256 tiled
+    kernel), ragged edges and a partial last K slice, on sampled elements."""
+    say("int gemm large tiles", fmt, M, N, K)
+    a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=13 * M + N + K + fmt)
+    pts = mxin.sample_points(M, N, 20000, seed=M + N + K + fmt)
+    r, c = mx_case(a32, b32, fmt, points=pts)
+    assert r["ok"], r
+    assert not np.isnan(c).any()
+
+
+@pytest.mark.parametrize("fmt", [6, 7])
 @pytest.mark.parametrize("M,N,K", [(8, 40, 2048), (40, 520, 8192), (13, 40, 4608), (100, 60, 256)])
 def test_int_nan_scale(fmt, M, N, K):
     """A NaN scale byte in a row of A and in a row of B (the integer codes
