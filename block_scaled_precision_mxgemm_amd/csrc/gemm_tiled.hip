@@ -67,7 +67,8 @@ struct Cfg {
   static_assert(NQA % NW == 0 && NQB % NW == 0, "tile copies split evenly over the waves");
   static_assert(BM <= NTHR && BN <= NTHR, "one scale row per thread");
   static_assert(!(BKN && KIND != kF16), "K x N right operand only for fp16");
-  static_assert(!B6 || (KIND == kMX && FA == kFmtFp8 && BM == 128), "FP6 weights: E4M3 x FP6 on 128 x 128 tiles");
+  static_assert(!B6 || (KIND == kMX && FA == kFmtFp8 && (BM == 128 || BM == 256)),
+                "FP6 weights: E4M3 x FP6 on 128 x 128 or 256 x 256 tiles");
   static_assert(!(BI4 || BI2) || (KIND == kMX && FA == kFmtFp8 && (BM == 128 || BM == 256)),
                 "integer weights: E4M3 x INT4 / INT2 on 128 x 128 or 256 x 256 tiles");
 };
@@ -119,7 +120,7 @@ struct Kernel {
                                                      int rows_valid, int64_t col_byte, uint8_t* lds, int wave,
                                                      int lane) {
     constexpr int kRsrcWord3 = 0x00020000;
-    const int nrows = min(rows_valid - row0, 128);
+    const int nrows = min(rows_valid - row0, T::BN);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)row0 * ld), 0, (int)(nrows * ld),
                                                       kRsrcWord3);
 #pragma unroll
@@ -522,9 +523,9 @@ using MxMid = Cfg<kMX, 128, 128, 2, 2, FA, FB, false>;
 // -> 0.595 ms; FP6 weights, whose fragments are only gathered, gained
 // nothing and keep 2 x 2).  Outputs of at least 256 tiles of 256 x 256 with
 // a plain fp32 store take the 256 x 256 tiles (2 x 2 waves of 128 x 128:
-// each fragment is remapped by two waves but feeds 8 MFMAs in each, the
-// same remap work per MFMA with fewer LDS bytes per MFMA; INT4 0.685 ->
-// 0.665 ms, INT2 0.585 -> 0.556 ms)
+// each fragment is remapped or gathered by two waves but feeds 8 MFMAs in
+// each, with fewer LDS bytes per MFMA; INT4 0.685 -> 0.665 ms, INT2 0.585 ->
+// 0.556 ms, FP6 0.685 -> 0.605 ms)
 template <int FB>
 using MxIntMid = Cfg<kMX, 128, 128, 1, 4, kFmtFp8, FB, false>;
 using MxBig88 = MxBig<kFmtFp8, kFmtFp8>;
@@ -558,10 +559,10 @@ hipError_t launch_mx_tiled(const void* A, const uint8_t* SA, const void* B, cons
   a.ldb = bf4 ? K / 2 : bf6 ? K / 4 * 3 : fmt == 7 ? K / 4 : K;
   a.scale_aligned = ((K & 127) == 0 && ((uintptr_t)SA & 3) == 0 && ((uintptr_t)SB & 3) == 0) ? 1 : 0;
   // E4M3 x FP6 (K a multiple of 128, checked by the caller): 128 x 128 tiles
-  if (fmt == 8) return launch<MxMid<kFmtFp8, kFmtFp6>, 2>(a, stream);
-  if (fmt == 9) return launch<MxMid<kFmtFp8, kFmtBf6>, 2>(a, stream);
-  // E4M3 x INT4 (codes remapped to E4M3 in registers): 128 x 128 tiles
   const bool big_int = use_big_tiles(M, N) && e.bias == nullptr && e.act == kActNone && e.out == kOutF32;
+  if (fmt == 8) return big_int ? launch<MxBig<kFmtFp8, kFmtFp6>, 1>(a, stream) : launch<MxMid<kFmtFp8, kFmtFp6>, 2>(a, stream);
+  if (fmt == 9) return big_int ? launch<MxBig<kFmtFp8, kFmtBf6>, 1>(a, stream) : launch<MxMid<kFmtFp8, kFmtBf6>, 2>(a, stream);
+  // E4M3 x INT4 (codes remapped to E4M3 in registers): 128 x 128 tiles
   if (fmt == 6) return big_int ? launch<MxBig<kFmtFp8, kElemInt4>, 1>(a, stream) : launch<MxIntMid<kElemInt4>, 2>(a, stream);
   // E4M3 x INT2 (codes remapped to E2M1 in registers): 128 x 128 tiles
   if (fmt == 7) return big_int ? launch<MxBig<kFmtFp8, kElemInt2>, 1>(a, stream) : launch<MxIntMid<kElemInt2>, 2>(a, stream);

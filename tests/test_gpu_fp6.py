@@ -113,6 +113,19 @@ def test_fp6_gemm(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", [8, 9])
+@pytest.mark.parametrize("M,N,K", [(4100, 4200, 384), (4096, 4352, 1024)])
+def test_fp6_gemm_large_tiles(fmt, M, N, K):
+    """Outputs with at least 256 tiles of 256 x 256 (the 256 x 256 tiled
+    kernel), full and ragged edges, on sampled elements."""
+    say("fp6 gemm large tiles", fmt, M, N, K)
+    a32, b32 = mx_sources("decode_16x28672x8192", M, N, K, seed=17 * M + N + K + fmt)
+    pts = mxin.sample_points(M, N, 20000, seed=M + N + K + fmt)
+    r, c = mx_case(a32, b32, fmt, points=pts)
+    assert r["ok"], r
+    assert not np.isnan(c).any()
+
+
+@pytest.mark.parametrize("fmt", [8, 9])
 @pytest.mark.parametrize("M,N,K", [(8, 40, 2048), (100, 60, 256)])
 def test_fp6_nan_scale(fmt, M, N, K):
     """A NaN scale byte in a row of A and in a row of B (FP6 has no NaN
